@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Throughput of matmul against GGUF block-quantized weights on one MI355X.
+
+One step is the decode GEMV workload: y = x . W^T for Q4_K and Q6_K weights
+of N=14336 rows by K=4096, each at M=1 and at M=8 tokens, f32 activations,
+f32 outputs -- four GEMV launches through the C ABI.  The reported value is
+the quantized-weight bytes those launches read per second (each weight byte
+counted once per launch), over exactly --steps steps after --warmup steps.
+
+Weights are resident in HBM before timing starts.  To measure HBM rather
+than the 256 MiB Infinity Cache, every launch reads a different copy of its
+weight set; a copy is read again only after more than 1 GiB of other weights
+has been streamed.  Steps are replayed from captured HIP graphs so host
+launch overhead does not enter the timing.
+
+Also printed in the same JSON line:
+  roofline      the dominant kernel's algorithmic bytes per launch over its
+                average launch duration (HIP events on its stream), against
+                the 8 TB/s HBM peak, with measured HBM traffic when a
+                counter summary for the current kernel sources exists;
+  cpu_baseline  the oracle (binary64 CPU reference) timed on the host cores
+                on full steps of the same workload;
+  cases         each of the four GEMVs alone;
+  secondary     the other workloads (Q4_0 GEMV, prefill GEMMs, codebook
+                kinds, routed experts), each timed the same way.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+F16_MFMA_PEAK_TFLOPS = 2500.0
+MALL_DEFEAT_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_digest() -> str:
+    """Hash of the HIP sources, to tell whether a stored counter summary
+    still describes the kernels being timed."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gguf_block_quantized_kind_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+class Case:
+    """One matmul (GEMV, GEMM or routed experts) on rotating weight copies."""
+
+    def __init__(self, name, kind, launch, copies, weight_bytes, flops):
+        self.name, self.kind, self.launch = name, kind, launch
+        self.copies, self.weight_bytes, self.flops = copies, weight_bytes, flops
+
+
+def make_copies(torch, W: np.ndarray, min_copies: int = 2):
+    base = torch.from_numpy(W).cuda()
+    n = max(min_copies, math.ceil(MALL_DEFEAT_BYTES / base.numel()) + 1)
+    return [base] + [base.clone() for _ in range(n - 1)]
+
+
+def capture(torch, fn, count: int):
+    """A HIP graph of `count` consecutive calls fn(i)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            fn(i)
+    return g
+
+
+def time_launches(torch, case: Case, launches: int) -> float:
+    """Average duration of one launch of `case`, from HIP events on the
+    stream the graph of back-to-back launches replays on (seconds)."""
+    g = capture(torch, lambda i: case.launch(i), launches)
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        g.replay()
+        end.record()
+        end.synchronize()
+        best = min(best, start.elapsed_time(end) / 1e3 / launches)
+    del g
+    return best
+
+
+def gemv_cases(torch, qmm, wl):
+    cases = []
+    for kind in ("Q4_K", "Q6_K"):
+        w1 = next(w for w in wl.C2 if w.kind == kind and w.M == 1)
+        W = w1.weights()
+        copies = make_copies(torch, W)
+        for M in (1, 8):
+            w = next(w for w in wl.C2 if w.kind == kind and w.M == M)
+            x = torch.from_numpy(w.x()).cuda()
+            y = torch.empty((M, w.N), dtype=torch.float32, device="cuda")
+            # M=1 reads even copies, M=8 odd ones, so one step never re-reads a copy.
+            par = 0 if M == 1 else 1
+
+            def launch(i, kind=kind, x=x, y=y, M=M, w=w, copies=copies, par=par):
+                c = copies[(2 * i + par) % len(copies)]
+                qmm.qmm_gemv_ex(kind, c, x, y, M, w.N, w.K)
+
+            cases.append(Case(w.name, kind, launch, copies, w.weight_bytes, w.flops))
+    return cases
+
+
+def secondary_cases(torch, qmm, wl):
+    cases = []
+    for w in wl.C1 + wl.C3 + wl.C4:
+        copies = make_copies(torch, w.weights())
+        x = torch.from_numpy(w.x()).cuda()
+        y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+
+        def launch(i, w=w, x=x, y=y, copies=copies):
+            qmm.qmm_matmul(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
+
+        cases.append(Case(w.name, w.kind, launch, copies, w.weight_bytes, w.flops))
+    for e in wl.C5:
+        ids_np = e.ids()
+        ids = torch.from_numpy(ids_np).cuda()
+        touched = e.touched_bytes(ids_np)
+        for mat, N, K, X, per_slot in (("gate_up", e.N_gu, e.K_gu, e.x(), 0),
+                                       ("down", e.N_d, e.K_d, e.h(), 1)):
+            W = e.w_gu() if mat == "gate_up" else e.w_d()
+            copies = make_copies(torch, W)
+            Xd = torch.from_numpy(X).cuda()
+            Y = torch.empty((e.M, e.topk, N), dtype=torch.float32, device="cuda")
+            ws = torch.empty((qmm.qmm_moe_workspace_bytes(e.E, e.M, e.topk) + 3) // 4,
+                             dtype=torch.int32, device="cuda")
+            row_b = wl.row_bytes(e.kind, K)
+            distinct = np.unique(ids_np).size
+
+            def launch(i, e=e, N=N, K=K, Xd=Xd, Y=Y, ws=ws, per_slot=per_slot, copies=copies, ids=ids):
+                qmm.qmm_moe(e.kind, copies[i % len(copies)], e.E, ids, e.topk, Xd, per_slot, Y,
+                            e.M, N, K, ws)
+
+            cases.append(Case(f"{e.name}_{mat}", e.kind, launch, copies, distinct * N * row_b,
+                              2 * e.M * e.topk * N * K))
+        del touched
+    return cases
+
+
+def describe(case: Case, seconds: float) -> dict:
+    gbs = case.weight_bytes / seconds / 1e9
+    tflops = case.flops / seconds / 1e12
+    out = {"us_per_launch": round(seconds * 1e6, 3), "weight_bytes": case.weight_bytes,
+           "weight_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "TFLOPs": round(tflops, 2)}
+    if "_m512" in case.name or "_m256" in case.name:
+        out["mfma_f16_frac"] = round(tflops / F16_MFMA_PEAK_TFLOPS, 4)
+    return out
+
+
+def measured_traffic(kernel_case: str):
+    """HBM bytes per launch from a stored rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("source_digest") != source_digest():
+        return None
+    entry = data.get("cases", {}).get(kernel_case)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, target_seconds: float) -> dict:
+    import oracle
+
+    orc = oracle.default()
+    data = []
+    for w in wl.C2:
+        data.append((w, w.weights(), w.x()))
+    total_bytes, steps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for w, W, X in data:
+            orc.matmul(w.kind, W, w.K, X)
+            total_bytes += w.weight_bytes
+        steps += 1
+        if time.perf_counter() - t0 >= target_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": orc.max_threads(),
+            "kind": "oracle",
+            "sample": (f"{steps} full step(s): Q4_K and Q6_K, M=1 and M=8, N=14336, K=4096, "
+                       f"binary64 decode + matmul + bound, no cache rotation, {dt:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+
+    import torch
+
+    import gguf_block_quantized_kind_amd as qmm
+    import workloads as wl
+
+    torch.cuda.set_device(0)
+    qmm.load_library()
+    props = torch.cuda.get_device_properties(0)
+
+    cases = gemv_cases(torch, qmm, wl)
+    for c in cases:  # eager once: loads the code objects before capture
+        c.launch(0)
+    torch.cuda.synchronize()
+
+    def step(t):
+        for c in cases:
+            c.launch(t)
+
+    per_graph = 8  # copies are >= 2 * 8 deep, so no copy repeats inside a graph
+    main_graph = capture(torch, step, per_graph)
+
+    def run(n):
+        for _ in range(n // per_graph):
+            main_graph.replay()
+        rem = n % per_graph
+        if rem:
+            g = capture(torch, step, rem)
+            g.replay()
+            torch.cuda.synchronize()
+            del g
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    rem_graph = capture(torch, step, args.steps % per_graph) if args.steps % per_graph else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps // per_graph):
+        main_graph.replay()
+    if rem_graph is not None:
+        rem_graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    bytes_per_step = sum(c.weight_bytes for c in cases)
+    value = bytes_per_step * args.steps / elapsed / 1e9
+
+    per_case = {c.name: describe(c, time_launches(torch, c, 64)) for c in cases}
+    dominant = max(cases, key=lambda c: per_case[c.name]["us_per_launch"])
+    dom = per_case[dominant.name]
+    achieved = dominant.weight_bytes / (dom["us_per_launch"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dominant.name),
+                "kernel": f"qmm GEMV {dominant.name}", "algorithmic_bytes_per_launch": dominant.weight_bytes}
+
+    secondary = {}
+    if not args.no_secondary:
+        del main_graph, rem_graph
+        for c in cases:
+            c.copies.clear()
+        torch.cuda.empty_cache()
+        for c in secondary_cases(torch, qmm, wl):
+            c.launch(0)
+            torch.cuda.synchronize()
+            secondary[c.name] = describe(c, time_launches(torch, c, 32))
+            c.copies.clear()
+            torch.cuda.empty_cache()
+
+    cpu = cpu_baseline(wl, args.cpu_seconds) if args.cpu_seconds > 0 else None
+
+    line = {
+        "metric": "quantized GEMV weight GB/s (% of HBM peak); prefill GEMM TFLOP/s (% MFMA peak)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV, Q4_K and Q6_K weights, M=1 and M=8, N=14336, K=4096, "
+                               "f32 activations, one launch per (kind, M) per step",
+                   "weight_bytes_per_step": bytes_per_step, "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+                   "device": props.name, "cus": props.multi_processor_count},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "cases": per_case,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

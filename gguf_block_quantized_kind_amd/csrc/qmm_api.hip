@@ -1,0 +1,221 @@
+// qmm_api.hip -- the exported C ABI: argument checks in the documented
+// order, then dispatch to the launchers.  Nothing here allocates.
+#include <stdarg.h>
+#include <string.h>
+
+#include <cstdio>
+#include <string>
+
+#include "../../include/qmm.h"
+#include "qmm_internal.h"
+
+#define QMM_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return QMM_OK;
+}
+
+struct KindInfo {
+  int id;
+  const char *name;
+  int block_bytes;
+  int block_elems;
+};
+
+// The kind table (GGUF type ids; ferrox-cuda 0.21.0 mul_mm.rs, KINDS).
+constexpr KindInfo kKinds[] = {
+    {QMM_Q8_0, "Q8_0", 34, 32},     {QMM_Q4_0, "Q4_0", 18, 32},     {QMM_Q5_0, "Q5_0", 22, 32},
+    {QMM_Q2_K, "Q2_K", 84, 256},    {QMM_Q3_K, "Q3_K", 110, 256},   {QMM_Q4_K, "Q4_K", 144, 256},
+    {QMM_Q5_K, "Q5_K", 176, 256},   {QMM_Q6_K, "Q6_K", 210, 256},   {QMM_IQ4_NL, "IQ4_NL", 18, 32},
+    {QMM_IQ4_XS, "IQ4_XS", 136, 256}, {QMM_MXFP4, "MXFP4", 17, 32},
+};
+
+const KindInfo *find_kind(int kind) {
+  for (const KindInfo &k : kKinds)
+    if (k.id == kind) return &k;
+  return nullptr;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Empty shape, then kind, then K alignment: the order of ferrox-cuda
+// mul_mm.rs validate_shape.  K and the per-launch sizes must also fit the
+// kernels' 32-bit indices.
+int check_shape(int kind, int64_t M, int64_t N, int64_t K, const KindInfo **out) {
+  if (M <= 0 || N <= 0 || K <= 0)
+    return fail(QMM_ERR_EMPTY_SHAPE, "empty shape: M=%lld N=%lld K=%lld", (long long)M, (long long)N,
+                (long long)K);
+  const KindInfo *k = find_kind(kind);
+  if (!k) return fail(QMM_ERR_UNSUPPORTED_KIND, "kind %d is not one of the eleven supported kinds", kind);
+  if (K % k->block_elems != 0)
+    return fail(QMM_ERR_K_NOT_BLOCK_ALIGNED, "K=%lld is not a whole number of %s blocks (%d elements)",
+                (long long)K, k->name, k->block_elems);
+  if (K > (int64_t)1 << 30 || N > (int64_t)1 << 40)
+    return fail(QMM_ERR_BAD_ARG, "K=%lld or N=%lld exceeds the supported range", (long long)K,
+                (long long)N);
+  *out = k;
+  return QMM_OK;
+}
+
+int check_dtype(int dtype) {
+  if (dtype != QMM_F32 && dtype != QMM_F16) return fail(QMM_ERR_BAD_DTYPE, "dtype %d is neither QMM_F32 nor QMM_F16", dtype);
+  return QMM_OK;
+}
+
+int check_act(const void *x, int dtype, const char *what) {
+  if (!x) return fail(QMM_ERR_BAD_ARG, "%s is NULL", what);
+  if (!aligned(x, dtype == QMM_F32 ? 4 : 2))
+    return fail(QMM_ERR_BAD_ARG, "%s is not aligned to its element size", what);
+  return QMM_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(QMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+QMM_EXPORT int qmm_gemv_ex(int kind, const void *W, const void *x, int x_dtype, float *y, int64_t M,
+                           int64_t N, int64_t K, void *stream) {
+  const KindInfo *k;
+  int st = check_shape(kind, M, N, K, &k);
+  if (st) return st;
+  if ((st = check_dtype(x_dtype))) return st;
+  if (!W || !y) return fail(QMM_ERR_BAD_ARG, "W or y is NULL");
+  if ((st = check_act(x, x_dtype, "x"))) return st;
+  if (!aligned(y, 4)) return fail(QMM_ERR_BAD_ARG, "y is not 4-byte aligned");
+  if (M > QMM_GEMV_MAX_M) return fail(QMM_ERR_BAD_ARG, "GEMV takes 1..%d tokens, got M=%lld", QMM_GEMV_MAX_M, (long long)M);
+  return hip_status(qmm::launch_gemv(kind, (const uint8_t *)W, x, x_dtype == QMM_F16, y, (int)M, N, K,
+                                     (hipStream_t)stream),
+                    "gemv launch");
+}
+
+QMM_EXPORT int qmm_gemv(int kind, const void *W, const float *x, float *y, int64_t N, int64_t K) {
+  return qmm_gemv_ex(kind, W, x, QMM_F32, y, 1, N, K, nullptr);
+}
+
+QMM_EXPORT int qmm_gemm_ex(int kind, const void *W, const void *A, int a_dtype, float *C, int64_t M,
+                           int64_t N, int64_t K, void *stream) {
+  const KindInfo *k;
+  int st = check_shape(kind, M, N, K, &k);
+  if (st) return st;
+  if ((st = check_dtype(a_dtype))) return st;
+  if (!W || !C) return fail(QMM_ERR_BAD_ARG, "W or C is NULL");
+  if ((st = check_act(A, a_dtype, "A"))) return st;
+  if (!aligned(C, 4)) return fail(QMM_ERR_BAD_ARG, "C is not 4-byte aligned");
+  if (M > (int64_t)65535 * 64) return fail(QMM_ERR_BAD_ARG, "M=%lld exceeds the supported range", (long long)M);
+  return hip_status(qmm::launch_gemm(kind, (const uint8_t *)W, A, a_dtype == QMM_F16, C, M, N, K,
+                                     (hipStream_t)stream),
+                    "gemm launch");
+}
+
+QMM_EXPORT int qmm_gemm(int kind, const void *W, const void *A, float *C, int64_t M, int64_t N, int64_t K) {
+  return qmm_gemm_ex(kind, W, A, QMM_F16, C, M, N, K, nullptr);
+}
+
+QMM_EXPORT int qmm_matmul(int kind, const void *W, const void *A, int a_dtype, float *C, int64_t M,
+                          int64_t N, int64_t K, void *stream) {
+  if (M >= 1 && M <= QMM_GEMV_MAX_M) return qmm_gemv_ex(kind, W, A, a_dtype, C, M, N, K, stream);
+  return qmm_gemm_ex(kind, W, A, a_dtype, C, M, N, K, stream);
+}
+
+QMM_EXPORT size_t qmm_moe_workspace_bytes(int64_t E, int64_t M, int64_t topk) {
+  if (E <= 0 || M < 0 || topk <= 0) return 0;
+  return qmm::moe_workspace_bytes(E, M, topk);
+}
+
+QMM_EXPORT int qmm_moe(int kind, const void *W, int64_t E, const int32_t *ids, int64_t topk, const void *X,
+                       int x_dtype, int x_per_slot, float *Y, int64_t M, int64_t N, int64_t K, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  const KindInfo *k;
+  if (E <= 0 || topk <= 0)
+    return fail(QMM_ERR_EMPTY_SHAPE, "empty shape: E=%lld topk=%lld", (long long)E, (long long)topk);
+  int st = check_shape(kind, M, N, K, &k);
+  if (st) return st;
+  if ((st = check_dtype(x_dtype))) return st;
+  if (!W || !ids || !Y) return fail(QMM_ERR_BAD_ARG, "W, ids or Y is NULL");
+  if ((st = check_act(X, x_dtype, "X"))) return st;
+  if (!aligned(ids, 4) || !aligned(Y, 4)) return fail(QMM_ERR_BAD_ARG, "ids or Y is not 4-byte aligned");
+  if (x_per_slot != 0 && x_per_slot != 1) return fail(QMM_ERR_BAD_ARG, "x_per_slot must be 0 or 1");
+  if (E > qmm::kMoeMaxExperts) return fail(QMM_ERR_BAD_ARG, "E=%lld exceeds %lld experts", (long long)E, (long long)qmm::kMoeMaxExperts);
+  if (M * topk > ((int64_t)1 << 31) - 1) return fail(QMM_ERR_BAD_ARG, "M*topk exceeds 2^31-1");
+  if (N > ((int64_t)1 << 31) / 4) return fail(QMM_ERR_BAD_ARG, "N=%lld exceeds the supported range", (long long)N);
+  const size_t need = qmm::moe_workspace_bytes(E, M, topk);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 4))
+    return fail(QMM_ERR_WORKSPACE, "workspace needs %zu bytes (4-byte aligned), got %zu", need, workspace_bytes);
+  return hip_status(qmm::launch_moe(kind, (const uint8_t *)W, E, ids, topk, X, x_dtype == QMM_F16, x_per_slot,
+                                    Y, M, N, K, workspace, (hipStream_t)stream),
+                    "moe launch");
+}
+
+QMM_EXPORT int qmm_dequant(int kind, const void *W, float *out, int64_t n_elems, void *stream) {
+  if (n_elems <= 0) return fail(QMM_ERR_EMPTY_SHAPE, "empty shape: n_elems=%lld", (long long)n_elems);
+  const KindInfo *k = find_kind(kind);
+  if (!k) return fail(QMM_ERR_UNSUPPORTED_KIND, "kind %d is not one of the eleven supported kinds", kind);
+  if (n_elems % k->block_elems != 0)
+    return fail(QMM_ERR_K_NOT_BLOCK_ALIGNED, "n_elems=%lld is not a whole number of %s blocks", (long long)n_elems, k->name);
+  if (!W || !out) return fail(QMM_ERR_BAD_ARG, "W or out is NULL");
+  if (!aligned(out, 4)) return fail(QMM_ERR_BAD_ARG, "out is not 4-byte aligned");
+  if (n_elems > ((int64_t)1 << 40)) return fail(QMM_ERR_BAD_ARG, "n_elems exceeds the supported range");
+  return hip_status(qmm::launch_dequant(kind, (const uint8_t *)W, out, n_elems / k->block_elems, (hipStream_t)stream),
+                    "dequant launch");
+}
+
+QMM_EXPORT int64_t qmm_row_bytes(int kind, int64_t K) {
+  const KindInfo *k = find_kind(kind);
+  if (!k || K < 0 || K % k->block_elems != 0) return -1;
+  return (K / k->block_elems) * k->block_bytes;
+}
+
+QMM_EXPORT int qmm_block_geometry(int kind, int *block_bytes, int *block_elems) {
+  const KindInfo *k = find_kind(kind);
+  if (!k) return fail(QMM_ERR_UNSUPPORTED_KIND, "kind %d is not one of the eleven supported kinds", kind);
+  if (block_bytes) *block_bytes = k->block_bytes;
+  if (block_elems) *block_elems = k->block_elems;
+  return ok();
+}
+
+QMM_EXPORT int qmm_kind_from_name(const char *name) {
+  if (!name) return -1;
+  for (const KindInfo &k : kKinds)
+    if (strcmp(k.name, name) == 0) return k.id;
+  return -1;
+}
+
+QMM_EXPORT const char *qmm_kind_name(int kind) {
+  const KindInfo *k = find_kind(kind);
+  return k ? k->name : nullptr;
+}
+
+QMM_EXPORT const char *qmm_status_string(int status) {
+  switch (status) {
+    case QMM_OK: return "ok";
+    case QMM_ERR_EMPTY_SHAPE: return "empty shape";
+    case QMM_ERR_UNSUPPORTED_KIND: return "unsupported kind";
+    case QMM_ERR_K_NOT_BLOCK_ALIGNED: return "K is not a whole number of blocks";
+    case QMM_ERR_BAD_DTYPE: return "bad activation dtype";
+    case QMM_ERR_BAD_ARG: return "bad argument";
+    case QMM_ERR_HIP: return "HIP launch failed";
+    case QMM_ERR_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+QMM_EXPORT const char *qmm_last_error(void) { return g_last_error.c_str(); }

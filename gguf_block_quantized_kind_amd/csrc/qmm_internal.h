@@ -1,0 +1,33 @@
+// qmm_internal.h -- host-side launchers behind the C ABI (not exported).
+// Each launcher assumes its arguments were validated by qmm_api.hip and
+// returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmm {
+
+// out[i] for i < n_blocks * block_elems.
+hipError_t launch_dequant(int kind, const uint8_t *W, float *out, int64_t n_blocks, hipStream_t s);
+
+// y[M][N] = x[M][K] . W^T, 1 <= M <= 8, x f32 (x_f16 == 0) or f16.
+hipError_t launch_gemv(int kind, const uint8_t *W, const void *x, int x_f16, float *y,
+                       int M, int64_t N, int64_t K, hipStream_t s);
+
+// C[M][N] = A[M][K] . W^T, any M >= 1, A f32 (a_f16 == 0) or f16.
+hipError_t launch_gemm(int kind, const uint8_t *W, const void *A, int a_f16, float *C,
+                       int64_t M, int64_t N, int64_t K, hipStream_t s);
+
+// Routed expert products; see qmm_moe in qmm.h.  `ws` holds
+// moe_workspace_bytes(E, M, topk) bytes.
+size_t moe_workspace_bytes(int64_t E, int64_t M, int64_t topk);
+hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids, int64_t topk,
+                      const void *X, int x_f16, int x_per_slot, float *Y, int64_t M, int64_t N,
+                      int64_t K, void *ws, hipStream_t s);
+
+// Largest expert count the routing prologue handles.
+constexpr int64_t kMoeMaxExperts = 4096;
+
+}  // namespace qmm

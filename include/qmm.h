@@ -1,0 +1,141 @@
+/*
+ * qmm.h -- matrix multiply against GGUF block-quantized weights on AMD
+ * MI355X (gfx950).  C ABI: plain pointers and sizes, no framework types.
+ *
+ * The operation (all entry points):  y[m][n] = sum_k x[m][k] * w[n][k]
+ *   W  the weight matrix, N rows of K elements.  Each row is K / block_elems
+ *      consecutive GGUF blocks and rows are stored back to back, so row n
+ *      starts at byte n * qmm_row_bytes(kind, K).  ("One output row's blocks
+ *      are contiguous": redgpu/Vulkore examples/llm/quant_test.cpp, the fused
+ *      dequant-matvec section; ferrox-cuda 0.21.0 mul_mm.rs, BODY_SRC and
+ *      validate_shape.)  Any byte alignment of W is accepted.
+ *   x  activations, row-major [M][K], f32 or f16 (QMM_F32 / QMM_F16), aligned
+ *      to their element size.
+ *   y  output, row-major [M][N] f32 (y[m * N + n]; ferrox-cuda mul_mm.rs,
+ *      BODY_SRC, writes dst[token * n_rows + row]).  Overwritten, never
+ *      accumulated into.
+ * Each weight element w[n][k] is decoded from its block by its kind's rule:
+ * scale * code + bias for the affine kinds, scale * table[code] for the
+ * codebook kinds (ferrox-cuda 0.20.0 mul_mm_kinds/codebook.rs, module docs).
+ *
+ * Numerics.  Accumulation is in f32.  The decode GEMV keeps every weight
+ * exact; the prefill GEMM rounds each decoded weight once to f16 (relative
+ * error <= 2^-11) and, for f32 activations, splits each activation into two
+ * f16 parts so that only one operand is ever rounded.  Results satisfy
+ * |y - y_exact| <= 1e-3 * sum_k |w||x| + 1e-6 per element.
+ *
+ * Ownership and asynchrony.  The caller owns every buffer; the library never
+ * allocates device memory.  W, x and ids are read only.  Calls that take a
+ * `stream` (a hipStream_t; NULL is the default stream) enqueue their kernels
+ * there and return without synchronizing; a fault inside a kernel surfaces at
+ * the caller's next synchronization.
+ *
+ * Errors.  Shape and argument errors are returned before anything is
+ * launched, checked in this order: empty shape -> unsupported kind -> K not a
+ * whole number of blocks -> bad dtype -> null pointer, misaligned activation
+ * or out-of-range M -> workspace too small.  A refused call computes nothing
+ * (ferrox-cuda mul_mm.rs: kind_by_name and MulMmUnsupported -- a kind or
+ * shape the kernel cannot do must be refused by name, never computed some
+ * other way).  A failed launch returns QMM_ERR_HIP.  qmm_last_error() gives
+ * the calling thread's most recent message.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The eleven kinds, by GGUF type id (ferrox-cuda mul_mm.rs, KINDS; MXFP4 is
+ * ggml type tag 39 per codebook.rs, the MXFP4 row). */
+enum qmm_kind {
+    QMM_Q4_0 = 2,    /*  18 B /  32: f16 d, 16 B nibbles; d*(q-8)               */
+    QMM_Q5_0 = 6,    /*  22 B /  32: f16 d, u32 qh, 16 B nibbles; d*(q-16)      */
+    QMM_Q8_0 = 8,    /*  34 B /  32: f16 d, 32 int8; d*q                        */
+    QMM_Q2_K = 10,   /*  84 B / 256: 16 scale/min bytes, 64 B 2-bit, d, dmin    */
+    QMM_Q3_K = 11,   /* 110 B / 256: 32 B hmask, 64 B 2-bit, 12 B scales, d    */
+    QMM_Q4_K = 12,   /* 144 B / 256: d, dmin, 12 B 6-bit scales/mins, 128 B     */
+    QMM_Q5_K = 13,   /* 176 B / 256: d, dmin, 12 B scales/mins, 32 B qh, 128 B  */
+    QMM_Q6_K = 14,   /* 210 B / 256: 128 B ql, 64 B qh, 16 int8 scales, d       */
+    QMM_IQ4_NL = 20, /*  18 B /  32: f16 d, 16 B codes into a 16-entry table    */
+    QMM_IQ4_XS = 23, /* 136 B / 256: d, scales_h, scales_l[4], 128 B codes      */
+    QMM_MXFP4 = 39   /*  17 B /  32: E8M0 scale byte, 16 B of E2M1 codes        */
+};
+
+enum qmm_dtype { QMM_F32 = 0, QMM_F16 = 1 };
+
+enum qmm_status {
+    QMM_OK = 0,
+    QMM_ERR_EMPTY_SHAPE = 1,          /* a zero dimension: nothing to launch   */
+    QMM_ERR_UNSUPPORTED_KIND = 2,     /* not one of the eleven kinds           */
+    QMM_ERR_K_NOT_BLOCK_ALIGNED = 3,  /* K is not a whole number of blocks     */
+    QMM_ERR_BAD_DTYPE = 4,            /* activation dtype not QMM_F32/QMM_F16  */
+    QMM_ERR_BAD_ARG = 5,              /* null/misaligned pointer, bad M, ids   */
+    QMM_ERR_HIP = 6,                  /* a HIP launch failed                   */
+    QMM_ERR_WORKSPACE = 7             /* workspace missing or too small        */
+};
+
+/* Largest M the decode GEMV takes in one call. */
+#define QMM_GEMV_MAX_M 8
+
+/* Decode GEMV, M = 1: y[N] = W . x[K], f32 x, on the default stream.
+ * ferrox-cuda mul_mm.rs worth_a_gemm: one token is a matvec. */
+int qmm_gemv(int kind, const void *W, const float *x, float *y, int64_t N, int64_t K);
+
+/* Decode GEMV, 1 <= M <= QMM_GEMV_MAX_M tokens, f32 or f16 x, on `stream`.
+ * Every weight is decoded exactly; products accumulate in f32. */
+int qmm_gemv_ex(int kind, const void *W, const void *x, int x_dtype, float *y,
+                int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Prefill GEMM: C[M][N] = A[M][K] . W^T with f16 A, on the default stream.
+ * Weight tiles are decoded to f16 and multiplied on the matrix cores with f32
+ * accumulation (inferencelayer cublas_prefill.rs, CublasPrefill::gemm: f16
+ * in, f32 accumulate, y = x . W^T). */
+int qmm_gemm(int kind, const void *W, const void *A, float *C, int64_t M, int64_t N, int64_t K);
+
+/* Prefill GEMM for any M >= 1 with f32 or f16 A, on `stream`. */
+int qmm_gemm_ex(int kind, const void *W, const void *A, int a_dtype, float *C,
+                int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Either path: the GEMV for M <= QMM_GEMV_MAX_M, the GEMM above. */
+int qmm_matmul(int kind, const void *W, const void *A, int a_dtype, float *C,
+               int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Routed expert products, every expert in one grouped launch (plus a small
+ * routing prologue).  W holds E experts of N rows each, back to back: expert
+ * e's row n starts at byte (e * N + n) * qmm_row_bytes(kind, K).
+ * ids is [M][topk] int32 in [0, E).  For token t and slot s with
+ * e = ids[t][s]:  Y[t][s][:] = W_e . x, where x is X[t] when x_per_slot is 0
+ * (X is [M][K]) and X[t][s] when it is 1 (X is [M][topk][K]).  Y is
+ * [M][topk][N] f32.  A pair whose id lies outside [0, E) is skipped and its Y
+ * row is left as it was; W is never read outside its E experts.
+ * workspace is device memory of at least
+ * qmm_moe_workspace_bytes(E, M, topk) bytes, overwritten by the call; calls
+ * that share a workspace must not overlap. */
+int qmm_moe(int kind, const void *W, int64_t E, const int32_t *ids, int64_t topk,
+            const void *X, int x_dtype, int x_per_slot, float *Y,
+            int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+            void *stream);
+size_t qmm_moe_workspace_bytes(int64_t E, int64_t M, int64_t topk);
+
+/* Dequantize n_elems consecutive elements (whole blocks) of W to f32 on
+ * `stream`.  Every value is the f32 rounding of the exact value, evaluated
+ * scale first with IEEE signed zeros (so MXFP4 code 8 gives -0.0). */
+int qmm_dequant(int kind, const void *W, float *out, int64_t n_elems, void *stream);
+
+/* Geometry and names. */
+int64_t qmm_row_bytes(int kind, int64_t K);  /* -1: bad kind or K not block-aligned */
+int qmm_block_geometry(int kind, int *block_bytes, int *block_elems);  /* QMM_OK or error */
+int qmm_kind_from_name(const char *gguf_name); /* -1 if the name is not one of the eleven */
+const char *qmm_kind_name(int kind);           /* NULL for an unsupported kind */
+const char *qmm_status_string(int status);
+const char *qmm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

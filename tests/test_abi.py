@@ -1,0 +1,157 @@
+"""The C-ABI library without a GPU: it loads, exports every function
+include/qmm.h declares, agrees with the oracle and the generators on block
+geometry, resolves exactly the eleven kinds by name, and refuses bad calls
+with the documented status, in the documented order, before launching
+anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gguf_block_quantized_kind_amd as qmm
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+OK, EMPTY, KIND, KALIGN, DTYPE, ARG, HIP, WS = range(8)
+FAKE = 0x1000  # never dereferenced: every call below is refused first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(qmm.LIBRARY):
+        import gguf_block_quantized_kind_amd._build as b
+        b.build()
+    return qmm.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(qmm_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("qmm_gemv", "qmm_gemm", "qmm_gemv_ex", "qmm_gemm_ex", "qmm_moe",
+                     "qmm_moe_workspace_bytes", "qmm_dequant", "qmm_row_bytes"):
+        assert required in names
+
+
+def test_every_declared_function_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", qmm.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (qmm_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        getattr(lib, n)
+
+
+def test_geometry_matches_oracle_and_generators(lib, oracle_mod):
+    for name, (kid, bb, be) in wl.KINDS.items():
+        assert qmm.qmm_kind_from_name(name) == kid
+        assert qmm.qmm_kind_name(kid) == name
+        assert qmm.qmm_block_geometry(kid) == (bb, be) == oracle_mod.block_geometry(kid)
+        for K in (be, 4096, 2048, 768):
+            if K % be == 0:
+                assert qmm.qmm_row_bytes(kid, K) == wl.row_bytes(name, K)
+        assert qmm.qmm_row_bytes(kid, be + 16) == -1
+
+
+def test_absent_kinds_do_not_resolve(lib):
+    for absent in ("Q4_1", "Q5_1", "Q8_1", "IQ1_S", "IQ2_XXS", "IQ3_S", "q4_0", ""):
+        assert qmm.qmm_kind_from_name(absent) == -1
+    for kid in (0, 1, 3, 7, 9, 15, 16, 19, 21, 22, 40):
+        assert qmm.qmm_kind_name(kid) is None
+        assert lib.qmm_row_bytes(kid, 4096) == -1
+        b, e = ctypes.c_int(), ctypes.c_int()
+        assert lib.qmm_block_geometry(kid, ctypes.byref(b), ctypes.byref(e)) == KIND
+
+
+def test_gemv_refusals_in_order(lib):
+    g = lib.qmm_gemv_ex
+    # empty beats everything else
+    assert g(3, None, None, 9, None, 0, 10, 48, None) == EMPTY
+    assert g(2, FAKE, FAKE, 0, FAKE, 1, 0, 4096, None) == EMPTY
+    assert g(2, FAKE, FAKE, 0, FAKE, 1, 10, 0, None) == EMPTY
+    # then the kind
+    assert g(3, None, None, 9, None, 1, 10, 48, None) == KIND
+    assert "kind 3" in qmm.qmm_last_error()
+    # then K against the block
+    assert g(2, None, None, 9, None, 1, 10, 48, None) == KALIGN
+    assert g(12, None, None, 9, None, 1, 10, 512 + 32, None) == KALIGN
+    # then the dtype
+    assert g(2, None, None, 9, None, 1, 10, 64, None) == DTYPE
+    # then pointers, alignment and M
+    assert g(2, None, FAKE, 0, FAKE, 1, 10, 64, None) == ARG
+    assert g(2, FAKE, None, 0, FAKE, 1, 10, 64, None) == ARG
+    assert g(2, FAKE, FAKE, 0, None, 1, 10, 64, None) == ARG
+    assert g(2, FAKE, FAKE + 2, 0, FAKE, 1, 10, 64, None) == ARG   # f32 x at 2 bytes
+    assert g(2, FAKE, FAKE, 0, FAKE + 2, 1, 10, 64, None) == ARG   # y misaligned
+    assert g(2, FAKE, FAKE, 0, FAKE, 9, 10, 64, None) == ARG       # M > 8
+    assert lib.qmm_gemv(2, None, FAKE, FAKE, 10, 64) == ARG
+
+
+def test_gemm_refusals_in_order(lib):
+    g = lib.qmm_gemm_ex
+    assert g(2, FAKE, FAKE, 1, FAKE, 0, 10, 64, None) == EMPTY
+    assert g(5, FAKE, FAKE, 1, FAKE, 10, 10, 64, None) == KIND
+    assert g(14, FAKE, FAKE, 1, FAKE, 10, 10, 64, None) == KALIGN
+    assert g(14, FAKE, FAKE, 2, FAKE, 10, 10, 256, None) == DTYPE
+    assert g(14, FAKE, None, 1, FAKE, 10, 10, 256, None) == ARG
+    assert g(14, FAKE, FAKE + 1, 1, FAKE, 10, 10, 256, None) == ARG  # f16 A at an odd address
+    assert lib.qmm_gemm(14, FAKE, FAKE, None, 10, 10, 256) == ARG
+    assert lib.qmm_matmul(39, FAKE, FAKE, 0, FAKE, 10, 10, 48, None) == KALIGN
+
+
+def test_moe_refusals_in_order(lib):
+    g = lib.qmm_moe
+    ws_need = lib.qmm_moe_workspace_bytes(128, 16, 8)
+    assert ws_need == (128 + 129 + 16 * 8) * 4
+    args = dict(kind=12, W=FAKE, E=128, ids=FAKE, topk=8, X=FAKE, dt=1, per=0, Y=FAKE, M=16, N=1536,
+                K=2048, ws=FAKE, wsb=ws_need, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return g(a["kind"], a["W"], a["E"], a["ids"], a["topk"], a["X"], a["dt"], a["per"], a["Y"],
+                 a["M"], a["N"], a["K"], a["ws"], a["wsb"], a["s"])
+
+    assert call(E=0) == EMPTY
+    assert call(topk=0) == EMPTY
+    assert call(M=0) == EMPTY
+    assert call(kind=1) == KIND
+    assert call(K=2048 + 32) == KALIGN
+    assert call(dt=5) == DTYPE
+    assert call(ids=None) == ARG
+    assert call(per=2) == ARG
+    assert call(E=5000) == ARG
+    assert call(ws=None) == WS
+    assert call(wsb=ws_need - 1) == WS
+    assert "workspace" in qmm.qmm_last_error()
+
+
+def test_dequant_refusals(lib):
+    assert lib.qmm_dequant(2, FAKE, FAKE, 0, None) == EMPTY
+    assert lib.qmm_dequant(4, FAKE, FAKE, 32, None) == KIND
+    assert lib.qmm_dequant(2, FAKE, FAKE, 33, None) == KALIGN
+    assert lib.qmm_dequant(2, None, FAKE, 32, None) == ARG
+    assert lib.qmm_dequant(2, FAKE, FAKE + 1, 32, None) == ARG
+
+
+def test_status_strings(lib):
+    for st in range(8):
+        assert qmm.qmm_status_string(st)
+    assert qmm.qmm_status_string(123) == "unknown status"
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = qmm._lib
+    qmm._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            qmm.load_library(str(tmp_path / "missing.so"))
+    finally:
+        qmm._lib = saved

@@ -80,7 +80,8 @@ def random_weights(kind, n_rows: int, K: int, g: np.random.Generator,
     * scales="stress": f16 fields take a random sign, a random 10-bit
       mantissa and an exponent field uniform in 8..22 (about 2^-7..2^7), so
       no field is zero, subnormal, Inf or NaN; the E8M0 byte is uniform over
-      0..254.
+      0..252, so every decoded MXFP4 weight (at most 6 * 2^125) is finite
+      in f32.
     """
     name = name_of(kind)
     bb, be = geometry(name)
@@ -100,7 +101,7 @@ def random_weights(kind, n_rows: int, K: int, g: np.random.Generator,
         raw[:, off] = (bits & 0xFF).astype(np.uint8)
         raw[:, off + 1] = (bits >> 8).astype(np.uint8)
     for off in E8M0_FIELDS.get(name, ()):
-        lo, hi = e8m0_range if scales == "config" else (0, 254)
+        lo, hi = e8m0_range if scales == "config" else (0, 252)
         raw[:, off] = g.integers(lo, hi + 1, size=nblk, dtype=np.int64).astype(np.uint8)
     return raw.reshape(n_rows, rb)
 

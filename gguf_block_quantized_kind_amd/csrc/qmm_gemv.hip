@@ -63,6 +63,8 @@ static hipError_t run_gemv(const uint8_t *W, const void *x, int x_f16, float *y,
 
 hipError_t launch_gemv(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int M,
                        int64_t N, int64_t K, hipStream_t s) {
+  const hipError_t e = launch_gemv_mfma(kind, W, x, x_f16, y, M, N, K, s);
+  if (e != hipErrorNotSupported) return e;
   switch (kind) {
 #define QMM_CASE(K_) \
   case K_:           \

@@ -1,0 +1,263 @@
+// qmm_gemv_mfma.h -- decode GEMV on the matrix cores, for M <= 8 tokens.
+//
+// Roles.  y[t][n] = sum_k x[t][k] w[n][k] is computed as D = A . B with
+// v_mfma_f32_16x16x32_f16: A (16 x 32) holds activations (row i = token i,
+// rows >= M are zero), B (32 x 16) holds weights (column j = weight row j of a
+// 16-row tile).  In the D layout lane l holds D[4*(l/16) + q][l % 16], so
+// every lane's outputs belong to one weight row -- the row whose bytes that
+// lane decoded -- and per-row scales are applied with no data exchange.
+//
+// Exact weights.  The B operand is an exact f16 integer: the block's code
+// with its integer sub-block scale folded in where the product fits in f16's
+// 11-bit significand (Q4_K: sc*q <= 63*15), or split into two exactly
+// representable parts (Q6_K: sc*(q-32) = 16*sh*(q-32) + sl*(q-32), each part
+// accumulated on its own and scaled by 16d or d).  The
+// remaining f16 super-block scale d multiplies each super-block's partial
+// sum in f32, and the Q4_K minimum term -dmin*m_j*X_j runs on
+// v_mfma_f32_16x16x4_f32 with exact f32 operands.  The sub-block sums X_j of
+// the activations come from extra MFMAs of the same activation fragments
+// against a 0/1 indicator, so they cost no vector-ALU work.
+//
+// Activations.  f32 activations are rounded once to f16 (relative error
+// <= 2^-11 per product); f16 activations are used as they are.  With exact
+// weights this keeps every output within 1e-3 * sum|w||x| (worst case
+// 2^-11 + the f32 accumulation error), and a unit-vector x still returns the
+// weight exactly.
+//
+// Codes to f16 without conversions: OR-ing a nibble into the mantissa of
+// f16 1024.0 (0x6400) gives 1024 + q (or 1024 + 16q for a high nibble left in
+// place); one packed FMA per pair then removes the offset and applies the
+// folded integer scale exactly.
+#pragma once
+
+#include "qmm_device.h"
+
+namespace qmm {
+namespace gv {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16 bytes from any address (the target allows unaligned vector loads).
+__device__ __forceinline__ u32x4 ld16(const uint8_t *p) {
+  u32x4 v;
+  __builtin_memcpy(&v, p, 16);
+  return v;
+}
+__device__ __forceinline__ u32x2 ld8(const uint8_t *p) {
+  u32x2 v;
+  __builtin_memcpy(&v, p, 8);
+  return v;
+}
+
+__device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+__device__ __forceinline__ uint32_t as_u(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+
+constexpr uint32_t kMagic = 0x64006400u;  // f16 pair (1024, 1024)
+
+// (v & mask) | magic as one v_and_or_b32.  The mask and the magic are passed
+// in registers: a gfx9 VOP3 instruction cannot encode two literal constants,
+// and the compiler would otherwise split this into an AND and an OR.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(mask), "v"(c));
+  return r;
+}
+// Two f16 values 1024 + field, field = v & mask.
+__device__ __forceinline__ uint32_t mag(uint32_t v, uint32_t mask) { return and_or(v, mask, kMagic); }
+
+// Exact fold: fma(e, f, b) is computed exactly and rounded once, and every
+// result here is an integer that f16 represents exactly.
+__device__ __forceinline__ uint32_t fold(uint32_t e, uint32_t f, uint32_t b) {
+  return as_u(__builtin_elementwise_fma(as_h2(e), as_h2(f), as_h2(b)));
+}
+
+__device__ __forceinline__ half8 pack8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(half8, v);
+}
+
+// f32 value of the low or high f16 of a dword.
+__device__ __forceinline__ float lo_f16(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu)); }
+__device__ __forceinline__ float hi_f16(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
+
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma4f32(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Each decoder describes one k-block (the elements that share the f32
+// post-scale) as seen by lane group G = lane / 16 of a 16-row tile:
+//   KB, NSTEP            elements per k-block and MFMA steps per k-block
+//   NPART                B operands per step (2 for a split fold)
+//   HAS_MIN              a minimum term runs on the f32 MFMA
+//   x_off(s, G)          first of the 8 consecutive elements step s gives G;
+//                        inside a step the pairs are ordered 0,2,1,3,4,6,5,7
+//   Raw / load           the lane's bytes of one k-block
+//   Sc / prep            the lane's scales for that k-block
+//   bop(raw, sc, s, p)   B operand p of step s
+//   ind(s, G, i)         1 if A-row i collects the sub-block that step s of
+//                        group G belongs to (indicator for the sums X_j)
+//   post(acc, D, X, sc)  acc += d * D[part] (- dmin * sum m_j X_j)
+
+// ---------------------------------------------------------------------------
+// Q4_K.  Group G decodes the 32 bytes 32G..32G+31 of the codes: low nibbles
+// are elements 64G + [0,32) (sub-block 2G), high nibbles 64G + 32 + [0,32)
+// (sub-block 2G+1).  Step s < 4 takes low nibbles of bytes 8s..8s+7, step
+// s >= 4 the high nibbles of bytes 8(s-4)..; the B value is sc_j * q.
+// ---------------------------------------------------------------------------
+struct DecQ4K {
+  static constexpr int KB = 256, NSTEP = 8, NPART = 1, BYTES = 144;
+  static constexpr bool HAS_MIN = true;
+  struct Raw { u32x4 hdr, q0, q1; };
+  struct Sc { uint32_t f_lo, b_lo, f_hi, b_hi; float d, mn_lo, mn_hi; };
+
+  __device__ static int x_off(int s, int G) { return 64 * G + (s < 4 ? 8 * s : 32 + 8 * (s - 4)); }
+
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+    r.hdr = ld16(blk);
+    r.q0 = ld16(blk + 16 + 32 * G);
+    r.q1 = ld16(blk + 32 + 32 * G);
+  }
+
+  __device__ static Sc prep(const Raw &r, int G) {
+    // Scales and mins of sub-blocks 2G, 2G+1 from the 12-byte pack
+    // (Vulkore quant_test.cpp, ref::q4k_scale_min), two 8-bit lanes at once.
+    const int c = 16 * (G & 1);
+    const uint32_t a = r.hdr.y >> c, b = r.hdr.z >> c, e = r.hdr.w >> c;
+    uint32_t sc2, mn2;
+    if (G < 2) {
+      sc2 = a & 0x3F3Fu;
+      mn2 = b & 0x3F3Fu;
+    } else {
+      sc2 = (e & 0x0F0Fu) | ((a >> 2) & 0x3030u);
+      mn2 = ((e >> 4) & 0x0F0Fu) | ((b >> 2) & 0x3030u);
+    }
+    Sc s;
+    // (1024 + sc_lo, 1024 + sc_hi) as an f16 pair, then the integers.
+    const half2v scs = as_h2(__builtin_amdgcn_perm(0x64646464u, sc2, 0x07010600u)) - half2v{1024, 1024};
+    const half2v f = scs * half2v{1.0f16, 0.0625f16};       // (sc_lo, sc_hi / 16)
+    const half2v b2 = scs * half2v{-1024.0f16, -64.0f16};   // offsets to remove
+    s.f_lo = as_u(half2v{f[0], f[0]});
+    s.b_lo = as_u(half2v{b2[0], b2[0]});
+    s.f_hi = as_u(half2v{f[1], f[1]});
+    s.b_hi = as_u(half2v{b2[1], b2[1]});
+    s.d = lo_f16(r.hdr.x);
+    const float dmin = hi_f16(r.hdr.x);
+    s.mn_lo = -dmin * (float)(mn2 & 0xFFu);
+    s.mn_hi = -dmin * (float)((mn2 >> 8) & 0xFFu);
+    return s;
+  }
+
+  __device__ static half8 bop(const Raw &r, const Sc &s, int st, int) {
+    const int w = st & 3;
+    const uint32_t v0 = w < 2 ? (w == 0 ? r.q0.x : r.q0.z) : (w == 2 ? r.q1.x : r.q1.z);
+    const uint32_t v1 = w < 2 ? (w == 0 ? r.q0.y : r.q0.w) : (w == 2 ? r.q1.y : r.q1.w);
+    const uint32_t mask = st < 4 ? 0x000F000Fu : 0x00F000F0u;
+    const uint32_t f = st < 4 ? s.f_lo : s.f_hi, b = st < 4 ? s.b_lo : s.b_hi;
+    return pack8(fold(mag(v0, mask), f, b), fold(mag(v0 >> 8, mask), f, b), fold(mag(v1, mask), f, b),
+                 fold(mag(v1 >> 8, mask), f, b));
+  }
+
+  // A-row 4G' + h collects sub-block 2G' + h; step s of group G is in
+  // sub-block 2G + (s >= 4).
+  __device__ static bool ind(int s, int G, int i) { return i == 4 * G + (s >= 4 ? 1 : 0); }
+
+  __device__ static floatx4 post(floatx4 acc, const floatx4 *D, floatx4 X, const Sc &s) {
+    acc = acc + s.d * D[0];
+    acc = mfma4f32(X[0], s.mn_lo, acc);
+    acc = mfma4f32(X[1], s.mn_hi, acc);
+    return acc;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Q6_K.  Group G = 2h + a covers half h and byte lane l in 16a..16a+15 of all
+// four quarters g (elements 128h + 32g + 16a + [0,16)).  Step s takes
+// quarter g = s/2, bytes 8(s%2)..+7 of that range, all in sub-block
+// 8h + 2g + a.  The int8 sub-block scale sc = 16*sh + sl (sh in -8..7, sl in
+// 0..15) is folded as two exact parts, sh*(q-32) and sl*(q-32), that
+// accumulate separately and are scaled by 16d and d.
+// ---------------------------------------------------------------------------
+struct DecQ6K {
+  static constexpr int KB = 256, NSTEP = 8, NPART = 2, BYTES = 210;
+  static constexpr bool HAS_MIN = false;
+  struct Raw { u32x4 ql0, ql1, qh; u32x2 sc; uint32_t d; };
+  struct Sc { uint32_t f[2][4], b[2][4]; float d; };
+
+  __device__ static int x_off(int s, int G) { return 128 * (G >> 1) + 32 * (s >> 1) + 16 * (G & 1) + 8 * (s & 1); }
+
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+    const int h = G >> 1, a = G & 1;
+    r.ql0 = ld16(blk + 64 * h + 16 * a);
+    r.ql1 = ld16(blk + 64 * h + 32 + 16 * a);
+    r.qh = ld16(blk + 128 + 32 * h + 16 * a);
+    r.sc = ld8(blk + 192 + 8 * h);
+    r.d = rd16(blk + 208);
+  }
+
+  __device__ static Sc prep(const Raw &r, int G) {
+    // The sub-block of quarter g is 8h + 2g + a: byte a + 2g of the 8 loaded.
+    const int a = G & 1;
+    const uint32_t lo = a ? (r.sc.x >> 8) : r.sc.x;  // g = 0, 1 at bits 0, 16
+    const uint32_t hi = a ? (r.sc.y >> 8) : r.sc.y;  // g = 2, 3
+    Sc s;
+    s.d = lo_f16(r.d);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int sc = (int)(int8_t)(uint8_t)(((g < 2 ? lo : hi) >> (16 * (g & 1))) & 0xFFu);
+      const int part[2] = {sc >> 4, sc & 15};  // sc = 16*sh + sl
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        // Codes arrive as e = 1024 + q (g < 2) or 1024 + 16q (g >= 2):
+        // c*(q - 32) = e*c - 1056c, or e*(c/16) - 96c.
+        const float c = (float)part[p];
+        const _Float16 f = (_Float16)(g < 2 ? c : c * 0.0625f);
+        const _Float16 b = (_Float16)(g < 2 ? -1056.0f * c : -96.0f * c);
+        s.f[p][g] = as_u(half2v{f, f});
+        s.b[p][g] = as_u(half2v{b, b});
+      }
+    }
+    return s;
+  }
+
+  __device__ static half8 bop(const Raw &r, const Sc &s, int st, int part) {
+    const int g = st >> 1, w = 2 * (st & 1);
+    const u32x4 &ql = (g & 1) ? r.ql1 : r.ql0;
+    const uint32_t q0 = w == 0 ? ql.x : ql.z, q1 = w == 0 ? ql.y : ql.w;
+    const uint32_t h0 = w == 0 ? r.qh.x : r.qh.z, h1 = w == 0 ? r.qh.y : r.qh.w;
+    // Low case: nibble at bits 0-3, the two high bits go to 4-5.
+    // High case: nibble stays at 4-7, the two high bits go to 8-9.
+    const uint32_t qm = g < 2 ? 0x000F000Fu : 0x00F000F0u;
+    const uint32_t hm = g < 2 ? 0x00300030u : 0x03000300u;
+    const int up = (g & 1) ? 2 : 4;  // moves bits 2g, 2g+1 to 4 (low case) or 8 (high case)
+    const uint32_t e0 = and_or(h0 << up, hm, mag(q0, qm));
+    const uint32_t e1 = and_or(h0 >> (8 - up), hm, mag(q0 >> 8, qm));
+    const uint32_t e2 = and_or(h1 << up, hm, mag(q1, qm));
+    const uint32_t e3 = and_or(h1 >> (8 - up), hm, mag(q1 >> 8, qm));
+    const uint32_t f = s.f[part][g], b = s.b[part][g];
+    return pack8(fold(e0, f, b), fold(e1, f, b), fold(e2, f, b), fold(e3, f, b));
+  }
+
+  __device__ static bool ind(int, int, int) { return false; }
+
+  __device__ static floatx4 post(floatx4 acc, const floatx4 *D, floatx4, const Sc &s) {
+    return acc + (16.0f * s.d) * D[0] + s.d * D[1];
+  }
+};
+
+template <int KIND> struct Dec;
+template <> struct Dec<Q4_K> : DecQ4K {};
+template <> struct Dec<Q6_K> : DecQ6K {};
+
+template <int KIND> struct HasDec { static constexpr bool value = false; };
+template <> struct HasDec<Q4_K> { static constexpr bool value = true; };
+template <> struct HasDec<Q6_K> { static constexpr bool value = true; };
+
+}  // namespace gv
+}  // namespace qmm

@@ -1,0 +1,234 @@
+// qmm_gemv_mfma.hip -- the matrix-core decode GEMV (see qmm_gemv_mfma.h).
+//
+// Work split.  A workgroup owns R tiles of 16 weight rows and S waves.  Wave
+// w takes k-blocks [w*n/S, (w+1)*n/S) of every row, so the S waves cut K into
+// S ranges and their partial sums meet in LDS at the end; every activation
+// k-block a wave stages serves its R tiles.
+#include <stdlib.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "qmm_gemv_mfma.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace gv {
+
+// Software pipeline.  Each wave walks its k-blocks in order with PD k-blocks
+// in flight: before it decodes k-block kb it issues, for k-block kb+PD, the
+// weight loads of its R tiles and its slice of the activations (each lane
+// loads 4 consecutive elements of one token, 16 bytes); then it waits for kb,
+// converts kb's activation slice to f16 into a wave-private LDS ring
+// (fragment layout below), and decodes and multiplies kb.  Loads therefore leave in the order they are
+// consumed, the activations never queue behind a full HBM stream, and only PD
+// k-blocks of registers are held.
+//
+// Fragment layout of one k-block: fragment (s, t, G) -- 8 elements of token
+// t in the pair order 0,2,1,3,4,6,5,7, 16 bytes -- at (s * MT + t) * 4 + G, so
+// the MT token rows of one step are MT * 64 contiguous bytes and no two lanes
+// of a read share a bank.  Lanes whose A-row is >= MT read a zero fragment.
+
+template <int KIND, int MT>
+struct XSlice {
+  using Dd = Dec<KIND>;
+  static constexpr int kFrag = Dd::NSTEP * MT * 4;   // fragments per k-block
+  static constexpr int kHalves = 2 * kFrag;          // 4-element halves per k-block
+  static constexpr int kPerLane = (kHalves + 63) / 64;
+};
+
+template <typename XT> struct XVec;
+template <> struct XVec<float> { typedef float type __attribute__((ext_vector_type(4))); };
+template <> struct XVec<_Float16> { typedef _Float16 type __attribute__((ext_vector_type(4))); };
+
+template <int KIND, typename XT, int MT, int S, int R, int PD, int OCC>
+__global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void gemv_mfma_kernel(
+    const uint8_t *__restrict__ W, int64_t row_bytes, const XT *__restrict__ X, float *__restrict__ Y, int M,
+    int64_t N, int K) {
+  using Dd = Dec<KIND>;
+  using XS = XSlice<KIND, MT>;
+  using X4 = typename XVec<XT>::type;
+  constexpr int kFrag = XS::kFrag;
+  extern __shared__ u32x4 lds[];  // S rings of PD+1 k-blocks, one zero fragment; later the reduction
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 15, G = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * (16 * R);
+  const int nkb = K / Dd::KB;
+  u32x4 *ring = lds + wave * (PD + 1) * kFrag;
+  const u32x4 *zero = lds + S * (PD + 1) * kFrag;
+  if (threadIdx.x == 0) lds[S * (PD + 1) * kFrag] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  const uint8_t *wr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int64_t row = row0 + 16 * r + j;
+    if (row >= N) row = N - 1;  // decode a real row; its outputs are not stored
+    wr[r] = W + row * row_bytes;
+  }
+  floatx4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // This lane's activation slice: half-fragment h = lane + 64 i of a k-block
+  // is elements x_off(s, G') + 4 (h & 1) + [0, 4) of token t.
+  int xoff[XS::kPerLane], xdst[XS::kPerLane];
+  bool xlive[XS::kPerLane];
+#pragma unroll
+  for (int i = 0; i < XS::kPerLane; ++i) {
+    const int h = lane + 64 * i, f = h >> 1;
+    const int g2 = f & 3, t = (f >> 2) % MT, st = (f >> 2) / MT;
+    xlive[i] = h < XS::kHalves && t < M;
+    xoff[i] = xlive[i] ? t * K + Dd::x_off(st, g2) + 4 * (h & 1) : 0;
+    xdst[i] = h < XS::kHalves ? h : -1;
+  }
+
+  // Ring of NS = PD + 1 slots: while k-block kb is decoded, k-blocks
+  // kb+1 .. kb+PD are in flight; the refill for kb+PD is issued before kb is
+  // decoded, so the memory pipe stays busy through every compute phase.
+  constexpr int NS = PD + 1;
+  const int kb0 = (int)((int64_t)wave * nkb / S), kb1 = (int)((int64_t)(wave + 1) * nkb / S);
+  typename Dd::Raw raw[NS][R];
+  X4 xv[NS][XS::kPerLane];
+  auto issue = [&](int kb, int slot) {
+#pragma unroll
+    for (int i = 0; i < XS::kPerLane; ++i) {
+      X4 v = {};
+      if (xlive[i]) __builtin_memcpy(&v, X + xoff[i] + (int64_t)kb * Dd::KB, sizeof(X4));
+      xv[slot][i] = v;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) Dd::load(wr[r] + (int64_t)kb * Dd::BYTES, G, raw[slot][r]);
+  };
+#pragma unroll
+  for (int d = 0; d < PD; ++d)
+    if (kb0 + d < kb1) issue(kb0 + d, d);
+
+  for (int kb = kb0; kb < kb1; kb += NS) {
+#pragma unroll
+    for (int d = 0; d < NS; ++d) {
+      if (kb + d >= kb1) break;
+      if (kb + d + PD < kb1) issue(kb + d + PD, (d + PD) % NS);
+      // Activations of k-block kb+d into ring slot d (pair order per half).
+      u32x4 *xk = ring + d * kFrag;
+#pragma unroll
+      for (int i = 0; i < XS::kPerLane; ++i) {
+        if (xdst[i] < 0) continue;
+        const X4 v = xv[d][i];
+        const half2v p0 = {(_Float16)v[0], (_Float16)v[2]}, p1 = {(_Float16)v[1], (_Float16)v[3]};
+        u32x2 *dst = reinterpret_cast<u32x2 *>(xk) + xdst[i];
+        *dst = u32x2{as_u(p0), as_u(p1)};
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const u32x4 *xr = j < MT ? xk + j * 4 + G : zero;
+      const int xstep = j < MT ? MT * 4 : 0;
+      half8 a[Dd::NSTEP];
+      floatx4 xsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < Dd::NSTEP; ++st) {
+        a[st] = __builtin_bit_cast(half8, xr[st * xstep]);
+        if constexpr (Dd::HAS_MIN) {
+          const _Float16 v = Dd::ind(st, G, j) ? (_Float16)1.0f : (_Float16)0.0f;
+          xsum = mfma16(half8{v, v, v, v, v, v, v, v}, a[st], xsum);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const typename Dd::Sc sc = Dd::prep(raw[d][r], G);
+        floatx4 D[Dd::NPART];
+#pragma unroll
+        for (int p = 0; p < Dd::NPART; ++p) D[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < Dd::NSTEP; ++st)
+#pragma unroll
+          for (int p = 0; p < Dd::NPART; ++p) D[p] = mfma16(a[st], Dd::bop(raw[d][r], sc, st, p), D[p]);
+        acc[r] = Dd::post(acc[r], D, xsum, sc);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();  // slot d is rewritten NS k-blocks later
+    }
+  }
+
+  if constexpr (S > 1) {
+    __syncthreads();  // every wave is done with its ring
+    floatx4 *red = reinterpret_cast<floatx4 *>(lds);
+    if (wave > 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) red[((wave - 1) * R + r) * 64 + lane] = acc[r];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < S - 1; ++w)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] += red[(w * R + r) * 64 + lane];
+  }
+  // Lane (j, G) holds D[token 4G + q][row j] of each tile.
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + 16 * r + j;
+    if (row >= N) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = 4 * G + q;
+      if (t < M) Y[(int64_t)t * N + row] = acc[r][q];
+    }
+  }
+}
+
+template <int KIND, int MT, int S, int R, int PD, int OCC = 1>
+static hipError_t run(const uint8_t *W, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,
+                      hipStream_t s) {
+  const int64_t row_bytes = (K / Geometry<KIND>::elems) * Geometry<KIND>::bytes;
+  const size_t ring = (size_t)S * (PD + 1) * XSlice<KIND, MT>::kFrag * 16 + 16;
+  const size_t lds = std::max<size_t>(ring, (size_t)(S - 1) * R * 64 * sizeof(floatx4));
+  const dim3 grid((unsigned)((N + 16 * R - 1) / (16 * R))), block(64 * S);
+  if (x_f16)
+    hipLaunchKernelGGL((gemv_mfma_kernel<KIND, _Float16, MT, S, R, PD, OCC>), grid, block, lds, s, W, row_bytes,
+                       (const _Float16 *)x, y, M, N, (int)K);
+  else
+    hipLaunchKernelGGL((gemv_mfma_kernel<KIND, float, MT, S, R, PD, OCC>), grid, block, lds, s, W, row_bytes,
+                       (const float *)x, y, M, N, (int)K);
+  return hipGetLastError();
+}
+
+// Launch shapes, chosen by M: small M keeps many k-blocks in flight per
+// wave; large M shares each staged activation k-block among R tiles.
+template <int KIND>
+static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,
+                        hipStream_t s, int cfg) {
+  switch (cfg) {
+    case 1: if (M <= 1) return run<KIND, 1, 4, 1, 1>(W, x, x_f16, y, M, N, K, s); break;
+    case 2: if (M <= 1) return run<KIND, 1, 2, 1, 2>(W, x, x_f16, y, M, N, K, s); break;
+    case 3: if (M <= 1) return run<KIND, 1, 2, 1, 3>(W, x, x_f16, y, M, N, K, s); break;
+    case 7: if (M <= 1) return run<KIND, 1, 1, 1, 3>(W, x, x_f16, y, M, N, K, s); break;
+    case 4: if (M > 4) return run<KIND, 8, 4, 1, 2>(W, x, x_f16, y, M, N, K, s); break;
+    case 5: if (M > 4) return run<KIND, 8, 4, 2, 1>(W, x, x_f16, y, M, N, K, s); break;
+    case 6: if (M > 4) return run<KIND, 8, 2, 2, 2>(W, x, x_f16, y, M, N, K, s); break;
+    default: break;
+  }
+  if (M <= 1) return run<KIND, 1, 4, 1, 2>(W, x, x_f16, y, M, N, K, s);
+  if (M <= 2) return run<KIND, 2, 4, 1, 2>(W, x, x_f16, y, M, N, K, s);
+  if (M <= 4) return run<KIND, 4, 4, 1, 2>(W, x, x_f16, y, M, N, K, s);
+  return run<KIND, 8, 4, 2, 2>(W, x, x_f16, y, M, N, K, s);
+}
+
+}  // namespace gv
+
+// Returns hipErrorNotSupported when the kind has no matrix-core decoder.
+hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int M,
+                            int64_t N, int64_t K, hipStream_t s) {
+  static const int cfg = [] {
+    const char *e = getenv("QMM_GEMV_CFG");
+    return e ? atoi(e) : 0;
+  }();
+  switch (kind) {
+    case Q4_K: return gv::run_m<Q4_K>(W, x, x_f16, y, M, N, K, s, cfg);
+    case Q6_K: return gv::run_m<Q6_K>(W, x, x_f16, y, M, N, K, s, cfg);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace qmm

@@ -16,6 +16,10 @@ hipError_t launch_dequant(int kind, const uint8_t *W, float *out, int64_t n_bloc
 hipError_t launch_gemv(int kind, const uint8_t *W, const void *x, int x_f16, float *y,
                        int M, int64_t N, int64_t K, hipStream_t s);
 
+// The matrix-core GEMV; hipErrorNotSupported for kinds it does not decode.
+hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16, float *y,
+                            int M, int64_t N, int64_t K, hipStream_t s);
+
 // C[M][N] = A[M][K] . W^T, any M >= 1, A f32 (a_f16 == 0) or f16.
 hipError_t launch_gemm(int kind, const uint8_t *W, const void *A, int a_f16, float *C,
                        int64_t M, int64_t N, int64_t K, hipStream_t s);

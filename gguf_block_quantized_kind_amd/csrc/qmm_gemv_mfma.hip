@@ -209,10 +209,10 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
     case 6: if (M > 4) return run<KIND, 8, 2, 2, 2>(W, x, x_f16, y, M, N, K, s); break;
     default: break;
   }
-  if (M <= 1) return run<KIND, 1, 4, 1, 2>(W, x, x_f16, y, M, N, K, s);
-  if (M <= 2) return run<KIND, 2, 4, 1, 2>(W, x, x_f16, y, M, N, K, s);
-  if (M <= 4) return run<KIND, 4, 4, 1, 2>(W, x, x_f16, y, M, N, K, s);
-  return run<KIND, 8, 4, 2, 2>(W, x, x_f16, y, M, N, K, s);
+  if (M <= 1) return run<KIND, 1, 2, 1, 2>(W, x, x_f16, y, M, N, K, s);
+  if (M <= 2) return run<KIND, 2, 2, 1, 2>(W, x, x_f16, y, M, N, K, s);
+  if (M <= 4) return run<KIND, 4, 2, 2, 2>(W, x, x_f16, y, M, N, K, s);
+  return run<KIND, 8, 2, 2, 2>(W, x, x_f16, y, M, N, K, s);
 }
 
 }  // namespace gv

@@ -18,11 +18,14 @@
  * scale * code + bias for the affine kinds, scale * table[code] for the
  * codebook kinds (ferrox-cuda 0.20.0 mul_mm_kinds/codebook.rs, module docs).
  *
- * Numerics.  Accumulation is in f32.  The decode GEMV keeps every weight
- * exact; the prefill GEMM rounds each decoded weight once to f16 (relative
- * error <= 2^-11) and, for f32 activations, splits each activation into two
- * f16 parts so that only one operand is ever rounded.  Results satisfy
- * |y - y_exact| <= 1e-3 * sum_k |w||x| + 1e-6 per element.
+ * Numerics.  Accumulation is in f32 and at most one factor of each product
+ * is rounded, once, to f16 (relative error <= 2^-11).  The decode GEMV keeps
+ * every weight exact (an exact f16 integer times an f32 scale) and, on its
+ * matrix-core path, rounds f32 activations once to f16.  The prefill GEMM
+ * rounds each decoded weight once to f16 and, for f32 activations, splits
+ * each activation into two f16 parts so that the activation stays exact to
+ * about 2^-22.  Results satisfy |y - y_exact| <= 1e-3 * sum_k |w||x| + 1e-6
+ * per element.
  *
  * Ownership and asynchrony.  The caller owns every buffer; the library never
  * allocates device memory.  W, x and ids are read only.  Calls that take a
@@ -86,7 +89,8 @@ enum qmm_status {
 int qmm_gemv(int kind, const void *W, const float *x, float *y, int64_t N, int64_t K);
 
 /* Decode GEMV, 1 <= M <= QMM_GEMV_MAX_M tokens, f32 or f16 x, on `stream`.
- * Every weight is decoded exactly; products accumulate in f32. */
+ * Every weight is decoded exactly; f32 x may be rounded once to f16;
+ * products accumulate in f32. */
 int qmm_gemv_ex(int kind, const void *W, const void *x, int x_dtype, float *y,
                 int64_t M, int64_t N, int64_t K, void *stream);
 

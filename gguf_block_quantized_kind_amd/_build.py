@@ -35,6 +35,13 @@ def compile_flags() -> list[str]:
             "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 
+# Per-source extra flags.  The GEMM keeps its matrix-core accumulators in
+# ordinary VGPRs: with accumulation registers the allocator rotates its
+# loop-carried accumulators through copies on every iteration.  (The GEMV
+# mixes inline assembly with its matrix-core code and keeps the default.)
+FILE_FLAGS = {"qmm_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -45,7 +52,7 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
 
     def one(src: str) -> str:
         obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-        cmd = [cc, *compile_flags(), "-c", src, "-o", obj]
+        cmd = [cc, *compile_flags(), *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -81,6 +81,30 @@ __device__ __forceinline__ float e2m1_value(uint32_t code) {
   return t[code & 15u];
 }
 
+// v_perm_b32: byte i of the result is byte sel[i] of the eight bytes
+// {hi:lo} (0..3 from lo, 4..7 from hi); selector 12 gives 0x00, 13 gives 0xFF.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// The IQ4_NL table plus 128, one unsigned byte per entry, in four words.
+constexpr uint32_t kIq4T0 = 0x3F2D1801u, kIq4T1 = 0x766A5D4Fu, kIq4T2 = 0xA6998D81u, kIq4T3 = 0xF1D9C5B5u;
+
+// Table lookup of four 4-bit indices (one per byte) giving table + 128 per
+// byte: entries 0..7 and 8..15 are looked up separately with v_perm and bit 3
+// of each index chooses.
+__device__ __forceinline__ uint32_t iq4_lookup(uint32_t idx) {
+  const uint32_t low3 = idx & 0x07070707u;
+  const uint32_t a = perm(kIq4T1, kIq4T0, low3);
+  const uint32_t b = perm(kIq4T3, kIq4T2, low3);
+  const uint32_t m = perm(0u, 0u, ((idx >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+  return (b & m) | (a & ~m);
+}
+
+// Bits 0..3 of x to bit 0 of bytes 0..3 (the four shifted copies of x
+// occupy disjoint bit ranges, so the product carries nothing).
+__device__ __forceinline__ uint32_t spread4(uint32_t x) { return ((x & 15u) * 0x00204081u) & 0x01010101u; }
+
 // 6-bit scale and min of 32-element group j of the Q4_K/Q5_K 12-byte pack
 // (Vulkore quant_test.cpp, ref::q4k_scale_min).
 __device__ __forceinline__ void k4_scale_min(const uint8_t *s, int j, int &sc, int &mn) {

@@ -58,12 +58,6 @@ __device__ __forceinline__ half2v splat(uint32_t f16_bits) {
   return half2v{v, v};
 }
 
-// v_perm_b32: byte i of the result is byte sel[i] of the eight bytes
-// {hi:lo} (0..3 from lo, 4..7 from hi); selector 12 gives 0x00, 13 gives 0xFF.
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
 // Bytes b0..b3 of v as the f16 pairs (1024 + b0, 1024 + b1) and
 // (1024 + b2, 1024 + b3).
 __device__ __forceinline__ void spread(uint32_t v, uint32_t &p01, uint32_t &p23) {
@@ -90,24 +84,6 @@ __device__ __forceinline__ void emit(uint32_t lo, uint32_t hi, int i, half2v off
   spread(hi, a, b);
   out[8 + 2 * i] = affine(a, off, d);
   out[9 + 2 * i] = affine(b, off, d);
-}
-
-// Bits 0..3 of x to bit 0 of bytes 0..3 (the four shifted copies of x
-// occupy disjoint bit ranges, so the product carries nothing).
-__device__ __forceinline__ uint32_t spread4(uint32_t x) { return ((x & 15u) * 0x00204081u) & 0x01010101u; }
-
-// The IQ4_NL table plus 128, one unsigned byte per entry, in four words
-// (ferrox-cuda 0.20.0 codebook.rs, KVALUES_IQ4NL).
-constexpr uint32_t kIq4T0 = 0x3F2D1801u, kIq4T1 = 0x766A5D4Fu, kIq4T2 = 0xA6998D81u, kIq4T3 = 0xF1D9C5B5u;
-
-// Table lookup of four 4-bit indices (one per byte): entries 0..7 and 8..15
-// are looked up separately with v_perm and bit 3 of each index chooses.
-__device__ __forceinline__ uint32_t iq4_lookup(uint32_t idx) {
-  const uint32_t low3 = idx & 0x07070707u;
-  const uint32_t a = perm(kIq4T1, kIq4T0, low3);
-  const uint32_t b = perm(kIq4T3, kIq4T2, low3);
-  const uint32_t m = perm(0u, 0u, ((idx >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
-  return (b & m) | (a & ~m);
 }
 
 template <int KIND> struct Chunk;

@@ -96,8 +96,12 @@ __device__ __forceinline__ floatx4 mfma4f32(float a, float b, floatx4 c) {
 //   KB, NSTEP            elements per k-block and MFMA steps per k-block
 //   NPART                B operands per step (2 for a split fold)
 //   HAS_MIN              a minimum term runs on the f32 MFMA
-//   x_off(s, G)          first of the 8 consecutive elements step s gives G;
-//                        inside a step the pairs are ordered 0,2,1,3,4,6,5,7
+//   x_off(s, G, h)       first of the 4 consecutive elements of half h (0, 1)
+//                        of the 8 elements step s gives G; inside a half the
+//                        pairs are ordered (0,2), (1,3)
+//   STEP_SCALE           every step has its own f32 scale: post_step(acc, D,
+//                        raw, s) adds scale(s) * D after each step's MFMA
+//                        (which starts from zero); otherwise post() below
 //   Raw / load           the lane's bytes of one k-block
 //   Sc / prep            the lane's scales for that k-block
 //   bop(raw, sc, s, p)   B operand p of step s
@@ -117,7 +121,8 @@ struct DecQ4K {
   struct Raw { u32x4 hdr, q0, q1; };
   struct Sc { uint32_t f_lo, b_lo, f_hi, b_hi; float d, mn_lo, mn_hi; };
 
-  __device__ static int x_off(int s, int G) { return 64 * G + (s < 4 ? 8 * s : 32 + 8 * (s - 4)); }
+  static constexpr bool STEP_SCALE = false;
+  __device__ static int x_off(int s, int G, int h) { return 64 * G + (s < 4 ? 8 * s : 32 + 8 * (s - 4)) + 4 * h; }
 
   __device__ static void load(const uint8_t *blk, int G, Raw &r) {
     r.hdr = ld16(blk);
@@ -190,7 +195,10 @@ struct DecQ6K {
   struct Raw { u32x4 ql0, ql1, qh; u32x2 sc; uint32_t d; };
   struct Sc { uint32_t f[2][4], b[2][4]; float d; };
 
-  __device__ static int x_off(int s, int G) { return 128 * (G >> 1) + 32 * (s >> 1) + 16 * (G & 1) + 8 * (s & 1); }
+  static constexpr bool STEP_SCALE = false;
+  __device__ static int x_off(int s, int G, int h) {
+    return 128 * (G >> 1) + 32 * (s >> 1) + 16 * (G & 1) + 8 * (s & 1) + 4 * h;
+  }
 
   __device__ static void load(const uint8_t *blk, int G, Raw &r) {
     const int h = G >> 1, a = G & 1;
@@ -251,13 +259,192 @@ struct DecQ6K {
   }
 };
 
+// ---------------------------------------------------------------------------
+// The 32-element kinds (and IQ4_XS's 32-element groups).  Every block has its
+// own scale, so a step is exactly one block: the B operand holds the block's
+// exact integer codes (or table values), the MFMA starts from zero, and the
+// block scale multiplies the step's D in f32.  A k-block is 8 blocks.
+//
+// Nibble kinds: group G takes code bytes 4G..4G+3, whose low nibbles are
+// elements 4G..4G+3 and high nibbles 16+4G..16+4G+3 (half 0 and half 1 of
+// the group's 8 elements).  Q8_0: group G takes bytes 8G..8G+7.
+// ---------------------------------------------------------------------------
+struct StepBase {
+  static constexpr int KB = 256, NSTEP = 8, NPART = 1;
+  static constexpr bool HAS_MIN = false, STEP_SCALE = true;
+  struct Sc {};
+  __device__ static int x_off(int s, int G, int h) { return 32 * s + 16 * h + 4 * G; }
+  __device__ static bool ind(int, int, int) { return false; }
+  __device__ static floatx4 post(floatx4 acc, const floatx4 *, floatx4, const Sc &) { return acc; }
+};
+
+__device__ __forceinline__ uint32_t ld4(const uint8_t *p) {
+  uint32_t v;
+  __builtin_memcpy(&v, p, 4);
+  return v;
+}
+
+// Four unsigned bytes u (low-nibble word) and four more (high-nibble word) as
+// the B fragment (1024 + u) - off in the order (0,2), (1,3) of each half.
+__device__ __forceinline__ half8 bytes_b(uint32_t lo, uint32_t hi, uint32_t off) {
+  const uint32_t m = 0x00FF00FFu, one = 0x3C003C00u;
+  return pack8(fold(mag(lo, m), one, off), fold(mag(lo >> 8, m), one, off), fold(mag(hi, m), one, off),
+               fold(mag(hi >> 8, m), one, off));
+}
+
+constexpr uint32_t kNeg1032 = 0xE408E408u;  // f16 pair (-1032, -1032)
+constexpr uint32_t kNeg1040 = 0xE410E410u;  // (-1040, -1040)
+constexpr uint32_t kNeg1152 = 0xE480E480u;  // (-1152, -1152)
+
+// Q4_0 (18 B): f16 d, 16 code bytes; w = d * (q - 8).
+struct DecQ4_0 : StepBase {
+  static constexpr int BYTES = 8 * 18;
+  struct Raw { uint32_t d[8], q[8]; };
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r.d[s] = rd16(blk + 18 * s);
+      r.q[s] = ld4(blk + 18 * s + 2 + 4 * G);
+    }
+  }
+  __device__ static Sc prep(const Raw &, int) { return Sc{}; }
+  __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {
+    return bytes_b(r.q[s] & 0x0F0F0F0Fu, (r.q[s] >> 4) & 0x0F0F0F0Fu, kNeg1032);
+  }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
+    return acc + lo_f16(r.d[s]) * D;
+  }
+};
+
+// Q5_0 (22 B): f16 d, u32 qh (bit e: fifth bit of element e), 16 code
+// bytes; w = d * (q - 16).
+struct DecQ5_0 : StepBase {
+  static constexpr int BYTES = 8 * 22;
+  struct Raw { uint32_t d[8], qh[8], q[8]; };
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r.d[s] = rd16(blk + 22 * s);
+      r.qh[s] = ld4(blk + 22 * s + 2) >> (4 * G);  // bits 0-3, 16-19: this group's fifth bits
+      r.q[s] = ld4(blk + 22 * s + 6 + 4 * G);
+    }
+  }
+  __device__ static Sc prep(const Raw &, int) { return Sc{}; }
+  __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {
+    const uint32_t lo = (r.q[s] & 0x0F0F0F0Fu) | (spread4(r.qh[s]) << 4);
+    const uint32_t hi = ((r.q[s] >> 4) & 0x0F0F0F0Fu) | (spread4(r.qh[s] >> 16) << 4);
+    return bytes_b(lo, hi, kNeg1040);
+  }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
+    return acc + lo_f16(r.d[s]) * D;
+  }
+};
+
+// Q8_0 (34 B): f16 d, 32 int8 codes; w = d * q.  Code XOR 0x80 = q + 128.
+struct DecQ8_0 : StepBase {
+  static constexpr int BYTES = 8 * 34;
+  struct Raw { uint32_t d[8]; u32x2 q[8]; };
+  __device__ static int x_off(int s, int G, int h) { return 32 * s + 8 * G + 4 * h; }
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r.d[s] = rd16(blk + 34 * s);
+      r.q[s] = ld8(blk + 34 * s + 2 + 8 * G);
+    }
+  }
+  __device__ static Sc prep(const Raw &, int) { return Sc{}; }
+  __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {
+    return bytes_b(r.q[s].x ^ 0x80808080u, r.q[s].y ^ 0x80808080u, kNeg1152);
+  }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
+    return acc + lo_f16(r.d[s]) * D;
+  }
+};
+
+// IQ4_NL (18 B): f16 d, 16 code bytes packed as Q4_0; w = d * table[code];
+// the B operand is the exact table value.
+struct DecIQ4NL : StepBase {
+  static constexpr int BYTES = 8 * 18;
+  struct Raw { uint32_t d[8], q[8]; };
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r.d[s] = rd16(blk + 18 * s);
+      r.q[s] = ld4(blk + 18 * s + 2 + 4 * G);
+    }
+  }
+  __device__ static Sc prep(const Raw &, int) { return Sc{}; }
+  __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {
+    return bytes_b(iq4_lookup(r.q[s] & 0x0F0F0F0Fu), iq4_lookup((r.q[s] >> 4) & 0x0F0F0F0Fu), kNeg1152);
+  }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
+    return acc + lo_f16(r.d[s]) * D;
+  }
+};
+
+// MXFP4 (17 B): E8M0 byte, 16 E2M1 code bytes packed as Q4_0;
+// w = 2^(e-127) * e2m1[code].  The gfx950 scaled FP4 conversion with scale 2
+// gives 2 * e2m1 exactly as f16 (an integer of at most 12) for the two
+// nibbles of a byte; the block scale 2^(e-128) is applied in f32.
+struct DecMXFP4 : StepBase {
+  static constexpr int BYTES = 8 * 17;
+  struct Raw { uint32_t e[8], q[8]; };
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r.e[s] = blk[17 * s];
+      r.q[s] = ld4(blk + 17 * s + 1 + 4 * G);
+    }
+  }
+  __device__ static Sc prep(const Raw &, int) { return Sc{}; }
+  __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {
+    const uint32_t v = r.q[s];
+    const uint32_t p0 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 0));
+    const uint32_t p1 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 1));
+    const uint32_t p2 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 2));
+    const uint32_t p3 = as_u(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 3));
+    // p_i = (element 4G+i, element 16+4G+i); regroup as (0,2), (1,3) per half.
+    return pack8(perm(p2, p0, 0x05040100u), perm(p3, p1, 0x05040100u), perm(p2, p0, 0x07060302u),
+                 perm(p3, p1, 0x07060302u));
+  }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
+    return acc + (e8m0_to_f32(r.e[s]) * 0.5f) * D;
+  }
+};
+
+// IQ4_XS (136 B / 256): f16 d, u16 scales_h, scales_l[4], then eight
+// 32-element groups packed as IQ4_NL blocks; one k-block is one super-block
+// and step s is group s, scaled by the exact f32 d * (ls_s - 32).
+struct DecIQ4XS : StepBase {
+  static constexpr int BYTES = 136;
+  struct Raw { u32x2 h; uint32_t q[8]; };
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+    r.h = ld8(blk);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r.q[s] = ld4(blk + 8 + 16 * s + 4 * G);
+  }
+  __device__ static Sc prep(const Raw &, int) { return Sc{}; }
+  __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {
+    return bytes_b(iq4_lookup(r.q[s] & 0x0F0F0F0Fu), iq4_lookup((r.q[s] >> 4) & 0x0F0F0F0Fu), kNeg1152);
+  }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
+    const float d = lo_f16(r.h.x);
+    const uint32_t sh = r.h.x >> 16;
+    const uint32_t sl = (r.h.y >> (4 * s)) & 15u;  // nibble s of scales_l
+    const int ls = (int)(sl | (((sh >> (2 * s)) & 3u) << 4));
+    return acc + (d * (float)(ls - 32)) * D;
+  }
+};
+
 template <int KIND> struct Dec;
 template <> struct Dec<Q4_K> : DecQ4K {};
 template <> struct Dec<Q6_K> : DecQ6K {};
-
-template <int KIND> struct HasDec { static constexpr bool value = false; };
-template <> struct HasDec<Q4_K> { static constexpr bool value = true; };
-template <> struct HasDec<Q6_K> { static constexpr bool value = true; };
+template <> struct Dec<Q4_0> : DecQ4_0 {};
+template <> struct Dec<Q5_0> : DecQ5_0 {};
+template <> struct Dec<Q8_0> : DecQ8_0 {};
+template <> struct Dec<IQ4_NL> : DecIQ4NL {};
+template <> struct Dec<MXFP4> : DecMXFP4 {};
+template <> struct Dec<IQ4_XS> : DecIQ4XS {};
 
 }  // namespace gv
 }  // namespace qmm

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   for (int r = 0; r < R; ++r) acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // This lane's activation slice: half-fragment h = lane + 64 i of a k-block
-  // is elements x_off(s, G') + 4 (h & 1) + [0, 4) of token t.
+  // is elements x_off(s, G', h & 1) + [0, 4) of token t.
   int xoff[XS::kPerLane], xdst[XS::kPerLane];
   bool xlive[XS::kPerLane];
 #pragma unroll
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
     const int h = lane + 64 * i, f = h >> 1;
     const int g2 = f & 3, t = (f >> 2) % MT, st = (f >> 2) / MT;
     xlive[i] = h < XS::kHalves && t < M;
-    xoff[i] = xlive[i] ? t * K + Dd::x_off(st, g2) + 4 * (h & 1) : 0;
+    xoff[i] = xlive[i] ? t * K + Dd::x_off(st, g2, h & 1) : 0;
     xdst[i] = h < XS::kHalves ? h : -1;
   }
 
@@ -137,14 +137,22 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const typename Dd::Sc sc = Dd::prep(raw[d][r], G);
-        floatx4 D[Dd::NPART];
+        if constexpr (Dd::STEP_SCALE) {
 #pragma unroll
-        for (int p = 0; p < Dd::NPART; ++p) D[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int st = 0; st < Dd::NSTEP; ++st) {
+            const floatx4 D = mfma16(a[st], Dd::bop(raw[d][r], sc, st, 0), floatx4{0.f, 0.f, 0.f, 0.f});
+            acc[r] = Dd::post_step(acc[r], D, raw[d][r], st);
+          }
+        } else {
+          floatx4 D[Dd::NPART];
 #pragma unroll
-        for (int st = 0; st < Dd::NSTEP; ++st)
+          for (int p = 0; p < Dd::NPART; ++p) D[p] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int p = 0; p < Dd::NPART; ++p) D[p] = mfma16(a[st], Dd::bop(raw[d][r], sc, st, p), D[p]);
-        acc[r] = Dd::post(acc[r], D, xsum, sc);
+          for (int st = 0; st < Dd::NSTEP; ++st)
+#pragma unroll
+            for (int p = 0; p < Dd::NPART; ++p) D[p] = mfma16(a[st], Dd::bop(raw[d][r], sc, st, p), D[p]);
+          acc[r] = Dd::post(acc[r], D, xsum, sc);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();  // slot d is rewritten NS k-blocks later
@@ -204,6 +212,9 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
     case 2: if (M <= 1) return run<KIND, 1, 2, 1, 2>(W, x, x_f16, y, M, N, K, s); break;
     case 3: if (M <= 1) return run<KIND, 1, 2, 1, 3>(W, x, x_f16, y, M, N, K, s); break;
     case 7: if (M <= 1) return run<KIND, 1, 1, 1, 3>(W, x, x_f16, y, M, N, K, s); break;
+    case 8: if (M <= 1) return run<KIND, 1, 8, 1, 1>(W, x, x_f16, y, M, N, K, s); break;
+    case 9: if (M <= 1) return run<KIND, 1, 8, 1, 2>(W, x, x_f16, y, M, N, K, s); break;
+    case 10: if (M <= 1) return run<KIND, 1, 4, 1, 2>(W, x, x_f16, y, M, N, K, s); break;
     case 4: if (M > 4) return run<KIND, 8, 4, 1, 2>(W, x, x_f16, y, M, N, K, s); break;
     case 5: if (M > 4) return run<KIND, 8, 4, 2, 1>(W, x, x_f16, y, M, N, K, s); break;
     case 6: if (M > 4) return run<KIND, 8, 2, 2, 2>(W, x, x_f16, y, M, N, K, s); break;
@@ -217,7 +228,8 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
 
 }  // namespace gv
 
-// Returns hipErrorNotSupported when the kind has no matrix-core decoder.
+// Returns hipErrorNotSupported when the kind has no matrix-core decoder or K
+// is not a whole number of the decoder's k-blocks.
 hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int M,
                             int64_t N, int64_t K, hipStream_t s) {
   static const int cfg = [] {
@@ -227,6 +239,18 @@ hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16
   switch (kind) {
     case Q4_K: return gv::run_m<Q4_K>(W, x, x_f16, y, M, N, K, s, cfg);
     case Q6_K: return gv::run_m<Q6_K>(W, x, x_f16, y, M, N, K, s, cfg);
+    case IQ4_XS: return gv::run_m<IQ4_XS>(W, x, x_f16, y, M, N, K, s, cfg);
+    default: break;
+  }
+  // The 32-element kinds walk K in k-blocks of eight blocks.
+  if (K % 256 != 0) return hipErrorNotSupported;
+  switch (kind) {
+    case Q4_0: return gv::run_m<Q4_0>(W, x, x_f16, y, M, N, K, s, cfg);
+    case Q5_0: return gv::run_m<Q5_0>(W, x, x_f16, y, M, N, K, s, cfg);
+    case Q8_0: return gv::run_m<Q8_0>(W, x, x_f16, y, M, N, K, s, cfg);
+    case IQ4_NL: return gv::run_m<IQ4_NL>(W, x, x_f16, y, M, N, K, s, cfg);
+    case MXFP4: return gv::run_m<MXFP4>(W, x, x_f16, y, M, N, K, s, cfg);
+    default: break;
   }
   return hipErrorNotSupported;
 }

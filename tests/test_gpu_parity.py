@@ -131,25 +131,37 @@ def test_dequant_f16_and_e8m0_sweeps():
 # ---------------------------------------------------------------------------
 # GEMV
 # ---------------------------------------------------------------------------
+def gemv_Ks(kind):
+    """K values that reach both GEMV paths: 1280 is a whole number of
+    256-element k-blocks (the matrix-core path for every kind that has one);
+    1312 is not, so the 32-element kinds take the f32 path there."""
+    _, be = wl.geometry(kind)
+    return (1280,) if be == 256 else (1280, 1312)
+
+
 @pytest.mark.parametrize("xdt", ["f32", "f16"])
 @pytest.mark.parametrize("kind", ALL_KINDS)
 def test_gemv_parity(oracle_mod, kind, xdt):
-    N, K = 130, small_K(kind)
-    g = wl.rng("gpu_gemv", f"{kind}_{xdt}")
-    W = wl.random_weights(kind, N, K, g)
-    dt = np.float32 if xdt == "f32" else np.float16
-    Wd = dev(W)
-    for M in (1, 2, 3, 8):
-        X = wl.activations((M, K), dt, g)
-        y = filled((M, N))
-        qmm.qmm_gemv_ex(kind, Wd, dev(X), y, M, N, K)
-        Y, B = oracle_mod.matmul(kind, W, K, X)
-        assert_within_bound(host(y), Y, B, f"{kind} M={M} {xdt}")
+    for K in gemv_Ks(kind):
+        N = 130
+        g = wl.rng("gpu_gemv", f"{kind}_{xdt}_{K}")
+        W = wl.random_weights(kind, N, K, g)
+        dt = np.float32 if xdt == "f32" else np.float16
+        Wd = dev(W)
+        for M in (1, 2, 3, 5, 8):
+            X = wl.activations((M, K), dt, g)
+            y = filled((M, N))
+            qmm.qmm_gemv_ex(kind, Wd, dev(X), y, M, N, K)
+            Y, B = oracle_mod.matmul(kind, W, K, X)
+            assert_within_bound(host(y), Y, B, f"{kind} K={K} M={M} {xdt}")
 
 
+@pytest.mark.parametrize("K", [1280, 1312])
 @pytest.mark.parametrize("kind", ALL_KINDS)
-def test_gemv_unit_vectors_return_the_weights(oracle_mod, kind):
-    N, K = 70, small_K(kind)
+def test_gemv_unit_vectors_return_the_weights(oracle_mod, kind, K):
+    if K not in gemv_Ks(kind):
+        pytest.skip("K is not block-aligned for this kind")
+    N = 70
     W = wl.random_weights(kind, N, K, wl.rng("gpu_gemv_unit", kind), scales="stress")
     Wd = oracle_mod.dequant(kind, W).reshape(N, K).astype(np.float32)
     ks = [0, 1, 15, 16, 31, 32, K // 2 + 5, K - 1]

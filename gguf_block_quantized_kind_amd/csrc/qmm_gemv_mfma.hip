@@ -41,10 +41,10 @@ template <typename XT> struct XVec;
 template <> struct XVec<float> { typedef float type __attribute__((ext_vector_type(4))); };
 template <> struct XVec<_Float16> { typedef _Float16 type __attribute__((ext_vector_type(4))); };
 
-template <int KIND, typename XT, int MT, int S, int R, int PD, int OCC>
+template <int KIND, typename XT, int MT, int S, int R, int PD, int OCC, bool ROUTED>
 __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void gemv_mfma_kernel(
     const uint8_t *__restrict__ W, int64_t row_bytes, const XT *__restrict__ X, float *__restrict__ Y, int M,
-    int64_t N, int K) {
+    int64_t N, int K, MoeRoute rt) {
   using Dd = Dec<KIND>;
   using XS = XSlice<KIND, MT>;
   using X4 = typename XVec<XT>::type;
@@ -52,7 +52,20 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   extern __shared__ u32x4 lds[];  // S rings of PD+1 k-blocks, one zero fragment; later the reduction
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 15, G = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * (16 * R);
+  // Routed experts: this workgroup serves one work item, up to MT pairs
+  // order[c0 ..] of expert e, whose rows start at expert e's weights.
+  int c0 = 0;
+  const int32_t *order = nullptr;
+  if constexpr (ROUTED) {
+    const int item = blockIdx.x;
+    if (item >= rt.ws[rt.nwork_at]) return;  // the whole workgroup leaves before any barrier
+    const int e = rt.ws[rt.work_at + 2 * item];
+    c0 = rt.ws[rt.work_at + 2 * item + 1];
+    order = rt.ws + rt.order_at;
+    M = min(MT, rt.ws[rt.offsets_at + e + 1] - c0);
+    W += (int64_t)e * N * row_bytes;
+  }
+  const int64_t row0 = (int64_t)(ROUTED ? blockIdx.y : blockIdx.x) * (16 * R);
   const int nkb = K / Dd::KB;
   u32x4 *ring = lds + wave * (PD + 1) * kFrag;
   const u32x4 *zero = lds + S * (PD + 1) * kFrag;
@@ -79,7 +92,12 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
     const int h = lane + 64 * i, f = h >> 1;
     const int g2 = f & 3, t = (f >> 2) % MT, st = (f >> 2) / MT;
     xlive[i] = h < XS::kHalves && t < M;
-    xoff[i] = xlive[i] ? t * K + Dd::x_off(st, g2, h & 1) : 0;
+    int64_t xrow = (int64_t)t * K;
+    if constexpr (ROUTED) {
+      const int pair = xlive[i] ? order[c0 + t] : 0;
+      xrow = (int64_t)(rt.x_per_slot ? pair : pair / rt.topk) * K;
+    }
+    xoff[i] = xlive[i] ? xrow + Dd::x_off(st, g2, h & 1) : 0;
     xdst[i] = h < XS::kHalves ? h : -1;
   }
 
@@ -181,24 +199,25 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int t = 4 * G + q;
-      if (t < M) Y[(int64_t)t * N + row] = acc[r][q];
+      if (t < M) Y[(int64_t)(ROUTED ? order[c0 + t] : t) * N + row] = acc[r][q];
     }
   }
 }
 
-template <int KIND, int MT, int S, int R, int PD, int OCC = 1>
+template <int KIND, int MT, int S, int R, int PD, int OCC = 1, bool ROUTED = false>
 static hipError_t run(const uint8_t *W, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,
-                      hipStream_t s) {
+                      hipStream_t s, MoeRoute rt = MoeRoute{}, int items = 0) {
   const int64_t row_bytes = (K / Geometry<KIND>::elems) * Geometry<KIND>::bytes;
   const size_t ring = (size_t)S * (PD + 1) * XSlice<KIND, MT>::kFrag * 16 + 16;
   const size_t lds = std::max<size_t>(ring, (size_t)(S - 1) * R * 64 * sizeof(floatx4));
-  const dim3 grid((unsigned)((N + 16 * R - 1) / (16 * R))), block(64 * S);
+  const unsigned tiles = (unsigned)((N + 16 * R - 1) / (16 * R));
+  const dim3 grid = ROUTED ? dim3((unsigned)items, tiles) : dim3(tiles), block(64 * S);
   if (x_f16)
-    hipLaunchKernelGGL((gemv_mfma_kernel<KIND, _Float16, MT, S, R, PD, OCC>), grid, block, lds, s, W, row_bytes,
-                       (const _Float16 *)x, y, M, N, (int)K);
+    hipLaunchKernelGGL((gemv_mfma_kernel<KIND, _Float16, MT, S, R, PD, OCC, ROUTED>), grid, block, lds, s, W,
+                       row_bytes, (const _Float16 *)x, y, M, N, (int)K, rt);
   else
-    hipLaunchKernelGGL((gemv_mfma_kernel<KIND, float, MT, S, R, PD, OCC>), grid, block, lds, s, W, row_bytes,
-                       (const float *)x, y, M, N, (int)K);
+    hipLaunchKernelGGL((gemv_mfma_kernel<KIND, float, MT, S, R, PD, OCC, ROUTED>), grid, block, lds, s, W,
+                       row_bytes, (const float *)x, y, M, N, (int)K, rt);
   return hipGetLastError();
 }
 
@@ -226,7 +245,46 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
   return run<KIND, 8, 2, 2, 2>(W, x, x_f16, y, M, N, K, s);
 }
 
+template <int KIND>
+static hipError_t run_routed(const uint8_t *W, const void *x, int x_f16, float *y, int mt, int64_t N, int64_t K,
+                             hipStream_t s, const MoeRoute &rt, int items) {
+  static const int cfg = [] {
+    const char *e = getenv("QMM_MOE_CFG");
+    return e ? atoi(e) : 0;
+  }();
+  if (mt == 1) return run<KIND, 1, 2, 1, 2, 1, true>(W, x, x_f16, y, 1, N, K, s, rt, items);
+  if (mt == 8) return run<KIND, 8, 2, 2, 2, 1, true>(W, x, x_f16, y, 8, N, K, s, rt, items);
+  if (cfg == 1) return run<KIND, 16, 2, 1, 2, 1, true>(W, x, x_f16, y, 16, N, K, s, rt, items);
+  if (cfg == 2) return run<KIND, 16, 4, 1, 1, 1, true>(W, x, x_f16, y, 16, N, K, s, rt, items);
+  return run<KIND, 16, 2, 1, 1, 1, true>(W, x, x_f16, y, 16, N, K, s, rt, items);
+}
+
 }  // namespace gv
+
+bool moe_mfma_supported(int kind, int64_t K) {
+  switch (kind) {
+    case Q4_K: case Q6_K: case IQ4_XS: case Q4_0: case Q5_0: case Q8_0: case IQ4_NL: case MXFP4:
+      return K % 256 == 0;
+    default:
+      return false;
+  }
+}
+
+hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int mt, int64_t N,
+                           int64_t K, const MoeRoute &rt, int items, hipStream_t s) {
+  switch (kind) {
+    case Q4_K: return gv::run_routed<Q4_K>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q6_K: return gv::run_routed<Q6_K>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case IQ4_XS: return gv::run_routed<IQ4_XS>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q4_0: return gv::run_routed<Q4_0>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q5_0: return gv::run_routed<Q5_0>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q8_0: return gv::run_routed<Q8_0>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case IQ4_NL: return gv::run_routed<IQ4_NL>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case MXFP4: return gv::run_routed<MXFP4>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    default: break;
+  }
+  return hipErrorNotSupported;
+}
 
 // Returns hipErrorNotSupported when the kind has no matrix-core decoder or K
 // is not a whole number of the decoder's k-blocks.

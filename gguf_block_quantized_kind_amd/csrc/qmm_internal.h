@@ -34,4 +34,19 @@ hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids,
 // Largest expert count the routing prologue handles.
 constexpr int64_t kMoeMaxExperts = 4096;
 
+// Where the grouped expert kernel finds the routing in the workspace (int32
+// offsets into it): per-expert offsets, the pair order, the number of work
+// items and the items themselves (expert, first pair index).
+struct MoeRoute {
+  const int32_t *ws;
+  int offsets_at, order_at, nwork_at, work_at;
+  int topk, x_per_slot;
+};
+
+// The matrix-core expert kernel: one workgroup per (work item, 16-row
+// tile); a work item is up to `mt` (1, 8 or 16) pairs of one expert.
+bool moe_mfma_supported(int kind, int64_t K);
+hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int mt, int64_t N,
+                           int64_t K, const MoeRoute &rt, int items, hipStream_t s);
+
 }  // namespace qmm

@@ -1,27 +1,45 @@
 // qmm_moe.hip -- routed expert products in one grouped launch.
 //
 // A one-workgroup prologue groups the (token, slot) pairs by expert: it counts
-// the pairs per expert, scans the counts into offsets and scatters the pair
-// indices into expert order in the workspace.  The grouped kernel then runs
-// one wave per (expert, weight row): the wave decodes the row exactly, as the
-// decode GEMV does, and multiplies it with the activations of up to eight of
-// the expert's pairs at a time, so each touched expert's weights are streamed
-// from memory once per eight pairs and untouched experts cost one early exit.
+// the pairs per expert, scans the counts into offsets, scatters the pair
+// indices into expert order in the workspace and cuts every expert's pairs
+// into work items of at most `mt` pairs.
+//
+// Kinds with a matrix-core GEMV decoder (and K a whole number of 256-element
+// k-blocks) then run the matrix-core GEMV kernel in its routed form: one
+// workgroup per (work item, 16-row tile), the item's pairs as the tokens, so
+// each touched expert's weights stream from memory once per item (mt = 16,
+// 8 or 1 pairs, by the average number of pairs per expert).  The other cases run one wave per
+// (expert, weight row), decoding the row to f32 and applying it to up to
+// eight of the expert's pairs at a time.
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
 namespace qmm {
 
-// Workspace layout (int32): counts[E], offsets[E + 1], order[M * topk].
+// Workspace layout (int32): counts[E], offsets[E + 1], order[P], nwork,
+// work[2 * (P + min(E, P))] with P = M * topk pairs.  Every expert with c
+// pairs gives ceil(c / mt) items, so there are at most P / mt + min(E, P).
+struct MoeLayout {
+  int64_t E, P;
+  __host__ __device__ int64_t offsets() const { return E; }
+  __host__ __device__ int64_t order() const { return 2 * E + 1; }
+  __host__ __device__ int64_t nwork() const { return 2 * E + 1 + P; }
+  __host__ __device__ int64_t work() const { return 2 * E + 2 + P; }
+  int64_t max_items() const { return P + (E < P ? E : P); }
+  int64_t words() const { return work() + 2 * max_items(); }
+};
+
 size_t moe_workspace_bytes(int64_t E, int64_t M, int64_t topk) {
-  return (size_t)(E + (E + 1) + M * topk) * sizeof(int32_t);
+  return (size_t)MoeLayout{E, M * topk}.words() * sizeof(int32_t);
 }
 
 __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restrict__ ids, int64_t pairs,
-                                                         int E, int32_t *__restrict__ ws) {
-  extern __shared__ int32_t lds[];  // counts[E] then cursor[E]
-  int32_t *cnt = lds, *cur = lds + E;
-  int32_t *offsets = ws + E, *order = ws + 2 * E + 1;
+                                                         int E, int mt, int32_t *__restrict__ ws) {
+  extern __shared__ int32_t lds[];  // counts[E], cursor[E], first item[E]
+  int32_t *cnt = lds, *cur = lds + E, *wof = lds + 2 * E;
+  const MoeLayout L{E, pairs};
+  int32_t *offsets = ws + L.offsets(), *order = ws + L.order(), *work = ws + L.work();
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
   for (int64_t p = threadIdx.x; p < pairs; p += blockDim.x) {
@@ -30,19 +48,29 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int run = 0;
+    int run = 0, items = 0;
     for (int e = 0; e < E; ++e) {
       offsets[e] = run;
       cur[e] = run;
+      wof[e] = items;
       ws[e] = cnt[e];
       run += cnt[e];
+      items += (cnt[e] + mt - 1) / mt;
     }
     offsets[E] = run;
+    ws[L.nwork()] = items;
   }
   __syncthreads();
   for (int64_t p = threadIdx.x; p < pairs; p += blockDim.x) {
     const int e = ids[p];
     if (e >= 0 && e < E) order[atomicAdd(&cur[e], 1)] = (int32_t)p;
+  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    for (int c = 0; c < cnt[e]; c += mt) {
+      const int item = wof[e] + c / mt;
+      work[2 * item] = e;
+      work[2 * item + 1] = offsets[e] + c;
+    }
   }
 }
 
@@ -52,7 +80,7 @@ __global__ __launch_bounds__(256) void moe_rows_kernel(const uint8_t *__restrict
                                                        const XT *__restrict__ X, int x_per_slot,
                                                        float *__restrict__ Y, int64_t N, int K) {
   const int e = blockIdx.y;
-  const int32_t *offsets = ws + E, *order = ws + 2 * E + 1;
+  const int32_t *offsets = ws + E, *order = ws + 2 * E + 1;  // MoeLayout
   const int begin = offsets[e], end = offsets[e + 1];
   if (begin == end) return;  // expert not routed to: the whole block leaves
   const int lane = threadIdx.x & 63;
@@ -114,10 +142,22 @@ hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids,
                       const void *X, int x_f16, int x_per_slot, float *Y, int64_t M, int64_t N,
                       int64_t K, void *ws, hipStream_t s) {
   int32_t *wsi = static_cast<int32_t *>(ws);
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), (size_t)(2 * E) * sizeof(int32_t), s, ids,
-                     M * topk, (int)E, wsi);
+  const MoeLayout L{E, M * topk};
+  // The matrix-core kernel addresses activations with 32-bit element offsets.
+  const bool mfma = moe_mfma_supported(kind, K) && L.P * K < ((int64_t)1 << 31);
+  // Pairs per work item: 16 (one full matrix-core tile of tokens) when
+  // experts average more than 8 pairs, 8 when pairs outnumber experts, else 1.
+  const int64_t touched = E < L.P ? E : L.P;
+  const int mt = !mfma ? 1 : (L.P > 8 * touched ? 16 : (L.P > E ? 8 : 1));
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), (size_t)(3 * E) * sizeof(int32_t), s, ids,
+                     M * topk, (int)E, mt, wsi);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (mfma) {
+    const MoeRoute rt{wsi, (int)L.offsets(), (int)L.order(), (int)L.nwork(), (int)L.work(), (int)topk, x_per_slot};
+    const int64_t items = (L.P + mt - 1) / mt + (E < L.P ? E : L.P);
+    return launch_moe_mfma(kind, W, X, x_f16, Y, mt, N, K, rt, (int)items, s);
+  }
   switch (kind) {
 #define QMM_CASE(K_) \
   case K_:           \

@@ -241,23 +241,30 @@ def test_matmul_dispatch_and_determinism(oracle_mod):
 # ---------------------------------------------------------------------------
 # Routed experts
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("kind", ["Q4_K", "Q8_0", "MXFP4", "Q6_K"])
+@pytest.mark.parametrize("kind", ["Q4_K", "Q8_0", "MXFP4", "Q6_K", "IQ4_XS", "Q5_0", "Q5_K"])
 def test_moe_parity(oracle_mod, kind):
-    E, N, K, M, topk = 6, 130, small_K(kind), 5, 3
-    g = wl.rng("gpu_moe", kind)
-    W = wl.random_weights(kind, E * N, K, g)
-    ids = wl.routing(M, E, topk, g)
-    ids[0] = [1, 2, 3]   # expert 1 is routed from two tokens
-    ids[1] = [1, 4, 5]
-    Wd, idd = dev(W), dev(ids)
-    for per_slot, xdt in ((False, np.float16), (True, np.float32), (True, np.float16)):
-        X = wl.activations((M, topk, K) if per_slot else (M, K), xdt, g)
-        Y = filled((M, topk, N))
-        nbytes = qmm.qmm_moe_workspace_bytes(E, M, topk)
-        ws = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device="cuda")
-        qmm.qmm_moe(kind, Wd, E, idd, topk, dev(X), int(per_slot), Y, M, N, K, ws)
-        Yr, Br = oracle_mod.moe(kind, W, E, N, K, ids, X, per_slot)
-        assert_within_bound(host(Y), Yr, Br, f"{kind} moe per_slot={per_slot}")
+    """Both expert kernels: K=1280 reaches the matrix-core one for every kind
+    that has a decoder (M=40: items of 16 pairs; M=5, 9: 8 pairs; M=2: 1
+    pair), K=1312 and Q5_K the f32 one."""
+    E, N, topk = 6, 130, 3
+    for K in gemv_Ks(kind):
+        for M in (5, 2, 9, 40):
+            g = wl.rng("gpu_moe", f"{kind}_{K}_{M}")
+            W = wl.random_weights(kind, E * N, K, g)
+            ids = wl.routing(M, E, topk, g)
+            ids[0] = [1, 2, 3]   # expert 1 is routed from two tokens
+            ids[1] = [1, 4, 5]
+            if M == 9:
+                ids[:, 0] = 0    # expert 0 takes 9 pairs: two items of up to 8
+            Wd, idd = dev(W), dev(ids)
+            for per_slot, xdt in ((False, np.float16), (True, np.float32), (True, np.float16)):
+                X = wl.activations((M, topk, K) if per_slot else (M, K), xdt, g)
+                Y = filled((M, topk, N))
+                nbytes = qmm.qmm_moe_workspace_bytes(E, M, topk)
+                ws = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device="cuda")
+                qmm.qmm_moe(kind, Wd, E, idd, topk, dev(X), int(per_slot), Y, M, N, K, ws)
+                Yr, Br = oracle_mod.moe(kind, W, E, N, K, ids, X, per_slot)
+                assert_within_bound(host(Y), Yr, Br, f"{kind} K={K} M={M} moe per_slot={per_slot}")
 
 
 # ---------------------------------------------------------------------------

@@ -110,7 +110,10 @@ def test_gemm_refusals_in_order(lib):
 def test_moe_refusals_in_order(lib):
     g = lib.qmm_moe
     ws_need = lib.qmm_moe_workspace_bytes(128, 16, 8)
-    assert ws_need == (128 + 129 + 16 * 8) * 4
+    # int32 counts[E], offsets[E+1], order[P], item count, items[2 (P + min(E, P))]
+    P = 16 * 8
+    assert ws_need == (128 + 129 + P + 1 + 2 * (P + min(128, P))) * 4
+    assert lib.qmm_moe_workspace_bytes(128, 1, 8) == (128 + 129 + 8 + 1 + 2 * (8 + 8)) * 4
     args = dict(kind=12, W=FAKE, E=128, ids=FAKE, topk=8, X=FAKE, dt=1, per=0, Y=FAKE, M=16, N=1536,
                 K=2048, ws=FAKE, wsb=ws_need, s=None)
 

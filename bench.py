@@ -182,6 +182,53 @@ def measured_traffic(kernel_case: str):
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
+def _pmc_average(directory: str, counter: str, kernel_substr: str) -> tuple[float, int]:
+    """Average per-dispatch value of `counter` over the dispatches of kernels
+    whose name contains kernel_substr, from rocprofv3's counter_collection
+    CSV files under `directory`."""
+    import csv
+    import glob
+
+    vals = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter and kernel_substr in row["Kernel_Name"]:
+                    vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} samples for '{kernel_substr}' under {directory}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(case, case_fetch, case_write, copy_fetch, copy_write, copy_bytes):
+    """HBM bytes per launch of one decode GEMV case from FETCH_SIZE /
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for a plain device copy of copy_bytes (it reads and writes copy_bytes)."""
+    cf, _ = _pmc_average(copy_fetch, "FETCH_SIZE", "copyBuffer")
+    cw, _ = _pmc_average(copy_write, "WRITE_SIZE", "copyBuffer")
+    fetch_scale = copy_bytes / (cf * 1024.0)
+    write_scale = copy_bytes / (cw * 1024.0)
+    out = {"source_digest": source_digest(), "copy_bytes": copy_bytes,
+           "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": fetch_scale, "write_scale": write_scale, "cases": {}}
+    f, nf = _pmc_average(case_fetch, "FETCH_SIZE", "gemv_mfma_kernel")
+    w, nw = _pmc_average(case_write, "WRITE_SIZE", "gemv_mfma_kernel")
+    out["cases"][case] = {"fetch_kib": f, "write_kib": w, "dispatches": [nf, nw],
+                          "hbm_bytes_per_launch": round(f * 1024.0 * fetch_scale + w * 1024.0 * write_scale)}
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, "traffic.json")
+    old = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            old = json.load(fh)
+    if old.get("source_digest") == out["source_digest"]:
+        old["cases"].update(out["cases"])
+        out["cases"] = old["cases"]
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def cpu_baseline(wl, target_seconds: float) -> dict:
     import oracle
 
@@ -212,7 +259,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0: skip)")
+    ap.add_argument("--profile-case", metavar="NAME",
+                    help="counter-collection mode: launch only this decode GEMV case, eagerly, --steps times")
+    ap.add_argument("--copy-probe", type=int, metavar="MIB",
+                    help="counter-calibration mode: --steps device copies of MIB MiB each")
+    ap.add_argument("--write-traffic", nargs=5, metavar=("CASE", "CASE_FETCH", "CASE_WRITE", "COPY_FETCH",
+                                                          "COPY_WRITE"),
+                    help="turn four rocprofv3 --pmc output directories (FETCH_SIZE and WRITE_SIZE of a "
+                         "--profile-case CASE run and of --copy-probe runs) into an entry of "
+                         "profiles/traffic.json")
+    ap.add_argument("--copy-mib", type=int, default=256, help="size of the --copy-probe copies (for --write-traffic)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, copy_bytes=args.copy_mib << 20)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -229,7 +289,23 @@ def main():
     qmm.load_library()
     props = torch.cuda.get_device_properties(0)
 
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel(), "copies": args.steps}))
+        return
+
     cases = gemv_cases(torch, qmm, wl)
+    if args.profile_case:
+        case = next(c for c in cases if c.name == args.profile_case)
+        for i in range(args.steps):
+            case.launch(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_case": case.name, "launches": args.steps}))
+        return
     for c in cases:  # eager once: loads the code objects before capture
         c.launch(0)
     torch.cuda.synchronize()

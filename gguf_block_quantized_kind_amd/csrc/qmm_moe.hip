@@ -34,38 +34,61 @@ size_t moe_workspace_bytes(int64_t E, int64_t M, int64_t topk) {
   return (size_t)MoeLayout{E, M * topk}.words() * sizeof(int32_t);
 }
 
+// One workgroup of 1024 threads; E <= 4096 experts, so each thread owns at
+// most four consecutive experts in the scans.
 __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restrict__ ids, int64_t pairs,
                                                          int E, int mt, int32_t *__restrict__ ws) {
-  extern __shared__ int32_t lds[];  // counts[E], cursor[E], first item[E]
+  extern __shared__ int32_t lds[];  // counts[E], cursor[E], first item[E], then 2 x 1024 scan slots
   int32_t *cnt = lds, *cur = lds + E, *wof = lds + 2 * E;
+  int32_t *scan_p = lds + 3 * E, *scan_i = scan_p + 1024;
   const MoeLayout L{E, pairs};
   int32_t *offsets = ws + L.offsets(), *order = ws + L.order(), *work = ws + L.work();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
-  for (int64_t p = threadIdx.x; p < pairs; p += blockDim.x) {
+  for (int64_t p = tid; p < pairs; p += blockDim.x) {
     const int e = ids[p];
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0, items = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = run;
-      cur[e] = run;
-      wof[e] = items;
-      ws[e] = cnt[e];
-      run += cnt[e];
-      items += (cnt[e] + mt - 1) / mt;
-    }
-    offsets[E] = run;
-    ws[L.nwork()] = items;
+  // Exclusive scans of the pair counts and of the item counts: each thread
+  // sums its experts, a Hillis-Steele scan runs over the 1024 partial sums,
+  // then each thread writes its experts' offsets.
+  const int per = (E + 1023) / 1024, e0 = tid * per, e1 = min(E, e0 + per);
+  int sp = 0, si = 0;
+  for (int e = e0; e < e1; ++e) {
+    sp += cnt[e];
+    si += (cnt[e] + mt - 1) / mt;
+  }
+  scan_p[tid] = sp;
+  scan_i[tid] = si;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int ap = tid >= off ? scan_p[tid - off] : 0, ai = tid >= off ? scan_i[tid - off] : 0;
+    __syncthreads();
+    scan_p[tid] += ap;
+    scan_i[tid] += ai;
+    __syncthreads();
+  }
+  int run = scan_p[tid] - sp, items = scan_i[tid] - si;  // exclusive prefix of this thread's experts
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = run;
+    cur[e] = run;
+    wof[e] = items;
+    ws[e] = cnt[e];
+    run += cnt[e];
+    items += (cnt[e] + mt - 1) / mt;
+  }
+  if (tid == 1023) {
+    offsets[E] = scan_p[1023];
+    ws[L.nwork()] = scan_i[1023];
   }
   __syncthreads();
-  for (int64_t p = threadIdx.x; p < pairs; p += blockDim.x) {
+  for (int64_t p = tid; p < pairs; p += blockDim.x) {
     const int e = ids[p];
     if (e >= 0 && e < E) order[atomicAdd(&cur[e], 1)] = (int32_t)p;
   }
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  for (int e = tid; e < E; e += blockDim.x) {
     for (int c = 0; c < cnt[e]; c += mt) {
       const int item = wof[e] + c / mt;
       work[2 * item] = e;
@@ -149,7 +172,7 @@ hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids,
   // experts average more than 8 pairs, 8 when pairs outnumber experts, else 1.
   const int64_t touched = E < L.P ? E : L.P;
   const int mt = !mfma ? 1 : (L.P > 8 * touched ? 16 : (L.P > E ? 8 : 1));
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), (size_t)(3 * E) * sizeof(int32_t), s, ids,
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), (size_t)(3 * E + 2048) * sizeof(int32_t), s, ids,
                      M * topk, (int)E, mt, wsi);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

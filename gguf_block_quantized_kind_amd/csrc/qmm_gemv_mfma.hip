@@ -248,15 +248,11 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
 template <int KIND>
 static hipError_t run_routed(const uint8_t *W, const void *x, int x_f16, float *y, int mt, int64_t N, int64_t K,
                              hipStream_t s, const MoeRoute &rt, int items) {
-  static const int cfg = [] {
-    const char *e = getenv("QMM_MOE_CFG");
-    return e ? atoi(e) : 0;
-  }();
   if (mt == 1) return run<KIND, 1, 2, 1, 2, 1, true>(W, x, x_f16, y, 1, N, K, s, rt, items);
   if (mt == 8) return run<KIND, 8, 2, 2, 2, 1, true>(W, x, x_f16, y, 8, N, K, s, rt, items);
-  if (cfg == 1) return run<KIND, 16, 2, 1, 2, 1, true>(W, x, x_f16, y, 16, N, K, s, rt, items);
-  if (cfg == 2) return run<KIND, 16, 4, 1, 1, 1, true>(W, x, x_f16, y, 16, N, K, s, rt, items);
-  return run<KIND, 16, 2, 1, 1, 1, true>(W, x, x_f16, y, 16, N, K, s, rt, items);
+  // Sixteen pairs per item: the activation k-block staged by a wave serves
+  // four 16-row tiles.
+  return run<KIND, 16, 1, 4, 1, 1, true>(W, x, x_f16, y, 16, N, K, s, rt, items);
 }
 
 }  // namespace gv

@@ -254,7 +254,8 @@ static hipError_t run(const uint8_t *W, const void *A, int a_f16, float *C, int6
 
 // Tile shapes.  Up to 64 tokens: 64 x 128 tiles.  Otherwise 128 x 64 tiles
 // with 128-element stages while that grid still fits the 256 compute units
-// in one round, else 128 x 128 tiles (fewer re-reads of the activations).
+// in one round, else 128 x 128 tiles with 128-element stages and eight waves
+// (fewer re-reads of the activations, two waves per SIMD).
 template <int KIND>
 static hipError_t run_m(const uint8_t *W, const void *A, int a_f16, float *C, int64_t M, int64_t N, int64_t K,
                         hipStream_t s, int cfg) {
@@ -267,11 +268,12 @@ static hipError_t run_m(const uint8_t *W, const void *A, int a_f16, float *C, in
     case 6: return run<KIND, 128, 64, 128, 2, 2>(W, A, a_f16, C, M, N, K, s);
     case 7: return run<KIND, 128, 128, 128, 2, 2>(W, A, a_f16, C, M, N, K, s);
     case 8: return run<KIND, 64, 128, 128, 1, 4>(W, A, a_f16, C, M, N, K, s);
+    case 9: return run<KIND, 128, 128, 128, 2, 4>(W, A, a_f16, C, M, N, K, s);
     default: break;
   }
   if (M <= 64) return run<KIND, 64, 128, 64, 1, 4>(W, A, a_f16, C, M, N, K, s);
   if (((M + 127) / 128) * ((N + 63) / 64) <= 256) return run<KIND, 128, 64, 128, 2, 2>(W, A, a_f16, C, M, N, K, s);
-  return run<KIND, 128, 128, 64, 2, 2>(W, A, a_f16, C, M, N, K, s);
+  return run<KIND, 128, 128, 128, 2, 4>(W, A, a_f16, C, M, N, K, s);
 }
 
 }  // namespace gm

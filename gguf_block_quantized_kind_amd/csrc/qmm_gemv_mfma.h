@@ -117,7 +117,7 @@ __device__ __forceinline__ floatx4 mfma4f32(float a, float b, floatx4 c) {
 // ---------------------------------------------------------------------------
 struct DecQ4K {
   static constexpr int KB = 256, NSTEP = 8, NPART = 1, BYTES = 144;
-  static constexpr bool HAS_MIN = true;
+  static constexpr bool HAS_MIN = true, CHUNKED = false;
   struct Raw { u32x4 hdr, q0, q1; };
   struct Sc { uint32_t f_lo, b_lo, f_hi, b_hi; float d, mn_lo, mn_hi; };
 
@@ -191,7 +191,7 @@ struct DecQ4K {
 // ---------------------------------------------------------------------------
 struct DecQ6K {
   static constexpr int KB = 256, NSTEP = 8, NPART = 2, BYTES = 210;
-  static constexpr bool HAS_MIN = false;
+  static constexpr bool HAS_MIN = false, CHUNKED = false;
   struct Raw { u32x4 ql0, ql1, qh; u32x2 sc; uint32_t d; };
   struct Sc { uint32_t f[2][4], b[2][4]; float d; };
 
@@ -269,20 +269,28 @@ struct DecQ6K {
 // elements 4G..4G+3 and high nibbles 16+4G..16+4G+3 (half 0 and half 1 of
 // the group's 8 elements).  Q8_0: group G takes bytes 8G..8G+7.
 // ---------------------------------------------------------------------------
+// These decoders read many small fields per k-block, so the kernel does not
+// fetch them from global memory one by one: it loads the tile's k-block as
+// contiguous 16-byte chunks, stages them in LDS, and load() reads the fields
+// from that LDS copy (CHUNKED).  Field offsets below are therefore LDS
+// offsets inside one row's copy of the k-block, at the natural alignment of
+// the block layout (2 bytes, or 1 for MXFP4's 17-byte blocks).
+__device__ __forceinline__ uint32_t s16(const uint8_t *p) {
+  return *reinterpret_cast<const uint16_t *>(__builtin_assume_aligned(p, 2));
+}
+__device__ __forceinline__ uint32_t s32a2(const uint8_t *p) { return s16(p) | (s16(p + 2) << 16); }
+__device__ __forceinline__ uint32_t s32a1(const uint8_t *p) {
+  return (uint32_t)p[0] | (s16(p + 1) << 8) | ((uint32_t)p[3] << 24);  // p odd: p + 1 is even
+}
+
 struct StepBase {
   static constexpr int KB = 256, NSTEP = 8, NPART = 1;
-  static constexpr bool HAS_MIN = false, STEP_SCALE = true;
+  static constexpr bool HAS_MIN = false, STEP_SCALE = true, CHUNKED = true;
   struct Sc {};
   __device__ static int x_off(int s, int G, int h) { return 32 * s + 16 * h + 4 * G; }
   __device__ static bool ind(int, int, int) { return false; }
   __device__ static floatx4 post(floatx4 acc, const floatx4 *, floatx4, const Sc &) { return acc; }
 };
-
-__device__ __forceinline__ uint32_t ld4(const uint8_t *p) {
-  uint32_t v;
-  __builtin_memcpy(&v, p, 4);
-  return v;
-}
 
 // Four unsigned bytes u (low-nibble word) and four more (high-nibble word) as
 // the B fragment (1024 + u) - off in the order (0,2), (1,3) of each half.
@@ -303,8 +311,8 @@ struct DecQ4_0 : StepBase {
   __device__ static void load(const uint8_t *blk, int G, Raw &r) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      r.d[s] = rd16(blk + 18 * s);
-      r.q[s] = ld4(blk + 18 * s + 2 + 4 * G);
+      r.d[s] = s16(blk + 18 * s);
+      r.q[s] = s32a2(blk + 18 * s + 2 + 4 * G);
     }
   }
   __device__ static Sc prep(const Raw &, int) { return Sc{}; }
@@ -324,9 +332,9 @@ struct DecQ5_0 : StepBase {
   __device__ static void load(const uint8_t *blk, int G, Raw &r) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      r.d[s] = rd16(blk + 22 * s);
-      r.qh[s] = ld4(blk + 22 * s + 2) >> (4 * G);  // bits 0-3, 16-19: this group's fifth bits
-      r.q[s] = ld4(blk + 22 * s + 6 + 4 * G);
+      r.d[s] = s16(blk + 22 * s);
+      r.qh[s] = s32a2(blk + 22 * s + 2) >> (4 * G);  // bits 0-3, 16-19: this group's fifth bits
+      r.q[s] = s32a2(blk + 22 * s + 6 + 4 * G);
     }
   }
   __device__ static Sc prep(const Raw &, int) { return Sc{}; }
@@ -348,8 +356,8 @@ struct DecQ8_0 : StepBase {
   __device__ static void load(const uint8_t *blk, int G, Raw &r) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      r.d[s] = rd16(blk + 34 * s);
-      r.q[s] = ld8(blk + 34 * s + 2 + 8 * G);
+      r.d[s] = s16(blk + 34 * s);
+      r.q[s] = u32x2{s32a2(blk + 34 * s + 2 + 8 * G), s32a2(blk + 34 * s + 6 + 8 * G)};
     }
   }
   __device__ static Sc prep(const Raw &, int) { return Sc{}; }
@@ -369,8 +377,8 @@ struct DecIQ4NL : StepBase {
   __device__ static void load(const uint8_t *blk, int G, Raw &r) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      r.d[s] = rd16(blk + 18 * s);
-      r.q[s] = ld4(blk + 18 * s + 2 + 4 * G);
+      r.d[s] = s16(blk + 18 * s);
+      r.q[s] = s32a2(blk + 18 * s + 2 + 4 * G);
     }
   }
   __device__ static Sc prep(const Raw &, int) { return Sc{}; }
@@ -393,7 +401,7 @@ struct DecMXFP4 : StepBase {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       r.e[s] = blk[17 * s];
-      r.q[s] = ld4(blk + 17 * s + 1 + 4 * G);
+      r.q[s] = (s & 1) ? s32a2(blk + 17 * s + 1 + 4 * G) : s32a1(blk + 17 * s + 1 + 4 * G);
     }
   }
   __device__ static Sc prep(const Raw &, int) { return Sc{}; }
@@ -419,9 +427,10 @@ struct DecIQ4XS : StepBase {
   static constexpr int BYTES = 136;
   struct Raw { u32x2 h; uint32_t q[8]; };
   __device__ static void load(const uint8_t *blk, int G, Raw &r) {
-    r.h = ld8(blk);
+    r.h = *reinterpret_cast<const u32x2 *>(__builtin_assume_aligned(blk, 8));
 #pragma unroll
-    for (int s = 0; s < 8; ++s) r.q[s] = ld4(blk + 8 + 16 * s + 4 * G);
+    for (int s = 0; s < 8; ++s)
+      r.q[s] = *reinterpret_cast<const uint32_t *>(__builtin_assume_aligned(blk + 8 + 16 * s + 4 * G, 4));
   }
   __device__ static Sc prep(const Raw &, int) { return Sc{}; }
   __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {

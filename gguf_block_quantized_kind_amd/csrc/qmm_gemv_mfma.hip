@@ -37,6 +37,20 @@ struct XSlice {
   static constexpr int kPerLane = (kHalves + 63) / 64;
 };
 
+// Weight bytes a lane holds for one tile and k-block between issue and
+// decode: the decoder's own fields, or (CHUNKED decoders) its share of the
+// k-block as 16-byte chunks -- lane (j, G) holds chunks G, G+4, ... of row j.
+template <typename Dd>
+struct Chunks {
+  static constexpr int C = (Dd::BYTES + 15) / 16;  // chunks per row (the last may overlap)
+  static constexpr int L = (C + 3) / 4;            // chunks per lane
+  static constexpr int RS = 16 * C;                // staging bytes per row
+  struct Held { u32x4 c[L]; };
+  __device__ static int offset(int c) { return c < C - 1 ? 16 * c : Dd::BYTES - 16; }
+};
+template <typename Dd>
+using Held = typename std::conditional<Dd::CHUNKED, typename Chunks<Dd>::Held, typename Dd::Raw>::type;
+
 template <typename XT> struct XVec;
 template <> struct XVec<float> { typedef float type __attribute__((ext_vector_type(4))); };
 template <> struct XVec<_Float16> { typedef _Float16 type __attribute__((ext_vector_type(4))); };
@@ -49,7 +63,9 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   using XS = XSlice<KIND, MT>;
   using X4 = typename XVec<XT>::type;
   constexpr int kFrag = XS::kFrag;
-  extern __shared__ u32x4 lds[];  // S rings of PD+1 k-blocks, one zero fragment; later the reduction
+  extern __shared__ u32x4 lds[];  // S rings of PD+1 k-blocks, one zero fragment, S weight stagings;
+                                  // later the reduction
+  using CK = Chunks<Dd>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 15, G = lane >> 4;
   // Routed experts: this workgroup serves one work item, up to MT pairs
@@ -106,7 +122,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   // decoded, so the memory pipe stays busy through every compute phase.
   constexpr int NS = PD + 1;
   const int kb0 = (int)((int64_t)wave * nkb / S), kb1 = (int)((int64_t)(wave + 1) * nkb / S);
-  typename Dd::Raw raw[NS][R];
+  Held<Dd> raw[NS][R];
   X4 xv[NS][XS::kPerLane];
   auto issue = [&](int kb, int slot) {
 #pragma unroll
@@ -116,8 +132,19 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
       xv[slot][i] = v;
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) Dd::load(wr[r] + (int64_t)kb * Dd::BYTES, G, raw[slot][r]);
+    for (int r = 0; r < R; ++r) {
+      if constexpr (Dd::CHUNKED) {
+#pragma unroll
+        for (int i = 0; i < CK::L; ++i)  // past the last chunk: a harmless re-read of it
+          raw[slot][r].c[i] = ld16(wr[r] + (int64_t)kb * Dd::BYTES + CK::offset(min(4 * i + G, CK::C - 1)));
+      } else {
+        Dd::load(wr[r] + (int64_t)kb * Dd::BYTES, G, raw[slot][r]);
+      }
+    }
   };
+  // This wave's LDS copy of one tile's k-block (CHUNKED decoders): row j at
+  // j * RS, each chunk at its byte offset in the k-block.
+  uint8_t *stage = reinterpret_cast<uint8_t *>(lds + S * (PD + 1) * kFrag + 1) + wave * 16 * CK::RS;
 #pragma unroll
   for (int d = 0; d < PD; ++d)
     if (kb0 + d < kb1) issue(kb0 + d, d);
@@ -154,14 +181,39 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const typename Dd::Sc sc = Dd::prep(raw[d][r], G);
-        if constexpr (Dd::STEP_SCALE) {
+        if constexpr (Dd::CHUNKED) {
+          // Stage the tile's k-block in LDS, then read the decoder's fields.
+          uint8_t *row = stage + j * CK::RS;
+#pragma unroll
+          for (int i = 0; i < CK::L; ++i) {
+            const int c = 4 * i + G;
+            if (c >= CK::C) continue;
+            const u32x4 v = raw[d][r].c[i];
+            if (Dd::BYTES % 16 == 0 || c < CK::C - 1) {
+              *reinterpret_cast<u32x4 *>(row + 16 * c) = v;
+            } else {  // the overlapping last chunk: 8-byte aligned for every chunked layout
+              static_assert(Dd::BYTES % 8 == 0, "last chunk alignment");
+              *reinterpret_cast<u32x2 *>(row + Dd::BYTES - 16) = u32x2{v[0], v[1]};
+              *reinterpret_cast<u32x2 *>(row + Dd::BYTES - 8) = u32x2{v[2], v[3]};
+            }
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          typename Dd::Raw fr;
+          Dd::load(row, G, fr);
+          const typename Dd::Sc sc = Dd::prep(fr, G);
 #pragma unroll
           for (int st = 0; st < Dd::NSTEP; ++st) {
-            const floatx4 D = mfma16(a[st], Dd::bop(raw[d][r], sc, st, 0), floatx4{0.f, 0.f, 0.f, 0.f});
-            acc[r] = Dd::post_step(acc[r], D, raw[d][r], st);
+            const floatx4 D = mfma16(a[st], Dd::bop(fr, sc, st, 0), floatx4{0.f, 0.f, 0.f, 0.f});
+            acc[r] = Dd::post_step(acc[r], D, fr, st);
           }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();  // the staging is rewritten by the next tile
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         } else {
+          static_assert(!Dd::STEP_SCALE, "step-scaled decoders are staged");
+          const typename Dd::Sc sc = Dd::prep(raw[d][r], G);
           floatx4 D[Dd::NPART];
 #pragma unroll
           for (int p = 0; p < Dd::NPART; ++p) D[p] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -208,7 +260,8 @@ template <int KIND, int MT, int S, int R, int PD, int OCC = 1, bool ROUTED = fal
 static hipError_t run(const uint8_t *W, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,
                       hipStream_t s, MoeRoute rt = MoeRoute{}, int items = 0) {
   const int64_t row_bytes = (K / Geometry<KIND>::elems) * Geometry<KIND>::bytes;
-  const size_t ring = (size_t)S * (PD + 1) * XSlice<KIND, MT>::kFrag * 16 + 16;
+  const size_t ring = (size_t)S * (PD + 1) * XSlice<KIND, MT>::kFrag * 16 + 16 +
+                      (Dec<KIND>::CHUNKED ? (size_t)S * 16 * Chunks<Dec<KIND>>::RS : 0);
   const size_t lds = std::max<size_t>(ring, (size_t)(S - 1) * R * 64 * sizeof(floatx4));
   const unsigned tiles = (unsigned)((N + 16 * R - 1) / (16 * R));
   const dim3 grid = ROUTED ? dim3((unsigned)items, tiles) : dim3(tiles), block(64 * S);
@@ -231,6 +284,7 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
     case 2: if (M <= 1) return run<KIND, 1, 2, 1, 2>(W, x, x_f16, y, M, N, K, s); break;
     case 3: if (M <= 1) return run<KIND, 1, 2, 1, 3>(W, x, x_f16, y, M, N, K, s); break;
     case 7: if (M <= 1) return run<KIND, 1, 1, 1, 3>(W, x, x_f16, y, M, N, K, s); break;
+
     case 8: if (M <= 1) return run<KIND, 1, 8, 1, 1>(W, x, x_f16, y, M, N, K, s); break;
     case 9: if (M <= 1) return run<KIND, 1, 8, 1, 2>(W, x, x_f16, y, M, N, K, s); break;
     case 10: if (M <= 1) return run<KIND, 1, 4, 1, 2>(W, x, x_f16, y, M, N, K, s); break;
@@ -238,6 +292,13 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
     case 5: if (M > 4) return run<KIND, 8, 4, 2, 1>(W, x, x_f16, y, M, N, K, s); break;
     case 6: if (M > 4) return run<KIND, 8, 2, 2, 2>(W, x, x_f16, y, M, N, K, s); break;
     default: break;
+  }
+  if constexpr (Dec<KIND>::CHUNKED) {
+    // Staged decoders hold one k-block ahead and split K over 4 or 8 waves.
+    if (M <= 1) {
+      if (N < 8192) return run<KIND, 1, 8, 1, 1>(W, x, x_f16, y, M, N, K, s);
+      return run<KIND, 1, 4, 1, 1>(W, x, x_f16, y, M, N, K, s);
+    }
   }
   if (M <= 1) return run<KIND, 1, 2, 1, 2>(W, x, x_f16, y, M, N, K, s);
   if (M <= 2) return run<KIND, 2, 2, 1, 2>(W, x, x_f16, y, M, N, K, s);

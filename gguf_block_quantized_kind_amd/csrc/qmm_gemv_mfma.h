@@ -109,6 +109,19 @@ __device__ __forceinline__ floatx4 mfma4f32(float a, float b, floatx4 c) {
 //                        group G belongs to (indicator for the sums X_j)
 //   post(acc, D, X, sc)  acc += d * D[part] (- dmin * sum m_j X_j)
 
+// Reads from a wave-private LDS copy of the tile's k-block (CHUNKED decoders
+// below: the kernel loads the k-block as contiguous 16-byte chunks and stages
+// it there), at the natural alignment of each field in the block layout.
+// The folded Q4_K and Q6_K decoders load their few 16-byte fields straight
+// from global memory instead.
+__device__ __forceinline__ uint32_t s16(const uint8_t *p) {
+  return *reinterpret_cast<const uint16_t *>(__builtin_assume_aligned(p, 2));
+}
+__device__ __forceinline__ uint32_t s32a2(const uint8_t *p) { return s16(p) | (s16(p + 2) << 16); }
+__device__ __forceinline__ uint32_t s32a1(const uint8_t *p) {
+  return (uint32_t)p[0] | (s16(p + 1) << 8) | ((uint32_t)p[3] << 24);  // p odd: p + 1 is even
+}
+
 // ---------------------------------------------------------------------------
 // Q4_K.  Group G decodes the 32 bytes 32G..32G+31 of the codes: low nibbles
 // are elements 64G + [0,32) (sub-block 2G), high nibbles 64G + 32 + [0,32)
@@ -269,20 +282,6 @@ struct DecQ6K {
 // elements 4G..4G+3 and high nibbles 16+4G..16+4G+3 (half 0 and half 1 of
 // the group's 8 elements).  Q8_0: group G takes bytes 8G..8G+7.
 // ---------------------------------------------------------------------------
-// These decoders read many small fields per k-block, so the kernel does not
-// fetch them from global memory one by one: it loads the tile's k-block as
-// contiguous 16-byte chunks, stages them in LDS, and load() reads the fields
-// from that LDS copy (CHUNKED).  Field offsets below are therefore LDS
-// offsets inside one row's copy of the k-block, at the natural alignment of
-// the block layout (2 bytes, or 1 for MXFP4's 17-byte blocks).
-__device__ __forceinline__ uint32_t s16(const uint8_t *p) {
-  return *reinterpret_cast<const uint16_t *>(__builtin_assume_aligned(p, 2));
-}
-__device__ __forceinline__ uint32_t s32a2(const uint8_t *p) { return s16(p) | (s16(p + 2) << 16); }
-__device__ __forceinline__ uint32_t s32a1(const uint8_t *p) {
-  return (uint32_t)p[0] | (s16(p + 1) << 8) | ((uint32_t)p[3] << 24);  // p odd: p + 1 is even
-}
-
 struct StepBase {
   static constexpr int KB = 256, NSTEP = 8, NPART = 1;
   static constexpr bool HAS_MIN = false, STEP_SCALE = true, CHUNKED = true;

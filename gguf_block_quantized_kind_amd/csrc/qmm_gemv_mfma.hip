@@ -181,47 +181,57 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
+        typename Dd::Raw fr;  // the decoder's fields for this tile and k-block
         if constexpr (Dd::CHUNKED) {
           // Stage the tile's k-block in LDS, then read the decoder's fields.
           uint8_t *row = stage + j * CK::RS;
+          constexpr int rem = Dd::BYTES - 16 * (CK::C - 1);  // new bytes in the last chunk
 #pragma unroll
           for (int i = 0; i < CK::L; ++i) {
             const int c = 4 * i + G;
             if (c >= CK::C) continue;
             const u32x4 v = raw[d][r].c[i];
-            if (Dd::BYTES % 16 == 0 || c < CK::C - 1) {
+            if constexpr (rem == 16) {
               *reinterpret_cast<u32x4 *>(row + 16 * c) = v;
-            } else {  // the overlapping last chunk: 8-byte aligned for every chunked layout
-              static_assert(Dd::BYTES % 8 == 0, "last chunk alignment");
-              *reinterpret_cast<u32x2 *>(row + Dd::BYTES - 16) = u32x2{v[0], v[1]};
-              *reinterpret_cast<u32x2 *>(row + Dd::BYTES - 8) = u32x2{v[2], v[3]};
+            } else {
+              if (c < CK::C - 1) {
+                *reinterpret_cast<u32x4 *>(row + 16 * c) = v;
+              } else if constexpr (rem == 8) {  // the last chunk overlaps: store its new bytes
+                *reinterpret_cast<u32x2 *>(row + 16 * c) = u32x2{v[2], v[3]};
+              } else {
+                static_assert(rem == 2, "last chunk layout");
+                *reinterpret_cast<uint16_t *>(row + 16 * c) = (uint16_t)(v[3] >> 16);
+              }
             }
           }
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          typename Dd::Raw fr;
           Dd::load(row, G, fr);
-          const typename Dd::Sc sc = Dd::prep(fr, G);
+        } else {
+          fr = raw[d][r];
+        }
+        const typename Dd::Sc sc = Dd::prep(fr, G);
+        if constexpr (Dd::STEP_SCALE) {
 #pragma unroll
           for (int st = 0; st < Dd::NSTEP; ++st) {
             const floatx4 D = mfma16(a[st], Dd::bop(fr, sc, st, 0), floatx4{0.f, 0.f, 0.f, 0.f});
             acc[r] = Dd::post_step(acc[r], D, fr, st);
           }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();  // the staging is rewritten by the next tile
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         } else {
-          static_assert(!Dd::STEP_SCALE, "step-scaled decoders are staged");
-          const typename Dd::Sc sc = Dd::prep(raw[d][r], G);
           floatx4 D[Dd::NPART];
 #pragma unroll
           for (int p = 0; p < Dd::NPART; ++p) D[p] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int st = 0; st < Dd::NSTEP; ++st)
 #pragma unroll
-            for (int p = 0; p < Dd::NPART; ++p) D[p] = mfma16(a[st], Dd::bop(raw[d][r], sc, st, p), D[p]);
+            for (int p = 0; p < Dd::NPART; ++p) D[p] = mfma16(a[st], Dd::bop(fr, sc, st, p), D[p]);
           acc[r] = Dd::post(acc[r], D, xsum, sc);
+        }
+        if constexpr (Dd::CHUNKED) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();  // the staging is rewritten by the next tile
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -97,7 +97,9 @@ int qmm_gemv_ex(int kind, const void *W, const void *x, int x_dtype, float *y,
 /* Prefill GEMM: C[M][N] = A[M][K] . W^T with f16 A, on the default stream.
  * Weight tiles are decoded to f16 and multiplied on the matrix cores with f32
  * accumulation (inferencelayer cublas_prefill.rs, CublasPrefill::gemm: f16
- * in, f32 accumulate, y = x . W^T). */
+ * in, f32 accumulate, y = x . W^T).  A decoded weight beyond the f16 range
+ * (|w| > 65504) becomes an infinity; the decode GEMV and qmm_moe keep every
+ * weight exact instead. */
 int qmm_gemm(int kind, const void *W, const void *A, float *C, int64_t M, int64_t N, int64_t K);
 
 /* Prefill GEMM for any M >= 1 with f32 or f16 A, on `stream`. */

@@ -205,6 +205,24 @@ def test_gemm_parity(oracle_mod, kind, xdt):
         assert_within_bound(host(C), Y, B, f"{kind} M={M} {xdt}")
 
 
+@pytest.mark.parametrize("kind", ["Q8_0", "IQ4_NL", "MXFP4", "Q4_K"])
+def test_gemm_large_grid_tiles(oracle_mod, kind):
+    """A grid larger than one round of 128 x 64 tiles takes the eight-wave
+    128 x 128 x 128 tiles; M, N and K are all ragged against them."""
+    M, N = 300, 9000
+    K = 1280 + (0 if wl.geometry(kind)[1] == 256 else 32)
+    g = wl.rng("gpu_gemm_large", kind)
+    W = wl.random_weights(kind, N, K, g)
+    X = wl.activations((M, K), np.float16, g)
+    C = filled((M, N))
+    qmm.qmm_gemm_ex(kind, dev(W), dev(X), C, M, N, K)
+    got = host(C)
+    rows = _sample_rows(N, g, n=300)
+    Y, B = oracle_mod.matmul(kind, W, K, X, rows=rows)
+    assert not np.any(got == SENTINEL)
+    assert_within_bound(got[:, rows], Y, B, f"{kind} M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("kind", ALL_KINDS)
 def test_gemm_unit_vectors_return_f16_weights(oracle_mod, kind):
     N, K = 130, small_K(kind)

@@ -259,6 +259,7 @@ static hipError_t run(const uint8_t *W, const void *A, int a_f16, float *C, int6
 template <int KIND>
 static hipError_t run_m(const uint8_t *W, const void *A, int a_f16, float *C, int64_t M, int64_t N, int64_t K,
                         hipStream_t s, int cfg) {
+#ifdef QMM_TUNING
   switch (cfg) {
     case 1: return run<KIND, 64, 128, 64, 1, 4>(W, A, a_f16, C, M, N, K, s);
     case 2: return run<KIND, 128, 128, 64, 2, 2>(W, A, a_f16, C, M, N, K, s);
@@ -271,6 +272,9 @@ static hipError_t run_m(const uint8_t *W, const void *A, int a_f16, float *C, in
     case 9: return run<KIND, 128, 128, 128, 2, 4>(W, A, a_f16, C, M, N, K, s);
     default: break;
   }
+#else
+  (void)cfg;
+#endif
   if (M <= 64) return run<KIND, 64, 128, 64, 1, 4>(W, A, a_f16, C, M, N, K, s);
   if (((M + 127) / 128) * ((N + 63) / 64) <= 256) return run<KIND, 128, 64, 128, 2, 2>(W, A, a_f16, C, M, N, K, s);
   return run<KIND, 128, 128, 128, 2, 4>(W, A, a_f16, C, M, N, K, s);
@@ -280,10 +284,16 @@ static hipError_t run_m(const uint8_t *W, const void *A, int a_f16, float *C, in
 
 hipError_t launch_gemm(int kind, const uint8_t *W, const void *A, int a_f16, float *C, int64_t M,
                        int64_t N, int64_t K, hipStream_t s) {
+  // Launch shapes are fixed by the rules in run_m.  A tuning build
+  // (-DQMM_TUNING) can pick an alternative shape from QMM_GEMM_CFG.
+#ifdef QMM_TUNING
   static const int cfg = [] {
     const char *e = getenv("QMM_GEMM_CFG");
     return e ? atoi(e) : 0;
   }();
+#else
+  constexpr int cfg = 0;
+#endif
   switch (kind) {
 #define QMM_CASE(K_) \
   case K_:           \

@@ -289,6 +289,7 @@ static hipError_t run(const uint8_t *W, const void *x, int x_f16, float *y, int 
 template <int KIND>
 static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,
                         hipStream_t s, int cfg) {
+#ifdef QMM_TUNING
   switch (cfg) {
     case 1: if (M <= 1) return run<KIND, 1, 4, 1, 1>(W, x, x_f16, y, M, N, K, s); break;
     case 2: if (M <= 1) return run<KIND, 1, 2, 1, 2>(W, x, x_f16, y, M, N, K, s); break;
@@ -303,6 +304,9 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
     case 6: if (M > 4) return run<KIND, 8, 2, 2, 2>(W, x, x_f16, y, M, N, K, s); break;
     default: break;
   }
+#else
+  (void)cfg;
+#endif
   if constexpr (Dec<KIND>::CHUNKED) {
     // Staged decoders hold one k-block ahead and split K over 4 or 8 waves.
     if (M <= 1) {
@@ -357,10 +361,16 @@ hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16,
 // is not a whole number of the decoder's k-blocks.
 hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int M,
                             int64_t N, int64_t K, hipStream_t s) {
+  // Launch shapes are fixed by the rules in run_m.  A tuning build
+  // (-DQMM_TUNING) can pick an alternative shape from QMM_GEMV_CFG.
+#ifdef QMM_TUNING
   static const int cfg = [] {
     const char *e = getenv("QMM_GEMV_CFG");
     return e ? atoi(e) : 0;
   }();
+#else
+  constexpr int cfg = 0;
+#endif
   switch (kind) {
     case Q4_K: return gv::run_m<Q4_K>(W, x, x_f16, y, M, N, K, s, cfg);
     case Q6_K: return gv::run_m<Q6_K>(W, x, x_f16, y, M, N, K, s, cfg);

@@ -9,7 +9,7 @@
 // k-blocks) then run the matrix-core GEMV kernel in its routed form: one
 // workgroup per (work item, 16-row tile), the item's pairs as the tokens, so
 // each touched expert's weights stream from memory once per item (mt = 16,
-// 8 or 1 pairs, by the average number of pairs per expert).  The other cases run one wave per
+// 8 or 1 pairs, by the number of pairs per expert).  The other cases run one wave per
 // (expert, weight row), decoding the row to f32 and applying it to up to
 // eight of the expert's pairs at a time.
 #include "qmm_device.h"
@@ -168,10 +168,11 @@ hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids,
   const MoeLayout L{E, M * topk};
   // The matrix-core kernel addresses activations with 32-bit element offsets.
   const bool mfma = moe_mfma_supported(kind, K) && L.P * K < ((int64_t)1 << 31);
-  // Pairs per work item: 16 (one full matrix-core tile of tokens) when
-  // experts average more than 8 pairs, 8 when pairs outnumber experts, else 1.
-  const int64_t touched = E < L.P ? E : L.P;
-  const int mt = !mfma ? 1 : (L.P > 8 * touched ? 16 : (L.P > E ? 8 : 1));
+  // Pairs per work item: 16 (one full matrix-core tile of tokens) when a
+  // uniform routing gives experts 16 pairs on average, 8 from 4 pairs on
+  // average, else 1 (an 8-pair item that carries one or two pairs costs
+  // more than streaming the expert once per pair).
+  const int mt = !mfma ? 1 : (L.P >= 16 * E ? 16 : (L.P >= 4 * E ? 8 : 1));
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), (size_t)(3 * E + 2048) * sizeof(int32_t), s, ids,
                      M * topk, (int)E, mt, wsi);
   hipError_t err = hipGetLastError();

@@ -262,7 +262,7 @@ def test_matmul_dispatch_and_determinism(oracle_mod):
 @pytest.mark.parametrize("kind", ["Q4_K", "Q8_0", "MXFP4", "Q6_K", "IQ4_XS", "Q5_0", "Q5_K"])
 def test_moe_parity(oracle_mod, kind):
     """Both expert kernels: K=1280 reaches the matrix-core one for every kind
-    that has a decoder (M=40: items of 16 pairs; M=5, 9: 8 pairs; M=2: 1
+    that has a decoder (M=40: items of 16 pairs; M=9: 8 pairs; M=2, 5: one
     pair), K=1312 and Q5_K the f32 one."""
     E, N, topk = 6, 130, 3
     for K in gemv_Ks(kind):

@@ -74,13 +74,23 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   const int32_t *order = nullptr;
   if constexpr (ROUTED) {
     const int item = blockIdx.x;
-    if (item >= rt.ws[rt.nwork_at]) return;  // the whole workgroup leaves before any barrier
-    const int e = rt.ws[rt.work_at + 2 * item];
-    c0 = rt.ws[rt.work_at + 2 * item + 1];
-    order = rt.ws + rt.order_at;
-    M = min(MT, rt.ws[rt.offsets_at + e + 1] - c0);
+    int e;
+    if (rt.ids != nullptr) {  // one pair per item, no grouping
+      e = item < rt.pairs ? rt.ids[item] : -1;
+      if (e < 0 || e >= rt.E) return;  // the whole workgroup leaves before any barrier
+      c0 = item;
+      M = 1;
+    } else {
+      if (item >= rt.ws[rt.nwork_at]) return;  // the whole workgroup leaves before any barrier
+      e = rt.ws[rt.work_at + 2 * item];
+      c0 = rt.ws[rt.work_at + 2 * item + 1];
+      order = rt.ws + rt.order_at;
+      M = min(MT, rt.ws[rt.offsets_at + e + 1] - c0);
+    }
     W += (int64_t)e * N * row_bytes;
   }
+  // Pair of token slot t of this item.
+  auto pair_of = [&](int t) { return order != nullptr ? order[c0 + t] : c0 + t; };
   const int64_t row0 = (int64_t)(ROUTED ? blockIdx.y : blockIdx.x) * (16 * R);
   const int nkb = K / Dd::KB;
   u32x4 *ring = lds + wave * (PD + 1) * kFrag;
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
     xlive[i] = h < XS::kHalves && t < M;
     int64_t xrow = (int64_t)t * K;
     if constexpr (ROUTED) {
-      const int pair = xlive[i] ? order[c0 + t] : 0;
+      const int pair = xlive[i] ? pair_of(t) : 0;
       xrow = (int64_t)(rt.x_per_slot ? pair : pair / rt.topk) * K;
     }
     xoff[i] = xlive[i] ? xrow + Dd::x_off(st, g2, h & 1) : 0;
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int t = 4 * G + q;
-      if (t < M) Y[(int64_t)(ROUTED ? order[c0 + t] : t) * N + row] = acc[r][q];
+      if (t < M) Y[(int64_t)(ROUTED ? pair_of(t) : t) * N + row] = acc[r][q];
     }
   }
 }

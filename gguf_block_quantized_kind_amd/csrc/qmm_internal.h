@@ -37,10 +37,14 @@ constexpr int64_t kMoeMaxExperts = 4096;
 // Where the grouped expert kernel finds the routing in the workspace (int32
 // offsets into it): per-expert offsets, the pair order, the number of work
 // items and the items themselves (expert, first pair index).
+// With `ids` set (items of one pair), work item i is pair i itself, its
+// expert read from ids[i], and the workspace lists are not used.
 struct MoeRoute {
   const int32_t *ws;
   int offsets_at, order_at, nwork_at, work_at;
   int topk, x_per_slot;
+  const int32_t *ids;
+  int E, pairs;
 };
 
 // The matrix-core expert kernel: one workgroup per (work item, 16-row

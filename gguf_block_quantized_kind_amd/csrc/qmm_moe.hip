@@ -9,7 +9,8 @@
 // k-blocks) then run the matrix-core GEMV kernel in its routed form: one
 // workgroup per (work item, 16-row tile), the item's pairs as the tokens, so
 // each touched expert's weights stream from memory once per item (mt = 16,
-// 8 or 1 pairs, by the number of pairs per expert).  The other cases run one wave per
+// 8 or 1 pairs, by the number of pairs per expert).  Items of one pair need
+// no grouping, so that case skips the prologue and reads ids directly.  The other cases run one wave per
 // (expert, weight row), decoding the row to f32 and applying it to up to
 // eight of the expert's pairs at a time.
 #include "qmm_device.h"
@@ -173,12 +174,19 @@ hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids,
   // average, else 1 (an 8-pair item that carries one or two pairs costs
   // more than streaming the expert once per pair).
   const int mt = !mfma ? 1 : (L.P >= 16 * E ? 16 : (L.P >= 4 * E ? 8 : 1));
+  if (mfma && mt == 1) {
+    // One pair per item needs no grouping: each workgroup reads its pair's
+    // expert from ids and the routing prologue is skipped.
+    const MoeRoute rt{wsi, 0, 0, 0, 0, (int)topk, x_per_slot, ids, (int)E, (int)L.P};
+    return launch_moe_mfma(kind, W, X, x_f16, Y, 1, N, K, rt, (int)L.P, s);
+  }
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), (size_t)(3 * E + 2048) * sizeof(int32_t), s, ids,
                      M * topk, (int)E, mt, wsi);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mfma) {
-    const MoeRoute rt{wsi, (int)L.offsets(), (int)L.order(), (int)L.nwork(), (int)L.work(), (int)topk, x_per_slot};
+    const MoeRoute rt{wsi, (int)L.offsets(), (int)L.order(), (int)L.nwork(), (int)L.work(), (int)topk, x_per_slot,
+                      nullptr, (int)E, (int)L.P};
     const int64_t items = (L.P + mt - 1) / mt + (E < L.P ? E : L.P);
     return launch_moe_mfma(kind, W, X, x_f16, Y, mt, N, K, rt, (int)items, s);
   }

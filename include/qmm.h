@@ -111,7 +111,7 @@ int qmm_matmul(int kind, const void *W, const void *A, int a_dtype, float *C,
                int64_t M, int64_t N, int64_t K, void *stream);
 
 /* Routed expert products, every expert in one grouped launch (plus a small
- * routing prologue).  W holds E experts of N rows each, back to back: expert
+ * routing prologue when an expert may receive several pairs).  W holds E experts of N rows each, back to back: expert
  * e's row n starts at byte (e * N + n) * qmm_row_bytes(kind, K).
  * ids is [M][topk] int32 in [0, E).  For token t and slot s with
  * e = ids[t][s]:  Y[t][s][:] = W_e . x, where x is X[t] when x_per_slot is 0

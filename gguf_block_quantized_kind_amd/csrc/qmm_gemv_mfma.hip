@@ -318,8 +318,10 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
   (void)cfg;
 #endif
   if constexpr (Dec<KIND>::CHUNKED) {
-    // Staged decoders hold one k-block ahead and split K over 4 or 8 waves.
+    // Staged decoders hold one k-block ahead and split K over 4 to 16 waves
+    // (more waves per tile when there are few tiles).
     if (M <= 1) {
+      if (N <= 4096) return run<KIND, 1, 16, 1, 1>(W, x, x_f16, y, M, N, K, s);
       if (N < 8192) return run<KIND, 1, 8, 1, 1>(W, x, x_f16, y, M, N, K, s);
       return run<KIND, 1, 4, 1, 1>(W, x, x_f16, y, M, N, K, s);
     }

@@ -66,7 +66,7 @@ int check_shape(int kind, int64_t M, int64_t N, int64_t K, const KindInfo **out)
   if (K % k->block_elems != 0)
     return fail(QMM_ERR_K_NOT_BLOCK_ALIGNED, "K=%lld is not a whole number of %s blocks (%d elements)",
                 (long long)K, k->name, k->block_elems);
-  if (K > (int64_t)1 << 30 || N > (int64_t)1 << 40)
+  if (K > (int64_t)1 << 30 || N > (int64_t)INT32_MAX)
     return fail(QMM_ERR_BAD_ARG, "K=%lld or N=%lld exceeds the supported range", (long long)K,
                 (long long)N);
   *out = k;

@@ -373,6 +373,8 @@ hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16,
 // is not a whole number of the decoder's k-blocks.
 hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int M,
                             int64_t N, int64_t K, hipStream_t s) {
+  // Activation offsets are 32-bit inside the kernel.
+  if ((int64_t)M * K >= ((int64_t)1 << 31)) return hipErrorNotSupported;
   // Launch shapes are fixed by the rules in run_m.  A tuning build
   // (-DQMM_TUNING) can pick an alternative shape from QMM_GEMV_CFG.
 #ifdef QMM_TUNING

@@ -35,8 +35,8 @@
  *
  * Errors.  Shape and argument errors are returned before anything is
  * launched, checked in this order: empty shape -> unsupported kind -> K not a
- * whole number of blocks -> bad dtype -> null pointer, misaligned activation
- * or out-of-range M -> workspace too small.  A refused call computes nothing
+ * whole number of blocks -> K > 2^30 or N > INT32_MAX -> bad dtype -> null
+ * pointer, misaligned activation or out-of-range M -> workspace too small.  A refused call computes nothing
  * (ferrox-cuda mul_mm.rs: kind_by_name and MulMmUnsupported -- a kind or
  * shape the kernel cannot do must be refused by name, never computed some
  * other way).  A failed launch returns QMM_ERR_HIP.  qmm_last_error() gives

@@ -93,6 +93,9 @@ def test_gemv_refusals_in_order(lib):
     assert g(2, FAKE, FAKE, 0, FAKE + 2, 1, 10, 64, None) == ARG   # y misaligned
     assert g(2, FAKE, FAKE, 0, FAKE, 9, 10, 64, None) == ARG       # M > 8
     assert lib.qmm_gemv(2, None, FAKE, FAKE, 10, 64) == ARG
+    # sizes beyond the kernels' 32-bit row and element counts
+    assert g(2, FAKE, FAKE, 0, FAKE, 1, 1 << 31, 64, None) == ARG   # N > INT32_MAX
+    assert g(2, FAKE, FAKE, 0, FAKE, 1, 10, (1 << 30) + 32, None) == ARG  # K > 2^30
 
 
 def test_gemm_refusals_in_order(lib):

@@ -239,6 +239,24 @@ def test_gemm_unit_vectors_return_f16_weights(oracle_mod, kind):
         assert np.array_equal(got[i], want[:, k]), f"{kind} column {k}"
 
 
+@pytest.mark.parametrize("kind", ALL_KINDS)
+def test_matmul_edge_shapes(oracle_mod, kind):
+    """Smallest shapes on every path: one block (and one 256-element
+    k-block) of K, a single row and a ragged 17 rows, M from 1 to 65."""
+    _, be = wl.geometry(kind)
+    g = wl.rng("gpu_edge", kind)
+    for K in sorted({be, 256}):
+        for N in (1, 17):
+            W = wl.random_weights(kind, N, K, g)
+            Wd = dev(W)
+            for M in (1, 8, 9, 65):
+                X = wl.activations((M, K), np.float16, g)
+                C = filled((M, N))
+                qmm.qmm_matmul(kind, Wd, dev(X), C, M, N, K)
+                Y, B = oracle_mod.matmul(kind, W, K, X)
+                assert_within_bound(host(C), Y, B, f"{kind} K={K} N={N} M={M}")
+
+
 def test_matmul_dispatch_and_determinism(oracle_mod):
     N, K = 300, 2048
     g = wl.rng("gpu_matmul", "dispatch")

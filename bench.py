@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 F16_MFMA_PEAK_TFLOPS = 2500.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense FP8 (and FP8 x FP4) matrix-core peak
 MALL_DEFEAT_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -129,6 +130,18 @@ def secondary_cases(torch, qmm, wl):
             qmm.qmm_matmul(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
 
         cases.append(Case(w.name, w.kind, launch, copies, w.weight_bytes, w.flops))
+    # The MXFP4 prefill workload again on the scaled FP8 x FP4 matrix cores
+    # (its own, looser tolerance; activations quantized to MX FP8 in the call).
+    for w in [w for w in wl.C4 if w.kind == "MXFP4" and w.M > 8]:
+        copies = make_copies(torch, w.weights())
+        x = torch.from_numpy(w.x()).cuda()
+        y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(qmm.qmm_gemm_mx_workspace_bytes(w.M, w.K), dtype=torch.uint8, device="cuda")
+
+        def launch(i, w=w, x=x, y=y, ws=ws, copies=copies):
+            qmm.qmm_gemm_mx(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K, ws)
+
+        cases.append(Case(w.name + "_mx", w.kind, launch, copies, w.weight_bytes, w.flops))
     for e in wl.C5:
         ids_np = e.ids()
         ids = torch.from_numpy(ids_np).cuda()
@@ -160,7 +173,9 @@ def describe(case: Case, seconds: float) -> dict:
     out = {"us_per_launch": round(seconds * 1e6, 3), "weight_bytes": case.weight_bytes,
            "weight_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
            "TFLOPs": round(tflops, 2)}
-    if "_m512" in case.name or "_m256" in case.name:
+    if case.name.endswith("_mx"):
+        out["mfma_fp8_frac"] = round(tflops / FP8_MFMA_PEAK_TFLOPS, 4)
+    elif "_m512" in case.name or "_m256" in case.name:
         out["mfma_f16_frac"] = round(tflops / F16_MFMA_PEAK_TFLOPS, 4)
     return out
 

@@ -54,6 +54,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         "qmm_matmul": (I, [I, P, P, I, P, I64, I64, I64, P]),
         "qmm_moe": (I, [I, P, I64, P, I64, P, I, I, P, I64, I64, I64, P, SZ, P]),
         "qmm_moe_workspace_bytes": (SZ, [I64, I64, I64]),
+        "qmm_gemm_mx": (I, [I, P, P, I, P, I64, I64, I64, P, SZ, P]),
+        "qmm_gemm_mx_workspace_bytes": (SZ, [I64, I64]),
         "qmm_dequant": (I, [I, P, P, I64, P]),
         "qmm_row_bytes": (I64, [I, I64]),
         "qmm_block_geometry": (I, [I, ctypes.POINTER(I), ctypes.POINTER(I)]),
@@ -108,6 +110,10 @@ def qmm_last_error() -> str:
 
 def qmm_moe_workspace_bytes(E: int, M: int, topk: int) -> int:
     return int(load_library().qmm_moe_workspace_bytes(int(E), int(M), int(topk)))
+
+
+def qmm_gemm_mx_workspace_bytes(M: int, K: int) -> int:
+    return int(load_library().qmm_gemm_mx_workspace_bytes(int(M), int(K)))
 
 
 def kind_id(kind) -> int:
@@ -197,6 +203,15 @@ def qmm_matmul(kind, W, A, C, M: int, N: int, K: int, stream=None):
                                      M, N, K, _stream(stream)))
 
 
+def qmm_gemm_mx(kind, W, A, C, M: int, N: int, K: int, workspace, stream=None):
+    _check_weights(kind, W, N, K)
+    _need(A, M * K, "A")
+    _need(C, M * N, "C")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().qmm_gemm_mx(kind_id(kind), _ptr(W), _ptr(A), _dtype_code(A), _ptr(C),
+                                      M, N, K, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def qmm_moe(kind, W, E: int, ids, topk: int, X, x_per_slot: int, Y, M: int, N: int, K: int,
             workspace, stream=None):
     _check_weights(kind, W, E * N, K)
@@ -250,6 +265,19 @@ def matmul(kind, W, A, N: int | None = None, stream=None):
     N = _rows_of(kind, W, K) if N is None else N
     C = torch.empty((M, N), dtype=torch.float32, device=A.device)
     qmm_matmul(kind, W, A, C, M, N, K, stream)
+    return C
+
+
+def gemm_mx(kind, W, A, N: int | None = None, stream=None, workspace=None):
+    """C [M, N] from MXFP4 weights with A quantized to MX FP8 (scaled FP4 matrix cores)."""
+    import torch
+    M, K = A.shape
+    N = _rows_of(kind, W, K) if N is None else N
+    C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if workspace is None:
+        nbytes = qmm_gemm_mx_workspace_bytes(M, K)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=A.device)
+    qmm_gemm_mx(kind, W, A, C, M, N, K, workspace, stream)
     return C
 
 

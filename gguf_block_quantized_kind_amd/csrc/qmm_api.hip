@@ -136,6 +136,38 @@ QMM_EXPORT int qmm_matmul(int kind, const void *W, const void *A, int a_dtype, f
   return qmm_gemm_ex(kind, W, A, a_dtype, C, M, N, K, stream);
 }
 
+QMM_EXPORT size_t qmm_gemm_mx_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
+  return qmm::gemm_mx_workspace_bytes(M, K);
+}
+
+QMM_EXPORT int qmm_gemm_mx(int kind, const void *W, const void *A, int a_dtype, float *C, int64_t M, int64_t N,
+                           int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+  const KindInfo *k;
+  int st = check_shape(kind, M, N, K, &k);
+  if (st) return st;
+  if (kind != QMM_MXFP4)
+    return fail(QMM_ERR_UNSUPPORTED_KIND, "the scaled FP4 GEMM takes MXFP4 weights only, not kind %d", kind);
+  if ((st = check_dtype(a_dtype))) return st;
+  if (!W || !C) return fail(QMM_ERR_BAD_ARG, "W or C is NULL");
+  if (!aligned(W, 16)) return fail(QMM_ERR_BAD_ARG, "W is not 16-byte aligned");
+  if ((st = check_act(A, a_dtype, "A"))) return st;
+  if (!aligned(C, 4)) return fail(QMM_ERR_BAD_ARG, "C is not 4-byte aligned");
+  // One workgroup per 64 x 256 tile in a one-dimensional grid.
+  const int64_t Mp = (M + 63) / 64 * 64;
+  if (M > (int64_t)65535 * 64 || (Mp / 64) * ((N + 255) / 256) > (int64_t)INT32_MAX - 7 ||
+      Mp * K > ((int64_t)1 << 40))
+    return fail(QMM_ERR_BAD_ARG, "M=%lld, N=%lld, K=%lld exceed the supported range", (long long)M,
+                (long long)N, (long long)K);
+  const size_t need = qmm::gemm_mx_workspace_bytes(M, K);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16))
+    return fail(QMM_ERR_WORKSPACE, "workspace needs %zu bytes at 16-byte alignment, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  return hip_status(qmm::launch_gemm_mx((const uint8_t *)W, A, a_dtype == QMM_F16, C, M, N, K, workspace,
+                                        (hipStream_t)stream),
+                    "gemm_mx launch");
+}
+
 QMM_EXPORT size_t qmm_moe_workspace_bytes(int64_t E, int64_t M, int64_t topk) {
   if (E <= 0 || M < 0 || topk <= 0) return 0;
   return qmm::moe_workspace_bytes(E, M, topk);

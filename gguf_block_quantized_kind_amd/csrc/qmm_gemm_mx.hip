@@ -1,0 +1,303 @@
+// qmm_gemm_mx.hip -- prefill GEMM for MXFP4 weights on gfx950's scaled
+// FP8 x FP4 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4).
+//
+// This is the separately toleranced variant of the MXFP4 prefill GEMM.  The
+// weights need no decode at all: for one 128-k step, lane (j, G) of a 16-row
+// tile holds weight row j, k = 32G .. 32G+31 -- exactly one MXFP4 block,
+// whose 16 code bytes are the FP4 B operand and whose E8M0 byte is the
+// lane's B scale.  The activations are quantized once, before the GEMM,
+// to MX FP8: per row and 32-element block, the shared E8M0 scale is the
+// smallest power of two 2^e with max |a| / 2^e <= 448 (E4M3's largest
+// value), so no element saturates, and each element is a / 2^e rounded to
+// E4M3 (nearest even).  That quantization is the variant's only rounding
+// besides the f32 accumulation; elements that are small integers times one
+// power of two per block (|a| <= 16 * 2^p) come through exactly.
+//
+// Operand layout of one 16 x 16 x 128 step (k counted within the step):
+//   B (FP4, 4 registers): lane (j, G) holds column j, k = 32G + p in nibble p
+//     of its 16 bytes, low nibble first;
+//   A (FP8, 8 registers): lane (j, G) holds row j, k = 16G + b in byte b of
+//     its first 16 bytes and k = 64 + 16G + b in byte b of the next 16;
+//   scales: lane group G gives the E8M0 scale of k = 32G .. 32G + 31, for A
+//     and for B, whichever lanes hold that block's A elements.
+// A GGUF MXFP4 block keeps element e < 16 in the low nibble of byte e and
+// element e + 16 in its high nibble, so nibble p is element p / 2 (p even)
+// or 16 + p / 2 (p odd).  The quantizer stores each block's activations in
+// that order, the weight bytes are used as they are, and a step's 128 FP8
+// bytes of a token are read as 16-byte chunks G and G + 4.
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace mx {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 64;   // tokens per tile (the workspace pads rows to this)
+constexpr int kBN = 256;  // weight rows per tile: 4 waves x 4 tiles of 16
+constexpr int kKS = 128;  // k per matrix-core step
+constexpr int kPD = 3;    // loads run this many steps ahead
+
+// Workspace: FP8 codes [Mp][K] bytes, then E8M0 scales [Mp][K / 32] bytes.
+struct Layout {
+  int64_t Mp, K;
+  Layout(int64_t M, int64_t K_) : Mp((M + kBM - 1) / kBM * kBM), K(K_) {}
+  int64_t scales() const { return Mp * K; }
+  int64_t bytes() const { return Mp * K + Mp * (K / 32); }
+};
+
+// Element of a 32-element block stored at position p (nibble p of the weights).
+__device__ __forceinline__ int src_of(int p) { return (p & 1) ? 16 + (p >> 1) : (p >> 1); }
+
+template <typename AT>
+__global__ __launch_bounds__(256) void quantize_kernel(const AT *__restrict__ A, int M, int64_t Mp, int K,
+                                                       uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+  const int nb = K / 32;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, block)
+  if (id >= Mp * nb) return;
+  const int64_t m = id / nb;
+  const int b = (int)(id % nb);
+  uint32_t out[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  uint32_t sbyte = 0u;  // rows past M: zero codes under the smallest scale
+  if (m < M) {
+    float a[32];
+    const AT *src = A + m * K + 32 * b;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) a[i] = (float)src[i];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(a[i]));
+    // amax = f * 2^x with f in [0.5, 1): 2^(x - 9) brings amax to [256, 512),
+    // one more step when that exceeds 448 (f > 0.875).
+    int e = -127;
+    if (amax > 0.f) {
+      const int x = __builtin_amdgcn_frexp_expf(amax);
+      e = x - 9 + (__builtin_amdgcn_frexp_mantf(amax) > 0.875f ? 1 : 0);
+    }
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    sbyte = (uint32_t)(e + 127);
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float s = __builtin_amdgcn_ldexpf(a[src_of(4 * w + q)], -e);
+        v[q] = fminf(fmaxf(s, -448.f), 448.f);
+      }
+      uint32_t packed = 0u;
+      packed = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], (int)packed, false);
+      packed = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], (int)packed, true);
+      out[w] = packed;
+    }
+  }
+  u32x4 *dst = reinterpret_cast<u32x4 *>(codes + m * K + 32 * b);
+  dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+  dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+  scales[m * nb + b] = (uint8_t)sbyte;
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t *p) {
+  u32x4 v;
+  __builtin_memcpy(&v, p, 16);
+  return v;
+}
+
+// One workgroup: 64 tokens x 256 weight rows; wave w owns rows 64w .. 64w+63
+// (four 16-row tiles) against all 64 tokens (four 16-token tiles), sixteen
+// scaled matrix-core steps per 128-k step.
+//
+// Loads.  Per step a row contributes four blocks, a 68-byte span starting at
+// a multiple of 4; the wave fetches each of its rows' spans as the five
+// aligned 16-byte chunks that cover it (320 chunks, five per lane, adjacent
+// lanes on adjacent chunks), and each thread fetches its share of the
+// tokens' FP8 codes and scales.  Everything is loaded PD steps ahead into a
+// ring of PD + 1 register slots and written to LDS one step ahead of use:
+// activations to a shared tile, weight chunks to a wave-private copy from
+// which each lane picks its 17-byte block at any byte offset.  Load
+// completion is counted in issue order, so both kinds of load keep one
+// distance.  Loads past the last step are clamped to it (a repeated read of
+// cached data), which keeps the loop body free of branches.
+template <int PD>
+__global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict__ W, int64_t row_bytes,
+                                                      const uint8_t *__restrict__ codes,
+                                                      const uint8_t *__restrict__ scales, float *__restrict__ C,
+                                                      int M, int N, int K, int n_tiles, int m_tiles) {
+  constexpr int NS = PD + 1;                    // ring slots
+  constexpr int U = NS % 2 == 0 ? NS : 2 * NS;  // unroll: whole ring turns and LDS buffer pairs
+  constexpr int kChunks = 5;                    // 16-byte chunks per row and step
+  __shared__ u32x4 a_lds[2][kBM * 8];  // token t, 16-byte chunk c at t * 8 + (c ^ (t & 7))
+  __shared__ uint32_t s_lds[2][kBM];   // token t: the four E8M0 bytes of the step
+  // Wave w, row r, chunk q at [w][5r + q]; one spare chunk past the end (a
+  // block read at the very end of a row window touches one dword beyond it).
+  __shared__ u32x4 b_lds[2][4 * 64 * kChunks + 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j = lane & 15, G = lane >> 4;
+  // Workgroups go to the eight XCDs in turn (id % 8).  Each XCD takes one
+  // contiguous run of tiles, token tiles fastest, so the token tiles that
+  // share a weight tile run on one XCD and read it through one L2.
+  const int64_t tiles = (int64_t)n_tiles * m_tiles, per = (tiles + 7) / 8;
+  const int64_t tile = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (tile >= tiles) return;  // the whole workgroup: no barrier is reached
+  const int64_t m0 = (tile % m_tiles) * kBM;
+  const int64_t n0 = (tile / m_tiles) * kBN + 64 * wave;
+  const int nb = K / 32, steps = K / kKS;
+  auto row_start = [&](int r) {  // byte offset of wave row r in W; rows past N read row N - 1
+    int64_t row = n0 + r;
+    if (row >= N) row = N - 1;
+    return row * row_bytes;
+  };
+
+  // This lane's chunks: chunk c = lane + 64 i is row c / 5, chunk c % 5.
+  int64_t cbase[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int c = lane + 64 * i;
+    cbase[i] = row_start(c / kChunks) + 16 * (c % kChunks);
+  }
+  // The rows this lane multiplies: 16 tn + j; their spans start at byte
+  // (rs + 68 st) mod 16 of the first chunk.
+  int rs16[4];
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) rs16[tn] = (int)(row_start(16 * tn + j) & 15);
+  // This thread's share of a step's activation tile: token at, chunks ac, ac + 1.
+  const int at = tid >> 2, ac = 2 * (tid & 3);
+  const uint8_t *asrc = codes + (m0 + at) * K + 16 * ac;
+  const uint8_t *ssrc = scales + (m0 + (tid & 63)) * nb;
+
+  u32x4 areg[NS][2];
+  uint32_t sreg[NS];
+  u32x4 breg[NS][kChunks];
+  auto load = [&](int st, int slot) {
+    st = st < steps ? st : steps - 1;
+    areg[slot][0] = *reinterpret_cast<const u32x4 *>(asrc + (int64_t)st * kKS);
+    areg[slot][1] = *reinterpret_cast<const u32x4 *>(asrc + (int64_t)st * kKS + 16);
+    sreg[slot] = *reinterpret_cast<const uint32_t *>(ssrc + 4 * st);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      // Aligned down to 16: the span starts at (row start + 68 st), a
+      // multiple of 4, so five chunks from there cover its 68 bytes.
+      const int64_t off = (cbase[i] + (int64_t)st * 68) & ~(int64_t)15;
+      breg[slot][i] = *reinterpret_cast<const u32x4 *>(W + off);
+    }
+  };
+  auto store = [&](int slot, int buf) {
+    a_lds[buf][at * 8 + (ac ^ (at & 7))] = areg[slot][0];
+    a_lds[buf][at * 8 + ((ac + 1) ^ (at & 7))] = areg[slot][1];
+    // Four threads load each token's scale word; all four store the same
+    // value, which keeps the step free of branches (a branch here lets the
+    // compiler sink the matrix-core chain past the later steps' barriers).
+    s_lds[buf][tid & (kBM - 1)] = sreg[slot];
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) b_lds[buf][wave * 64 * kChunks + lane + 64 * i] = breg[slot][i];
+  };
+
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int st, int buf) {
+    // This lane's weight block of each tile: E8M0 byte and 16 code bytes at
+    // byte x of the wave's copy, read as the five dwords from x & ~3.
+    uint32_t bq[4][4], be[4];
+    const uint32_t *wl = reinterpret_cast<const uint32_t *>(&b_lds[buf][wave * 64 * kChunks]);
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const int x = 80 * (16 * tn + j) + ((rs16[tn] + 4 * st) & 15) + 17 * G;
+      const uint32_t *d = wl + (x >> 2);
+      uint32_t w[5];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) w[i] = d[i];
+      const int sh = 8 * (x & 3);
+      be[tn] = (w[0] >> sh) & 0xFFu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bq[tn][i] = (uint32_t)((((uint64_t)w[i + 1] << 32) | w[i]) >> (sh + 8));
+    }
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+      const int t = 16 * tm + j;
+      const u32x4 lo = a_lds[buf][t * 8 + (G ^ (t & 7))];
+      const u32x4 hi = a_lds[buf][t * 8 + ((G + 4) ^ (t & 7))];
+      const v8i af = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const int sa = (int)((s_lds[buf][t] >> (8 * G)) & 0xFFu);
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) {
+        const v8i bf = v8i{(int)bq[tn][0], (int)bq[tn][1], (int)bq[tn][2], (int)bq[tn][3], 0, 0, 0, 0};
+        // Format codes: 0 = FP8 E4M3 (A), 4 = FP4 E2M1 (B); scales are E8M0.
+        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[tm][tn], 0, 4, 0, sa, 0,
+                                                                       (int)be[tn]);
+      }
+    }
+  };
+  // Step st: operands in LDS buffer st % 2.  The step issues the loads of
+  // step st + PD and, after its products, stages step st + 1 from slot
+  // (st + 1) % NS.
+  auto step = [&](int st, int u) {
+    load(st + PD, (u + PD) % NS);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st, u % 2);
+    __builtin_amdgcn_sched_barrier(0);
+    store((u + 1) % NS, (u + 1) % 2);
+    __syncthreads();
+  };
+
+#pragma unroll
+  for (int p = 0; p < PD; ++p) load(p, p);
+  store(0, 0);
+  __syncthreads();
+  int st0 = 0;
+  for (; st0 + U <= steps; st0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) step(st0 + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (st0 + u < steps) step(st0 + u, u);
+
+  // D[i][j] of a 16x16 tile sits in lane j + 16*(i/4), register i%4.
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const int64_t n = n0 + 16 * tn + j;
+      if (n >= N) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t m = m0 + 16 * tm + 4 * G + q;
+        if (m < M) C[m * N + n] = acc[tm][tn][q];
+      }
+    }
+}
+
+}  // namespace mx
+
+size_t gemm_mx_workspace_bytes(int64_t M, int64_t K) { return (size_t)mx::Layout(M, K).bytes(); }
+
+hipError_t launch_gemm_mx(const uint8_t *W, const void *A, int a_f16, float *C, int64_t M, int64_t N, int64_t K,
+                          void *ws, hipStream_t s) {
+  if (K % mx::kKS != 0) return launch_gemm(MXFP4, W, A, a_f16, C, M, N, K, s);
+  const mx::Layout L(M, K);
+  uint8_t *codes = static_cast<uint8_t *>(ws), *scales = codes + L.scales();
+  const int64_t blocks = L.Mp * (K / 32);
+  const dim3 qgrid((unsigned)((blocks + 255) / 256)), block(256);
+  if (a_f16)
+    hipLaunchKernelGGL(mx::quantize_kernel<_Float16>, qgrid, block, 0, s, (const _Float16 *)A, (int)M, L.Mp,
+                       (int)K, codes, scales);
+  else
+    hipLaunchKernelGGL(mx::quantize_kernel<float>, qgrid, block, 0, s, (const float *)A, (int)M, L.Mp, (int)K,
+                       codes, scales);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t row_bytes = (K / 32) * 17;
+  const int64_t n_tiles = (N + mx::kBN - 1) / mx::kBN, m_tiles = L.Mp / mx::kBM;
+  const dim3 grid((unsigned)(8 * ((n_tiles * m_tiles + 7) / 8)));
+  hipLaunchKernelGGL(mx::gemm_mx_kernel<mx::kPD>, grid, block, 0, s, W, row_bytes, codes, scales, C, (int)M, (int)N,
+                     (int)K, (int)n_tiles, (int)m_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace qmm

@@ -24,6 +24,13 @@ hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16
 hipError_t launch_gemm(int kind, const uint8_t *W, const void *A, int a_f16, float *C,
                        int64_t M, int64_t N, int64_t K, hipStream_t s);
 
+// MXFP4 weights on the scaled FP8 x FP4 matrix cores (activations quantized
+// to MX FP8 into `ws`, gemm_mx_workspace_bytes(M, K) bytes); K not a multiple
+// of 128 takes the f16 GEMM.
+size_t gemm_mx_workspace_bytes(int64_t M, int64_t K);
+hipError_t launch_gemm_mx(const uint8_t *W, const void *A, int a_f16, float *C, int64_t M, int64_t N, int64_t K,
+                          void *ws, hipStream_t s);
+
 // Routed expert products; see qmm_moe in qmm.h.  `ws` holds
 // moe_workspace_bytes(E, M, topk) bytes.
 size_t moe_workspace_bytes(int64_t E, int64_t M, int64_t topk);

@@ -110,6 +110,34 @@ int qmm_gemm_ex(int kind, const void *W, const void *A, int a_dtype, float *C,
 int qmm_matmul(int kind, const void *W, const void *A, int a_dtype, float *C,
                int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Prefill GEMM for MXFP4 weights on the scaled FP8 x FP4 matrix cores, a
+ * separately toleranced variant of qmm_gemm_ex for kind QMM_MXFP4 only (the
+ * block: an E8M0 scale byte and 32 E2M1 codes; codebook.rs, the MXFP4 row).
+ * The weight blocks go to the matrix cores as they are stored; W must be
+ * 16-byte aligned, and its rows are fetched as aligned 16-byte pieces, so the
+ * last piece may cover up to 12 bytes past the end of W (never past its
+ * 16-byte granule, hence never onto another page).  A (f32 or f16,
+ * [M][K]) is first quantized into `workspace` to MX FP8: per row and
+ * 32-element block, a power-of-two scale 2^e, the smallest with
+ * max|a| / 2^e <= 448, and each a / 2^e rounded to E4M3, nearest even.  That
+ * rounding (relative error at most 2^-4 per element, so
+ * |C - exact| <= 2^-4 . sum|w||a| plus f32 accumulation) is the only
+ * difference from the exact product; blocks whose elements are integers of
+ * magnitude <= 16 times one power of two come through exactly.
+ * K a multiple of 128 runs the scaled path; any other K runs qmm_gemm_ex's
+ * f16 GEMM.  workspace is device memory of at least
+ * qmm_gemm_mx_workspace_bytes(M, K) bytes at 16-byte alignment, overwritten by
+ * the call; calls that share it must not overlap.  Errors: kinds other than
+ * MXFP4 give QMM_ERR_UNSUPPORTED_KIND, a short workspace QMM_ERR_WORKSPACE,
+ * M > 65535 * 64 or more than 2^31 - 8 tiles of 64 x 256 QMM_ERR_BAD_ARG,
+ * the rest as qmm_gemm_ex. */
+int qmm_gemm_mx(int kind, const void *W, const void *A, int a_dtype, float *C,
+                int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                void *stream);
+/* Bytes of workspace qmm_gemm_mx needs: M rounded up to 64, times K * 33 / 32;
+ * 0 for M <= 0, K <= 0 or K not a multiple of 32. */
+size_t qmm_gemm_mx_workspace_bytes(int64_t M, int64_t K);
+
 /* Routed expert products, every expert in one grouped launch (plus a small
  * routing prologue when an expert may receive several pairs).  W holds E experts of N rows each, back to back: expert
  * e's row n starts at byte (e * N + n) * qmm_row_bytes(kind, K).

@@ -139,6 +139,29 @@ def test_moe_refusals_in_order(lib):
     assert "workspace" in qmm.qmm_last_error()
 
 
+def test_gemm_mx_refusals_in_order(lib):
+    g = lib.qmm_gemm_mx
+    need = lib.qmm_gemm_mx_workspace_bytes(10, 256)
+    # FP8 codes and E8M0 scales for M rounded up to 64 rows.
+    assert need == 64 * 256 + 64 * 8
+    assert lib.qmm_gemm_mx_workspace_bytes(65, 4096) == 128 * 4096 * 33 // 32
+    assert lib.qmm_gemm_mx_workspace_bytes(0, 256) == 0
+    assert lib.qmm_gemm_mx_workspace_bytes(10, 48) == 0
+    assert g(39, FAKE, FAKE, 1, FAKE, 0, 10, 256, FAKE, need, None) == EMPTY
+    assert g(5, FAKE, FAKE, 1, FAKE, 10, 10, 256, FAKE, need, None) == KIND
+    assert g(39, FAKE, FAKE, 1, FAKE, 10, 10, 48, FAKE, need, None) == KALIGN
+    assert g(2, FAKE, FAKE, 1, FAKE, 10, 10, 256, FAKE, need, None) == KIND   # Q4_0: MXFP4 only
+    assert "MXFP4" in qmm.qmm_last_error()
+    assert g(39, FAKE, FAKE, 3, FAKE, 10, 10, 256, FAKE, need, None) == DTYPE
+    assert g(39, None, FAKE, 1, FAKE, 10, 10, 256, FAKE, need, None) == ARG
+    assert g(39, FAKE + 4, FAKE, 1, FAKE, 10, 10, 256, FAKE, need, None) == ARG  # W not 16-byte aligned
+    assert g(39, FAKE, FAKE + 1, 1, FAKE, 10, 10, 256, FAKE, need, None) == ARG
+    assert g(39, FAKE, FAKE, 1, FAKE, 65535 * 64 + 1, 10, 256, FAKE, 1 << 40, None) == ARG
+    assert g(39, FAKE, FAKE, 1, FAKE, 10, 10, 256, None, need, None) == WS
+    assert g(39, FAKE, FAKE, 1, FAKE, 10, 10, 256, FAKE, need - 1, None) == WS
+    assert g(39, FAKE, FAKE, 1, FAKE, 10, 10, 256, FAKE + 8, need, None) == WS
+
+
 def test_dequant_refusals(lib):
     assert lib.qmm_dequant(2, FAKE, FAKE, 0, None) == EMPTY
     assert lib.qmm_dequant(4, FAKE, FAKE, 32, None) == KIND

@@ -233,6 +233,57 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
       }
     }
   };
+  // The same step when every row starts on a 16-byte boundary (row_bytes a
+  // multiple of 16, i.e. K a multiple of 512) and st0 is a multiple of 4:
+  // a row's span then starts at byte 4 (st % 4) of its first chunk for every
+  // row, so all addresses are a lane constant plus an immediate offset, and
+  // a lane's 16 code bytes sit at byte (G + 1) % 4 of five dwords, two by two
+  // joined with v_alignbyte.
+  const int bq_dw = 20 * j + 4 * G + ((G + 1) >> 2);  // dword of the codes, tile 0, step % 4 = 0
+  const int be_b = 80 * j + 17 * G;                     // byte of the E8M0 scale
+  const int bsh = (G + 1) & 3;
+  auto compute_fast = [&](int u, int buf) {
+    uint32_t bq[4][4], be[4];
+    const uint32_t *wl = reinterpret_cast<const uint32_t *>(&b_lds[buf][wave * 64 * kChunks]);
+    const uint8_t *bl = reinterpret_cast<const uint8_t *>(wl);
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const uint32_t *d = wl + bq_dw + 320 * tn + u;
+      uint32_t w[5];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) w[i] = d[i];
+      be[tn] = bl[be_b + 1280 * tn + 4 * u];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bq[tn][i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], bsh);
+    }
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+      const int t = 16 * tm + j;
+      const u32x4 lo = a_lds[buf][t * 8 + (G ^ (t & 7))];
+      const u32x4 hi = a_lds[buf][t * 8 + ((G + 4) ^ (t & 7))];
+      const v8i af = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const int sa = (int)((s_lds[buf][t] >> (8 * G)) & 0xFFu);
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) {
+        const v8i bf = v8i{(int)bq[tn][0], (int)bq[tn][1], (int)bq[tn][2], (int)bq[tn][3], 0, 0, 0, 0};
+        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[tm][tn], 0, 4, 0, sa, 0,
+                                                                       (int)be[tn]);
+      }
+    }
+  };
+  // Loads of step st0 + PD + u for that case: pointers advance once per
+  // group of U steps; within the group every offset is an immediate.
+  auto load_fast = [&](int st0, int u, int slot) {
+    const int64_t sp = st0 + PD;  // st0 % 4 == 0, so 68 * st0 is a multiple of 16
+    const uint8_t *ag = asrc + sp * kKS + u * kKS;
+    areg[slot][0] = *reinterpret_cast<const u32x4 *>(ag);
+    areg[slot][1] = *reinterpret_cast<const u32x4 *>(ag + 16);
+    sreg[slot] = *reinterpret_cast<const uint32_t *>(ssrc + 4 * sp + 4 * u);
+    const int delta = 16 * ((68 * (PD + u)) >> 4);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+      breg[slot][i] = *reinterpret_cast<const u32x4 *>(W + cbase[i] + (int64_t)st0 * 68 + delta);
+  };
   // Step st: operands in LDS buffer st % 2.  The step issues the loads of
   // step st + PD and, after its products, stages step st + 1 from slot
   // (st + 1) % NS.
@@ -250,6 +301,21 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
   store(0, 0);
   __syncthreads();
   int st0 = 0;
+  if ((row_bytes & 15) == 0) {
+    static_assert(U % 4 == 0, "the aligned path walks groups of four steps");
+    // Every load of these groups lies before the last step: no clamping.
+    for (; st0 + U + PD <= steps; st0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        load_fast(st0, u, (u + PD) % NS);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_fast(u, u % 2);
+        __builtin_amdgcn_sched_barrier(0);
+        store((u + 1) % NS, (u + 1) % 2);
+        __syncthreads();
+      }
+    }
+  }
   for (; st0 + U <= steps; st0 += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) step(st0 + u, u);

@@ -43,14 +43,17 @@ def run(W, X, N, ws=None):
     return host(C)
 
 
+@pytest.mark.parametrize("K", [1280, 2048])
 @pytest.mark.parametrize("scales", ["config", "stress"])
 @pytest.mark.parametrize("xdt", ["f16", "f32"])
-def test_gemm_mx_unit_vectors_return_the_weights(oracle_mod, xdt, scales):
+def test_gemm_mx_unit_vectors_return_the_weights(oracle_mod, xdt, scales, K):
     """A one-hot row quantizes exactly (scale 2^-8, code 256), so each output
-    is one weight times one, exactly.  K = 1280 is ten 128-k steps: one full
-    turn of the unrolled loop and a ragged tail; N = 300 leaves a partial
-    256-row tile."""
-    N, K = 300, 1280
+    is one weight times one, exactly.  K = 1280 is ten 128-k steps with rows
+    of 680 bytes (the general path: two full turns of the unrolled loop and a
+    ragged tail); K = 2048 has rows of 1088 bytes, a multiple of 16, and takes
+    the aligned path for its first groups.  N = 300 leaves a partial 256-row
+    tile."""
+    N = 300
     W = wl.random_weights(KIND, N, K, wl.rng("gpu_mx_unit", f"{xdt}_{scales}"), scales=scales)
     want = oracle_mod.dequant(KIND, W).reshape(N, K).astype(np.float32)
     ks = [0, 1, 16, 17, 31, 127, 128, K // 3, K - 2, K - 1]
@@ -63,11 +66,13 @@ def test_gemm_mx_unit_vectors_return_the_weights(oracle_mod, xdt, scales):
 
 
 @pytest.mark.parametrize("xdt", ["f16", "f32"])
-@pytest.mark.parametrize("K", [512, 1280])
+@pytest.mark.parametrize("K", [512, 1280, 2048, 2560])
 def test_gemm_mx_exact_activations(oracle_mod, K, xdt):
     """Integers in [-16, 16] pass the MX FP8 quantization unchanged, so the
     result is the exact product up to f32 accumulation.  M spans one, two and
-    three 64-token tiles (ragged), N two 256-row tiles (ragged)."""
+    three 64-token tiles (ragged), N two 256-row tiles (ragged).  K = 512 and
+    1280 take the general path only; 2048 and 2560 (rows a multiple of 16
+    bytes) run aligned groups, then the general path for the last steps."""
     N = 300
     g = wl.rng("gpu_mx_exact", f"{K}_{xdt}")
     W = wl.random_weights(KIND, N, K, g)

@@ -149,6 +149,67 @@ class Oracle:
         return Y, B
 
 
+    def moe_ffn(self, kind, W_gu, W_d, E: int, N_ff: int, K: int, ids, topk_w, X, rows=None,
+                threads: int = 0):
+        """Routed SiLU-gated expert FFN with a weighted top-k combine, in
+        binary64.  Model semantics, not on the pages (which stop at the
+        routed expert products): for token t and slot s with e = ids[t][s]
+        in [0, E),
+
+            g = W_gu[e][0 : N_ff] . X[t]        (gate: the first N_ff rows)
+            u = W_gu[e][N_ff : 2 N_ff] . X[t]   (up: the next N_ff rows)
+            h = silu(g) * u
+            y[t] += topk_w[t][s] * (W_d[e] . h)
+
+        W_gu holds E experts of 2 N_ff rows of K elements, W_d E experts of K
+        rows of N_ff elements.  A pair whose id lies outside [0, E) adds
+        nothing.  ``rows`` selects output columns of y.
+
+        Returns (y, tol), each [M][n_sel].  tol bounds |y_gpu - y| for an
+        implementation whose every matmul stays within 1e-3 sum|w||x| + 1e-6
+        of its exact value (the workload bar), whose SiLU-product is
+        evaluated in f32 to within 2^-20 relative, and whose combine sums the
+        top-k terms in f32:
+            a_g = 1e-3 Bg + 1e-6, a_u likewise            (gate, up errors)
+            a_h = (|silu g| + 1.1 a_g) a_u + 1.1 a_g |u|  (|silu'| < 1.1)
+                  + 2^-20 (|h| + that)
+            a_d = (1 + 1e-3) sum|W_d| a_h + 1e-3 sum|W_d||h| + 1e-6
+            tol = sum_s |w_s| a_d + topk 2^-23 sum_s |w_s| (|d_s| + a_d)
+        """
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        M, topk = ids.shape
+        valid = (ids >= 0) & (ids < E)
+        safe = np.where(valid, ids, 0).astype(np.int32)
+        G, BG = self.moe(kind, W_gu, E, 2 * N_ff, K, safe, X, False, threads=threads)
+        g, u = G[..., :N_ff], G[..., N_ff:]
+        a_g = 1e-3 * BG[..., :N_ff] + 1e-6
+        a_u = 1e-3 * BG[..., N_ff:] + 1e-6
+        sg = silu(g)
+        h = sg * u
+        a_h0 = (np.abs(sg) + 1.1 * a_g) * a_u + 1.1 * a_g * np.abs(u)
+        a_h = a_h0 + 2.0 ** -20 * (np.abs(h) + a_h0)
+        D, BD = self.moe(kind, W_d, E, K, N_ff, safe, h, True, rows=rows, threads=threads)
+        _, BA = self.moe(kind, W_d, E, K, N_ff, safe, a_h, True, rows=rows, threads=threads)
+        a_d = (1.0 + 1e-3) * BA + 1e-3 * BD + 1e-6
+        w = np.where(valid, np.asarray(topk_w, dtype=np.float64), 0.0)[..., None]
+        y = np.sum(w * D, axis=1)
+        tol = np.sum(np.abs(w) * a_d, axis=1) + topk * 2.0 ** -23 * np.sum(np.abs(w) * (np.abs(D) + a_d), axis=1)
+        return y, tol
+
+
+def silu(v):
+    """SiLU (the sigmoid-weighted linear unit) in binary64:
+    silu(v) = v / (1 + exp(-v)), evaluated as v e^v / (1 + e^v) for v < 0 so
+    that neither branch overflows."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    pos = v >= 0
+    out[pos] = v[pos] / (1.0 + np.exp(-v[pos]))
+    e = np.exp(v[~pos])
+    out[~pos] = v[~pos] * e / (1.0 + e)
+    return out
+
+
 _default = None
 
 
@@ -178,3 +239,7 @@ def matmul(kind, W, K, X, rows=None, threads=0):
 
 def moe(kind, W, E, N, K, ids, X, x_per_slot, rows=None, threads=0):
     return default().moe(kind, W, E, N, K, ids, X, x_per_slot, rows=rows, threads=threads)
+
+
+def moe_ffn(kind, W_gu, W_d, E, N_ff, K, ids, topk_w, X, rows=None, threads=0):
+    return default().moe_ffn(kind, W_gu, W_d, E, N_ff, K, ids, topk_w, X, rows=rows, threads=threads)

@@ -22,7 +22,8 @@ Also printed in the same JSON line:
                 on full steps of the same workload;
   cases         each of the four GEMVs alone;
   secondary     the other workloads (Q4_0 GEMV, prefill GEMMs, codebook
-                kinds, routed experts), each timed the same way.
+                kinds, routed experts, the scaled MXFP4 GEMM, the routed
+                expert FFN), each timed the same way.
 """
 from __future__ import annotations
 
@@ -164,6 +165,29 @@ def secondary_cases(torch, qmm, wl):
             cases.append(Case(f"{e.name}_{mat}", e.kind, launch, copies, distinct * N * row_b,
                               2 * e.M * e.topk * N * K))
         del touched
+    # The whole routed expert FFN (gate/up, SiLU-product, down, weighted
+    # combine) on the same experts and routing; bytes are the touched
+    # experts' gate/up and down weights, each read once.
+    for e in wl.C5:
+        ids_np = e.ids()
+        ids = torch.from_numpy(ids_np).cuda()
+        gu = make_copies(torch, e.w_gu())
+        dn = make_copies(torch, e.w_d())
+        n = min(len(gu), len(dn))
+        g = wl.rng(e.name, "ffn")
+        w = g.uniform(0.05, 1.0, size=(e.M, e.topk))
+        w = torch.from_numpy((w / w.sum(axis=1, keepdims=True)).astype(np.float32)).cuda()
+        Xd = torch.from_numpy(e.x()).cuda()
+        N_ff = e.N_gu // 2
+        Y = torch.empty((e.M, e.K_gu), dtype=torch.float32, device="cuda")
+        ws = torch.empty(qmm.qmm_moe_ffn_workspace_bytes(e.E, e.M, e.topk, N_ff, e.K_gu), dtype=torch.uint8,
+                         device="cuda")
+
+        def launch(i, e=e, ids=ids, w=w, Xd=Xd, Y=Y, ws=ws, gu=gu, dn=dn, n=n, N_ff=N_ff):
+            qmm.qmm_moe_ffn(e.kind, gu[i % n], dn[i % n], e.E, ids, w, e.topk, Xd, Y, e.M, N_ff, e.K_gu, ws)
+
+        cases.append(Case(f"{e.name}_ffn", e.kind, launch, gu + dn, e.touched_bytes(ids_np),
+                          2 * e.M * e.topk * (e.N_gu * e.K_gu + e.N_d * e.K_d)))
     return cases
 
 

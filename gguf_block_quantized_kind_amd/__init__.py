@@ -55,6 +55,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         "qmm_moe": (I, [I, P, I64, P, I64, P, I, I, P, I64, I64, I64, P, SZ, P]),
         "qmm_moe_workspace_bytes": (SZ, [I64, I64, I64]),
         "qmm_gemm_mx": (I, [I, P, P, I, P, I64, I64, I64, P, SZ, P]),
+        "qmm_moe_ffn": (I, [I, P, P, I64, P, P, I64, P, I, P, I64, I64, I64, P, SZ, P]),
+        "qmm_moe_ffn_workspace_bytes": (SZ, [I64, I64, I64, I64, I64]),
         "qmm_gemm_mx_workspace_bytes": (SZ, [I64, I64]),
         "qmm_dequant": (I, [I, P, P, I64, P]),
         "qmm_row_bytes": (I64, [I, I64]),
@@ -110,6 +112,10 @@ def qmm_last_error() -> str:
 
 def qmm_moe_workspace_bytes(E: int, M: int, topk: int) -> int:
     return int(load_library().qmm_moe_workspace_bytes(int(E), int(M), int(topk)))
+
+
+def qmm_moe_ffn_workspace_bytes(E: int, M: int, topk: int, N_ff: int, K: int) -> int:
+    return int(load_library().qmm_moe_ffn_workspace_bytes(int(E), int(M), int(topk), int(N_ff), int(K)))
 
 
 def qmm_gemm_mx_workspace_bytes(M: int, K: int) -> int:
@@ -212,6 +218,20 @@ def qmm_gemm_mx(kind, W, A, C, M: int, N: int, K: int, workspace, stream=None):
                                       M, N, K, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def qmm_moe_ffn(kind, W_gu, W_d, E: int, ids, topk_w, topk: int, X, Y, M: int, N_ff: int, K: int,
+                workspace, stream=None):
+    _check_weights(kind, W_gu, E * 2 * N_ff, K)
+    _check_weights(kind, W_d, E * K, N_ff)
+    _need(ids, M * topk, "ids")
+    _need(topk_w, M * topk, "topk_w")
+    _need(X, M * K, "X")
+    _need(Y, M * K, "Y")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().qmm_moe_ffn(kind_id(kind), _ptr(W_gu), _ptr(W_d), E, _ptr(ids), _ptr(topk_w), topk,
+                                      _ptr(X), _dtype_code(X), _ptr(Y), M, N_ff, K, _ptr(workspace), ws_bytes,
+                                      _stream(stream)))
+
+
 def qmm_moe(kind, W, E: int, ids, topk: int, X, x_per_slot: int, Y, M: int, N: int, K: int,
             workspace, stream=None):
     _check_weights(kind, W, E * N, K)
@@ -290,6 +310,20 @@ def moe(kind, W, E: int, ids, X, N: int, K: int, x_per_slot: bool, stream=None, 
         nbytes = qmm_moe_workspace_bytes(E, M, topk)
         workspace = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=X.device)
     qmm_moe(kind, W, E, ids, topk, X, 1 if x_per_slot else 0, Y, M, N, K, workspace, stream)
+    return Y
+
+
+def moe_ffn(kind, W_gu, W_d, E: int, ids, topk_w, X, N_ff: int, stream=None, workspace=None):
+    """Y [M, K] = sum over slots of topk_w * down(silu(gate) * up) for ids [M, topk] int32,
+    topk_w [M, topk] f32 and X [M, K]."""
+    import torch
+    M, topk = ids.shape
+    K = X.shape[1]
+    Y = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    if workspace is None:
+        nbytes = qmm_moe_ffn_workspace_bytes(E, M, topk, N_ff, K)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
+    qmm_moe_ffn(kind, W_gu, W_d, E, ids, topk_w, topk, X, Y, M, N_ff, K, workspace, stream)
     return Y
 
 

@@ -136,6 +136,41 @@ QMM_EXPORT int qmm_matmul(int kind, const void *W, const void *A, int a_dtype, f
   return qmm_gemm_ex(kind, W, A, a_dtype, C, M, N, K, stream);
 }
 
+QMM_EXPORT size_t qmm_moe_ffn_workspace_bytes(int64_t E, int64_t M, int64_t topk, int64_t N_ff, int64_t K) {
+  if (E <= 0 || M <= 0 || topk <= 0 || N_ff <= 0 || K <= 0) return 0;
+  return qmm::moe_ffn_workspace_bytes(E, M, topk, N_ff, K);
+}
+
+QMM_EXPORT int qmm_moe_ffn(int kind, const void *W_gu, const void *W_d, int64_t E, const int32_t *ids,
+                           const float *topk_w, int64_t topk, const void *X, int x_dtype, float *Y, int64_t M,
+                           int64_t N_ff, int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+  const KindInfo *k;
+  if (E <= 0 || topk <= 0 || N_ff <= 0)
+    return fail(QMM_ERR_EMPTY_SHAPE, "empty shape: E=%lld topk=%lld N_ff=%lld", (long long)E, (long long)topk,
+                (long long)N_ff);
+  int st = check_shape(kind, M, 2 * N_ff, K, &k);  // gate/up: 2 N_ff rows of K
+  if (st) return st;
+  if ((st = check_shape(kind, M, K, N_ff, &k))) return st;  // down: K rows of N_ff
+  if ((st = check_dtype(x_dtype))) return st;
+  if (!W_gu || !W_d || !ids || !topk_w || !Y) return fail(QMM_ERR_BAD_ARG, "W_gu, W_d, ids, topk_w or Y is NULL");
+  if ((st = check_act(X, x_dtype, "X"))) return st;
+  if (!aligned(ids, 4) || !aligned(topk_w, 4)) return fail(QMM_ERR_BAD_ARG, "ids or topk_w is not 4-byte aligned");
+  if (!aligned(Y, 16)) return fail(QMM_ERR_BAD_ARG, "Y is not 16-byte aligned");
+  if (E > qmm::kMoeMaxExperts) return fail(QMM_ERR_BAD_ARG, "E=%lld exceeds %lld experts", (long long)E, (long long)qmm::kMoeMaxExperts);
+  const int64_t P = M * topk;
+  if (P > ((int64_t)1 << 31) - 1 || P * (N_ff > K ? 2 * N_ff : K) > ((int64_t)1 << 38) ||
+      2 * N_ff > ((int64_t)1 << 31) / 4 || K > ((int64_t)1 << 31) / 4)
+    return fail(QMM_ERR_BAD_ARG, "M*topk=%lld with N_ff=%lld, K=%lld exceeds the supported range", (long long)P,
+                (long long)N_ff, (long long)K);
+  const size_t need = qmm::moe_ffn_workspace_bytes(E, M, topk, N_ff, K);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(QMM_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  return hip_status(qmm::launch_moe_ffn(kind, (const uint8_t *)W_gu, (const uint8_t *)W_d, E, ids, topk_w, topk, X,
+                                        x_dtype == QMM_F16, Y, M, N_ff, K, workspace, (hipStream_t)stream),
+                    "moe_ffn launch");
+}
+
 QMM_EXPORT size_t qmm_gemm_mx_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
   return qmm::gemm_mx_workspace_bytes(M, K);

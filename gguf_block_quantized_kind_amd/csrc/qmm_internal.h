@@ -24,6 +24,13 @@ hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16
 hipError_t launch_gemm(int kind, const uint8_t *W, const void *A, int a_f16, float *C,
                        int64_t M, int64_t N, int64_t K, hipStream_t s);
 
+// Routed SiLU-gated expert FFN with a weighted top-k combine; see
+// qmm_moe_ffn in qmm.h.
+size_t moe_ffn_workspace_bytes(int64_t E, int64_t M, int64_t topk, int64_t N_ff, int64_t K);
+hipError_t launch_moe_ffn(int kind, const uint8_t *W_gu, const uint8_t *W_d, int64_t E, const int32_t *ids,
+                          const float *topk_w, int64_t topk, const void *X, int x_f16, float *Y, int64_t M,
+                          int64_t N_ff, int64_t K, void *ws, hipStream_t s);
+
 // MXFP4 weights on the scaled FP8 x FP4 matrix cores (activations quantized
 // to MX FP8 into `ws`, gemm_mx_workspace_bytes(M, K) bytes); K not a multiple
 // of 128 takes the f16 GEMM.

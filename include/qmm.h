@@ -25,7 +25,11 @@
  * rounds each decoded weight once to f16 and, for f32 activations, splits
  * each activation into two f16 parts so that the activation stays exact to
  * about 2^-22.  Results satisfy |y - y_exact| <= 1e-3 * sum_k |w||x| + 1e-6
- * per element.
+ * per element.  Activations are taken in f16 on the matrix-core paths (the
+ * GEMV at M <= 8 for every kind but Q2_K, Q3_K and Q5_K, qmm_moe, the GEMM),
+ * so an f32 activation must lie within the f16 range, |x| <= 65504; a larger
+ * one overflows to infinity there.  qmm_moe_ffn scales its intermediate
+ * activations into that range itself.
  *
  * Ownership and asynchrony.  The caller owns every buffer; the library never
  * allocates device memory.  W, x and ids are read only.  Calls that take a
@@ -109,6 +113,32 @@ int qmm_gemm_ex(int kind, const void *W, const void *A, int a_dtype, float *C,
 /* Either path: the GEMV for M <= QMM_GEMV_MAX_M, the GEMM above. */
 int qmm_matmul(int kind, const void *W, const void *A, int a_dtype, float *C,
                int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Routed SiLU-gated expert FFN with a weighted top-k combine (model
+ * semantics beyond the pages, which stop at the routed expert products of
+ * qmm_moe).  W_gu holds E experts of 2 * N_ff rows of K elements (rows
+ * [0, N_ff) are the gate, [N_ff, 2 N_ff) the up projection); W_d holds E
+ * experts of K rows of N_ff elements; both in the layout of qmm_moe.  For
+ * token t and slot s with e = ids[t][s] in [0, E):
+ *   h = silu(W_gate[e] . X[t]) * (W_up[e] . X[t]),  silu(v) = v / (1 + e^-v)
+ *   Y[t] = sum over such slots, in slot order, of topk_w[t][s] * (W_d[e] . h)
+ * X is [M][K] f32 or f16; topk_w is [M][topk] f32; Y is [M][K] f32, 16-byte
+ * aligned, overwritten.  Slots whose id lies outside [0, E) add nothing.
+ * The products run as qmm_moe (each within 1e-3 sum|w||x| + 1e-6), h and
+ * the combine in f32; each pair's h is divided by a power of two that
+ * brings max|h| to 2^14 or below before the down product (whose matrix-core
+ * path takes f16 activations), and the combine multiplies it back, exactly.  workspace: qmm_moe_ffn_workspace_bytes(E, M, topk,
+ * N_ff, K) bytes, 256-byte aligned, overwritten; calls sharing it must not
+ * overlap.  Errors as qmm_moe, with both matrices' shapes checked (gate/up
+ * first) and a NULL topk_w or misaligned Y as QMM_ERR_BAD_ARG. */
+int qmm_moe_ffn(int kind, const void *W_gu, const void *W_d, int64_t E, const int32_t *ids,
+                const float *topk_w, int64_t topk, const void *X, int x_dtype, float *Y,
+                int64_t M, int64_t N_ff, int64_t K, void *workspace, size_t workspace_bytes,
+                void *stream);
+/* Workspace of qmm_moe_ffn: the routing words of qmm_moe plus f32 gate/up,
+ * h, per-slot down outputs and per-pair scales; 0 for a non-positive
+ * argument. */
+size_t qmm_moe_ffn_workspace_bytes(int64_t E, int64_t M, int64_t topk, int64_t N_ff, int64_t K);
 
 /* Prefill GEMM for MXFP4 weights on the scaled FP8 x FP4 matrix cores, a
  * separately toleranced variant of qmm_gemm_ex for kind QMM_MXFP4 only (the

@@ -162,6 +162,38 @@ def test_gemm_mx_refusals_in_order(lib):
     assert g(39, FAKE, FAKE, 1, FAKE, 10, 10, 256, FAKE + 8, need, None) == WS
 
 
+def test_moe_ffn_refusals_in_order(lib):
+    g = lib.qmm_moe_ffn
+    need = lib.qmm_moe_ffn_workspace_bytes(8, 4, 2, 256, 512)
+    route = lib.qmm_moe_workspace_bytes(8, 4, 2)
+    up = lambda b: (b + 255) // 256 * 256
+    # routing words, f32 gate/up [P][2 N_ff], h [P][N_ff], down [P][K], per-pair scales [P]
+    assert need == up(route) + up(8 * 512 * 4) + up(8 * 256 * 4) + up(8 * 512 * 4) + up(8 * 4)
+    assert lib.qmm_moe_ffn_workspace_bytes(0, 4, 2, 256, 512) == 0
+    a = dict(kind=12, Wgu=FAKE, Wd=FAKE, E=8, ids=FAKE, w=FAKE, topk=2, X=FAKE, dt=1, Y=FAKE, M=4, Nff=256,
+             K=512, ws=FAKE, wsb=need, s=None)
+
+    def call(**kw):
+        b = dict(a, **kw)
+        return g(b["kind"], b["Wgu"], b["Wd"], b["E"], b["ids"], b["w"], b["topk"], b["X"], b["dt"], b["Y"],
+                 b["M"], b["Nff"], b["K"], b["ws"], b["wsb"], b["s"])
+
+    assert call(E=0) == EMPTY
+    assert call(Nff=0) == EMPTY
+    assert call(M=0) == EMPTY
+    assert call(kind=1) == KIND
+    assert call(K=512 + 32) == KALIGN      # gate/up row length
+    assert call(Nff=256 + 32) == KALIGN    # down row length
+    assert call(dt=4) == DTYPE
+    assert call(w=None) == ARG
+    assert call(Wd=None) == ARG
+    assert call(Y=FAKE + 4) == ARG         # Y must be 16-byte aligned
+    assert call(E=5000) == ARG
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(ws=FAKE + 16) == WS        # 256-byte aligned
+
+
 def test_dequant_refusals(lib):
     assert lib.qmm_dequant(2, FAKE, FAKE, 0, None) == EMPTY
     assert lib.qmm_dequant(4, FAKE, FAKE, 32, None) == KIND

@@ -1,0 +1,102 @@
+"""GPU parity of the routed expert FFN (qmm_moe_ffn) against the oracle's
+binary64 composition, within the tolerance the oracle derives from the
+per-matmul bar (1e-3 sum|w||x| + 1e-6 for each routed product, an f32
+SiLU-product and an f32 combine).
+
+Cases span the routed paths: 256-element kinds with N_ff and K whole
+256-element k-blocks (matrix-core expert kernel, one-pair and grouped work
+items by the pairs-per-expert rule), 32-element kinds with K not a multiple
+of 256 (the f32 expert kernel), skipped slots (ids -1 and E), and the
+128-expert, top-8 workload at full size on sampled output columns.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import gguf_block_quantized_kind_amd as qmm  # noqa: E402
+
+from test_gpu_parity import SENTINEL, dev, host  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qmm.load_library()
+
+
+def _weights(g, M, topk):
+    w = g.uniform(0.05, 1.0, size=(M, topk))
+    return (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def run_ffn(kind, W_gu, W_d, E, ids, w, X, N_ff):
+    M, K = X.shape
+    Y = torch.full((M, K), SENTINEL, dtype=torch.float32, device="cuda")
+    ws = torch.empty(qmm.qmm_moe_ffn_workspace_bytes(E, M, ids.shape[1], N_ff, K), dtype=torch.uint8,
+                     device="cuda")
+    qmm.qmm_moe_ffn(kind, dev(W_gu), dev(W_d), E, dev(ids), dev(w), ids.shape[1], dev(X), Y, M, N_ff, K, ws)
+    return host(Y)
+
+
+def check(got, y, tol, what):
+    assert not np.any(got == SENTINEL), f"{what}: outputs left untouched"
+    err = np.abs(got.astype(np.float64) - y)
+    ratio = err / tol
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, f"{what}: worst |err|/tol = {ratio.max():.3g} at {worst}: got {got[worst]} want {y[worst]}"
+    return float(ratio.max())
+
+
+@pytest.mark.parametrize("kind,N_ff,K", [("Q4_K", 256, 512), ("Q6_K", 512, 256), ("Q8_0", 96, 160),
+                                         ("MXFP4", 256, 512), ("IQ4_XS", 256, 256)])
+def test_ffn_parity(oracle_mod, kind, N_ff, K):
+    E, topk = 6, 3
+    g = wl.rng("gpu_ffn", f"{kind}_{N_ff}_{K}")
+    W_gu = wl.random_weights(kind, E * 2 * N_ff, K, g)
+    W_d = wl.random_weights(kind, E * K, N_ff, g)
+    for M in (1, 5, 40):
+        ids = wl.routing(M, E, topk, g)
+        if M > 1:
+            ids[1, 0] = -1      # skipped slots
+            ids[M - 1, 2] = E
+        w = _weights(g, M, topk)
+        X = wl.activations((M, K), np.float16, g)
+        got = run_ffn(kind, W_gu, W_d, E, ids, w, X, N_ff)
+        y, tol = oracle_mod.moe_ffn(kind, W_gu, W_d, E, N_ff, K, ids, w, X)
+        check(got, y, tol, f"{kind} M={M}")
+
+
+def test_ffn_f32_activations(oracle_mod):
+    kind, E, topk, N_ff, K, M = "Q4_K", 4, 2, 256, 256, 7
+    g = wl.rng("gpu_ffn_f32", kind)
+    W_gu = wl.random_weights(kind, E * 2 * N_ff, K, g)
+    W_d = wl.random_weights(kind, E * K, N_ff, g)
+    ids = wl.routing(M, E, topk, g)
+    w = _weights(g, M, topk)
+    X = wl.activations((M, K), np.float32, g)
+    got = run_ffn(kind, W_gu, W_d, E, ids, w, X, N_ff)
+    y, tol = oracle_mod.moe_ffn(kind, W_gu, W_d, E, N_ff, K, ids, w, X)
+    check(got, y, tol, "f32 X")
+
+
+def test_ffn_full_size_sampled(oracle_mod):
+    """128 experts, top 8, gate/up [1536, 2048] and down [2048, 768] Q4_K,
+    16 tokens; the oracle computes 64 sampled output columns."""
+    e = next(x for x in wl.C5 if x.M == 16)
+    N_ff, K = e.N_gu // 2, e.K_gu
+    ids = e.ids()
+    W_gu, W_d = e.w_gu(), e.w_d()
+    g = wl.rng(e.name, "ffn")
+    w = _weights(g, e.M, e.topk)
+    X = e.x()
+    got = run_ffn(e.kind, W_gu, W_d, e.E, ids, w, X, N_ff)
+    cols = np.unique(np.concatenate([[0, K - 1], g.choice(K, size=62, replace=False)]))
+    y, tol = oracle_mod.moe_ffn(e.kind, W_gu, W_d, e.E, N_ff, K, ids, w, X, rows=cols)
+    assert not np.any(got == SENTINEL)
+    ratio = check(got[:, cols], y, tol, e.name)
+    print(f"worst error / tolerance: {ratio:.3g}")

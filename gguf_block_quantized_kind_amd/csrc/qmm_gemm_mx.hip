@@ -98,12 +98,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(const AT *__restrict__ A,
   scales[m * nb + b] = (uint8_t)sbyte;
 }
 
-__device__ __forceinline__ u32x4 ld16(const uint8_t *p) {
-  u32x4 v;
-  __builtin_memcpy(&v, p, 16);
-  return v;
-}
-
 // One workgroup: 64 tokens x 256 weight rows; wave w owns rows 64w .. 64w+63
 // (four 16-row tiles) against all 64 tokens (four 16-token tiles), sixteen
 // scaled matrix-core steps per 128-k step.

@@ -46,7 +46,8 @@ def run_ffn(kind, W_gu, W_d, E, ids, w, X, N_ff):
 def check(got, y, tol, what):
     assert not np.any(got == SENTINEL), f"{what}: outputs left untouched"
     err = np.abs(got.astype(np.float64) - y)
-    ratio = err / tol
+    # A row with no valid slot is exactly zero, with tolerance zero.
+    ratio = np.divide(err, tol, out=np.where(err == 0, 0.0, np.inf), where=tol > 0)
     worst = np.unravel_index(np.argmax(ratio), ratio.shape)
     assert ratio.max() <= 1.0, f"{what}: worst |err|/tol = {ratio.max():.3g} at {worst}: got {got[worst]} want {y[worst]}"
     return float(ratio.max())
@@ -100,3 +101,26 @@ def test_ffn_full_size_sampled(oracle_mod):
     assert not np.any(got == SENTINEL)
     ratio = check(got[:, cols], y, tol, e.name)
     print(f"worst error / tolerance: {ratio:.3g}")
+
+
+def test_ffn_all_slots_skipped_and_determinism(oracle_mod):
+    """A token whose every slot is skipped gets a zero row; repeated calls on
+    one workspace agree bit for bit (the combine sums slots in order)."""
+    kind, E, topk, N_ff, K, M = "Q4_K", 5, 3, 256, 512, 6
+    g = wl.rng("gpu_ffn_skip", kind)
+    W_gu = wl.random_weights(kind, E * 2 * N_ff, K, g)
+    W_d = wl.random_weights(kind, E * K, N_ff, g)
+    ids = wl.routing(M, E, topk, g)
+    ids[2, :] = [-1, E, -7]
+    w = _weights(g, M, topk)
+    X = wl.activations((M, K), np.float16, g)
+    ws = torch.empty(qmm.qmm_moe_ffn_workspace_bytes(E, M, topk, N_ff, K), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        Y = torch.full((M, K), SENTINEL, dtype=torch.float32, device="cuda")
+        qmm.qmm_moe_ffn(kind, dev(W_gu), dev(W_d), E, dev(ids), dev(w), topk, dev(X), Y, M, N_ff, K, ws)
+        outs.append(host(Y))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.all(outs[0][2] == 0.0)
+    y, tol = oracle_mod.moe_ffn(kind, W_gu, W_d, E, N_ff, K, ids, w, X)
+    check(outs[0], y, tol, "skipped row")

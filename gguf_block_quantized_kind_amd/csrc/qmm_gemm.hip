@@ -235,27 +235,37 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(const uint8_t *__res
     }
 }
 
+// A workgroup's LDS on gfx950 holds at most 160 KiB.
+constexpr size_t kMaxLds = 160 * 1024;
+
+template <int KIND, typename AT, int BM, int BN, int BK, int WM, int WN>
+static hipError_t run_as(const uint8_t *W, const void *A, float *C, int64_t M, int64_t N, int64_t K,
+                         hipStream_t s) {
+  constexpr size_t lds = Tile<BM, BN, BK, sizeof(AT) == 4>::LDS_BYTES;
+  if constexpr (lds > kMaxLds) {
+    return hipErrorInvalidConfiguration;  // a shape that does not fit is never launched
+  } else {
+    const int64_t row_bytes = (K / Geometry<KIND>::elems) * Geometry<KIND>::bytes;
+    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(64 * WM * WN);
+    hipLaunchKernelGGL((gemm_kernel<KIND, AT, BM, BN, BK, WM, WN>), grid, block, lds, s, W, row_bytes,
+                       (const AT *)A, C, (int)M, (int)N, (int)K);
+    return hipGetLastError();
+  }
+}
+
 template <int KIND, int BM, int BN, int BK, int WM, int WN>
 static hipError_t run(const uint8_t *W, const void *A, int a_f16, float *C, int64_t M, int64_t N, int64_t K,
                       hipStream_t s) {
-  const int64_t row_bytes = (K / Geometry<KIND>::elems) * Geometry<KIND>::bytes;
-  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(64 * WM * WN);
-  if (a_f16) {
-    constexpr size_t lds = Tile<BM, BN, BK, false>::LDS_BYTES;
-    hipLaunchKernelGGL((gemm_kernel<KIND, _Float16, BM, BN, BK, WM, WN>), grid, block, lds, s, W, row_bytes,
-                       (const _Float16 *)A, C, (int)M, (int)N, (int)K);
-  } else {
-    constexpr size_t lds = Tile<BM, BN, BK, true>::LDS_BYTES;
-    hipLaunchKernelGGL((gemm_kernel<KIND, float, BM, BN, BK, WM, WN>), grid, block, lds, s, W, row_bytes,
-                       (const float *)A, C, (int)M, (int)N, (int)K);
-  }
-  return hipGetLastError();
+  return a_f16 ? run_as<KIND, _Float16, BM, BN, BK, WM, WN>(W, A, C, M, N, K, s)
+               : run_as<KIND, float, BM, BN, BK, WM, WN>(W, A, C, M, N, K, s);
 }
 
 // Tile shapes.  Up to 64 tokens: 64 x 128 tiles.  Otherwise 128 x 64 tiles
 // with 128-element stages while that grid still fits the 256 compute units
-// in one round, else 128 x 128 tiles with 128-element stages and eight waves
-// (fewer re-reads of the activations, two waves per SIMD).
+// in one round, else 128 x 128 tiles with eight waves (fewer re-reads of the
+// activations, two waves per SIMD): 128-element stages for f16 A, 64-element
+// stages for f32 A, whose two f16 planes would need 192 KiB of LDS with
+// 128-element stages.
 template <int KIND>
 static hipError_t run_m(const uint8_t *W, const void *A, int a_f16, float *C, int64_t M, int64_t N, int64_t K,
                         hipStream_t s, int cfg) {
@@ -277,7 +287,8 @@ static hipError_t run_m(const uint8_t *W, const void *A, int a_f16, float *C, in
 #endif
   if (M <= 64) return run<KIND, 64, 128, 64, 1, 4>(W, A, a_f16, C, M, N, K, s);
   if (((M + 127) / 128) * ((N + 63) / 64) <= 256) return run<KIND, 128, 64, 128, 2, 2>(W, A, a_f16, C, M, N, K, s);
-  return run<KIND, 128, 128, 128, 2, 4>(W, A, a_f16, C, M, N, K, s);
+  if (a_f16) return run_as<KIND, _Float16, 128, 128, 128, 2, 4>(W, A, C, M, N, K, s);
+  return run_as<KIND, float, 128, 128, 64, 2, 4>(W, A, C, M, N, K, s);
 }
 
 }  // namespace gm

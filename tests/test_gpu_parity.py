@@ -223,6 +223,24 @@ def test_gemm_large_grid_tiles(oracle_mod, kind):
     assert_within_bound(got[:, rows], Y, B, f"{kind} M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("kind", ["Q8_0", "Q4_K"])
+def test_gemm_large_grid_f32_activations(oracle_mod, kind):
+    """f32 A on a grid past one round of 128 x 64 tiles: the large-tile
+    shape with the activation split into two f16 planes."""
+    M, N = 300, 9000
+    K = 1280 if wl.geometry(kind)[1] == 256 else 1312
+    g = wl.rng("gpu_gemm_large_f32", kind)
+    W = wl.random_weights(kind, N, K, g)
+    X = wl.activations((M, K), np.float32, g)
+    C = filled((M, N))
+    qmm.qmm_gemm_ex(kind, dev(W), dev(X), C, M, N, K)
+    got = host(C)
+    rows = _sample_rows(N, g, n=200)
+    Y, B = oracle_mod.matmul(kind, W, K, X, rows=rows)
+    assert not np.any(got == SENTINEL)
+    assert_within_bound(got[:, rows], Y, B, f"{kind} f32 M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("kind", ALL_KINDS)
 def test_gemm_unit_vectors_return_f16_weights(oracle_mod, kind):
     N, K = 130, small_K(kind)

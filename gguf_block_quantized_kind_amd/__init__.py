@@ -153,9 +153,17 @@ def _stream(stream) -> int:
     return int(s.cuda_stream)
 
 
-def _need(t, count: int, what: str):
+_F32, _F16, _F32_OR_F16, _I32 = ("float32",), ("float16",), ("float32", "float16"), ("int32",)
+
+
+def _need(t, count: int, what: str, dtypes=None):
+    """Length, layout and element type of a buffer the library will touch:
+    a wrong element type would make the counts below mean other byte sizes
+    (an f16 output of M*N elements is half the bytes the kernel writes)."""
     if t is None:
         return
+    if dtypes is not None and str(t.dtype).replace("torch.", "") not in dtypes:
+        raise TypeError(f"{what} must be {' or '.join(dtypes)}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     if t.numel() < count:
@@ -163,6 +171,8 @@ def _need(t, count: int, what: str):
 
 
 def _check_weights(kind, W, rows: int, K: int):
+    if W is not None and W.element_size() != 1:
+        raise TypeError(f"W must be a byte tensor (uint8 or int8), got {W.dtype}")
     rb = qmm_row_bytes(kind, K)
     if rb > 0:
         _need(W, rows * rb, "W (bytes)")
@@ -173,46 +183,46 @@ def _check_weights(kind, W, rows: int, K: int):
 # ---------------------------------------------------------------------------
 def qmm_gemv(kind, W, x, y, N: int, K: int):
     _check_weights(kind, W, N, K)
-    _need(x, K, "x")
-    _need(y, N, "y")
+    _need(x, K, "x", _F32)
+    _need(y, N, "y", _F32)
     _check(load_library().qmm_gemv(kind_id(kind), _ptr(W), _ptr(x), _ptr(y), N, K))
 
 
 def qmm_gemv_ex(kind, W, x, y, M: int, N: int, K: int, stream=None):
     _check_weights(kind, W, N, K)
-    _need(x, M * K, "x")
-    _need(y, M * N, "y")
+    _need(x, M * K, "x", _F32_OR_F16)
+    _need(y, M * N, "y", _F32)
     _check(load_library().qmm_gemv_ex(kind_id(kind), _ptr(W), _ptr(x), _dtype_code(x), _ptr(y),
                                       M, N, K, _stream(stream)))
 
 
 def qmm_gemm(kind, W, A, C, M: int, N: int, K: int):
     _check_weights(kind, W, N, K)
-    _need(A, M * K, "A")
-    _need(C, M * N, "C")
+    _need(A, M * K, "A", _F16)
+    _need(C, M * N, "C", _F32)
     _check(load_library().qmm_gemm(kind_id(kind), _ptr(W), _ptr(A), _ptr(C), M, N, K))
 
 
 def qmm_gemm_ex(kind, W, A, C, M: int, N: int, K: int, stream=None):
     _check_weights(kind, W, N, K)
-    _need(A, M * K, "A")
-    _need(C, M * N, "C")
+    _need(A, M * K, "A", _F32_OR_F16)
+    _need(C, M * N, "C", _F32)
     _check(load_library().qmm_gemm_ex(kind_id(kind), _ptr(W), _ptr(A), _dtype_code(A), _ptr(C),
                                       M, N, K, _stream(stream)))
 
 
 def qmm_matmul(kind, W, A, C, M: int, N: int, K: int, stream=None):
     _check_weights(kind, W, N, K)
-    _need(A, M * K, "A")
-    _need(C, M * N, "C")
+    _need(A, M * K, "A", _F32_OR_F16)
+    _need(C, M * N, "C", _F32)
     _check(load_library().qmm_matmul(kind_id(kind), _ptr(W), _ptr(A), _dtype_code(A), _ptr(C),
                                      M, N, K, _stream(stream)))
 
 
 def qmm_gemm_mx(kind, W, A, C, M: int, N: int, K: int, workspace, stream=None):
     _check_weights(kind, W, N, K)
-    _need(A, M * K, "A")
-    _need(C, M * N, "C")
+    _need(A, M * K, "A", _F32_OR_F16)
+    _need(C, M * N, "C", _F32)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().qmm_gemm_mx(kind_id(kind), _ptr(W), _ptr(A), _dtype_code(A), _ptr(C),
                                       M, N, K, _ptr(workspace), ws_bytes, _stream(stream)))
@@ -222,10 +232,10 @@ def qmm_moe_ffn(kind, W_gu, W_d, E: int, ids, topk_w, topk: int, X, Y, M: int, N
                 workspace, stream=None):
     _check_weights(kind, W_gu, E * 2 * N_ff, K)
     _check_weights(kind, W_d, E * K, N_ff)
-    _need(ids, M * topk, "ids")
-    _need(topk_w, M * topk, "topk_w")
-    _need(X, M * K, "X")
-    _need(Y, M * K, "Y")
+    _need(ids, M * topk, "ids", _I32)
+    _need(topk_w, M * topk, "topk_w", _F32)
+    _need(X, M * K, "X", _F32_OR_F16)
+    _need(Y, M * K, "Y", _F32)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().qmm_moe_ffn(kind_id(kind), _ptr(W_gu), _ptr(W_d), E, _ptr(ids), _ptr(topk_w), topk,
                                       _ptr(X), _dtype_code(X), _ptr(Y), M, N_ff, K, _ptr(workspace), ws_bytes,
@@ -235,9 +245,9 @@ def qmm_moe_ffn(kind, W_gu, W_d, E: int, ids, topk_w, topk: int, X, Y, M: int, N
 def qmm_moe(kind, W, E: int, ids, topk: int, X, x_per_slot: int, Y, M: int, N: int, K: int,
             workspace, stream=None):
     _check_weights(kind, W, E * N, K)
-    _need(ids, M * topk, "ids")
-    _need(X, M * (topk if x_per_slot else 1) * K, "X")
-    _need(Y, M * topk * N, "Y")
+    _need(ids, M * topk, "ids", _I32)
+    _need(X, M * (topk if x_per_slot else 1) * K, "X", _F32_OR_F16)
+    _need(Y, M * topk * N, "Y", _F32)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().qmm_moe(kind_id(kind), _ptr(W), E, _ptr(ids), topk, _ptr(X),
                                   _dtype_code(X), int(x_per_slot), _ptr(Y), M, N, K,
@@ -247,8 +257,10 @@ def qmm_moe(kind, W, E: int, ids, topk: int, X, x_per_slot: int, Y, M: int, N: i
 def qmm_dequant(kind, W, out, n_elems: int, stream=None):
     bb, be = qmm_block_geometry(kind)
     if n_elems % be == 0:
+        if W is not None and W.element_size() != 1:
+            raise TypeError(f"W must be a byte tensor (uint8 or int8), got {W.dtype}")
         _need(W, (n_elems // be) * bb, "W (bytes)")
-    _need(out, n_elems, "out")
+    _need(out, n_elems, "out", _F32)
     _check(load_library().qmm_dequant(kind_id(kind), _ptr(W), _ptr(out), n_elems, _stream(stream)))
 
 

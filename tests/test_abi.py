@@ -216,3 +216,34 @@ def test_binding_fails_loudly_without_library(tmp_path):
             qmm.load_library(str(tmp_path / "missing.so"))
     finally:
         qmm._lib = saved
+
+
+def test_binding_refuses_wrong_element_types(lib):
+    """The binding checks element types before calling the library: an f16
+    output of M*N elements is half the bytes the kernel writes, int64 ids
+    would be read as int32 pairs.  (CPU tensors: nothing reaches the GPU.)"""
+    torch = pytest.importorskip("torch")
+    u8 = torch.zeros(18 * 4, dtype=torch.uint8)
+    x32, x16 = torch.zeros(32), torch.zeros(32, dtype=torch.float16)
+    y32, y16 = torch.zeros(4), torch.zeros(4, dtype=torch.float16)
+    with pytest.raises(TypeError, match="y must be float32"):
+        qmm.qmm_gemv_ex("Q4_0", u8, x32, y16, 1, 4, 32)
+    with pytest.raises(TypeError, match="W must be a byte tensor"):
+        qmm.qmm_gemv_ex("Q4_0", torch.zeros(18, dtype=torch.int32), x32, y32, 1, 4, 32)
+    with pytest.raises(TypeError, match="x must be float32"):
+        qmm.qmm_gemv("Q4_0", u8, x16, y32, 4, 32)
+    with pytest.raises(TypeError, match="A must be float16"):
+        qmm.qmm_gemm("Q4_0", u8, x32, y32, 1, 4, 32)
+    with pytest.raises(TypeError, match="C must be float32"):
+        qmm.qmm_matmul("Q4_0", u8, x16, y16, 1, 4, 32)
+    ids64 = torch.zeros((1, 2), dtype=torch.int64)
+    with pytest.raises(TypeError, match="ids must be int32"):
+        qmm.qmm_moe("Q4_0", torch.zeros(18 * 8, dtype=torch.uint8), 2, ids64, 2, x32, 0,
+                    torch.zeros(8), 1, 4, 32, None)
+    ids32 = torch.zeros((1, 2), dtype=torch.int32)
+    with pytest.raises(TypeError, match="topk_w must be float32"):
+        qmm.qmm_moe_ffn("Q4_0", torch.zeros(18 * 8, dtype=torch.uint8), torch.zeros(18 * 8, dtype=torch.uint8),
+                        2, ids32, torch.zeros((1, 2), dtype=torch.float16), 2, x32, torch.zeros(32), 1, 2, 32,
+                        None)
+    with pytest.raises(TypeError, match="out must be float32"):
+        qmm.qmm_dequant("Q4_0", u8, torch.zeros(32, dtype=torch.float16), 32)

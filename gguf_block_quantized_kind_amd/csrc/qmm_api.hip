@@ -188,9 +188,9 @@ QMM_EXPORT int qmm_gemm_mx(int kind, const void *W, const void *A, int a_dtype, 
   if (!aligned(W, 16)) return fail(QMM_ERR_BAD_ARG, "W is not 16-byte aligned");
   if ((st = check_act(A, a_dtype, "A"))) return st;
   if (!aligned(C, 4)) return fail(QMM_ERR_BAD_ARG, "C is not 4-byte aligned");
-  // One workgroup per 64 x 192 (or 64 x 256) tile in a one-dimensional grid.
+  // One workgroup per 64 x 128 or 64 x 192 tile in a one-dimensional grid.
   const int64_t Mp = (M + 63) / 64 * 64;
-  if (M > (int64_t)65535 * 64 || (Mp / 64) * ((N + 191) / 192) > (int64_t)INT32_MAX - 7 ||
+  if (M > (int64_t)65535 * 64 || (Mp / 64) * ((N + 127) / 128) > (int64_t)INT32_MAX - 7 ||
       Mp * K > ((int64_t)1 << 40))
     return fail(QMM_ERR_BAD_ARG, "M=%lld, N=%lld, K=%lld exceed the supported range", (long long)M,
                 (long long)N, (long long)K);

@@ -36,13 +36,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 64;   // tokens per tile (the workspace pads rows to this)
-// Weight rows per tile: 4 waves x kTN tiles of 16 rows.  Three tiles per
+// Weight rows per tile: 4 waves x TN tiles of 16 rows.  Three tiles per
 // wave (192 rows) keep a wave within 256 registers, so two workgroups share
 // a compute unit; that beats four tiles per wave (256 rows, one workgroup
 // per compute unit) at every size measured: 256 tokens x 11008 rows, 35.5
 // against 43.1 us; 1024 tokens, 102 against 119 us.  Memory parallelism per
 // compute unit bounds this kernel, and the second workgroup adds to it.
+// Two tiles per wave (128 rows) pay off only when 192-row tiles would leave
+// most compute units idle: 128 tokens, 27.9 against 33.8 us, but 41.0
+// against 35.5 us at 256 tokens.
 constexpr int kTN = 3;
+constexpr int kTNSmall = 2;
 constexpr int kKS = 128;  // k per matrix-core step
 constexpr int kPD = 3;    // loads run this many steps ahead
 
@@ -363,10 +367,18 @@ hipError_t launch_gemm_mx(const uint8_t *W, const void *A, int a_f16, float *C, 
   if (e != hipSuccess) return e;
   const int64_t row_bytes = (K / 32) * 17;
   const int64_t m_tiles = L.Mp / mx::kBM;
-  const int64_t n_tiles = (N + 64 * mx::kTN - 1) / (64 * mx::kTN);
+  // 192-row tiles, or 128-row tiles when there would be fewer than 128 of
+  // the larger ones (half the compute units).
+  const bool small = (N + 64 * mx::kTN - 1) / (64 * mx::kTN) * m_tiles < 128;
+  const int tn = small ? mx::kTNSmall : mx::kTN;
+  const int64_t n_tiles = (N + 64 * tn - 1) / (64 * tn);
   const dim3 grid((unsigned)(8 * ((n_tiles * m_tiles + 7) / 8)));
-  hipLaunchKernelGGL((mx::gemm_mx_kernel<mx::kPD, mx::kTN>), grid, block, 0, s, W, row_bytes, codes, scales, C,
-                     (int)M, (int)N, (int)K, (int)n_tiles, (int)m_tiles);
+  if (small)
+    hipLaunchKernelGGL((mx::gemm_mx_kernel<mx::kPD, mx::kTNSmall>), grid, block, 0, s, W, row_bytes, codes, scales,
+                       C, (int)M, (int)N, (int)K, (int)n_tiles, (int)m_tiles);
+  else
+    hipLaunchKernelGGL((mx::gemm_mx_kernel<mx::kPD, mx::kTN>), grid, block, 0, s, W, row_bytes, codes, scales, C,
+                       (int)M, (int)N, (int)K, (int)n_tiles, (int)m_tiles);
   return hipGetLastError();
 }
 

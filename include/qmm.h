@@ -159,7 +159,7 @@ size_t qmm_moe_ffn_workspace_bytes(int64_t E, int64_t M, int64_t topk, int64_t N
  * qmm_gemm_mx_workspace_bytes(M, K) bytes at 16-byte alignment, overwritten by
  * the call; calls that share it must not overlap.  Errors: kinds other than
  * MXFP4 give QMM_ERR_UNSUPPORTED_KIND, a short workspace QMM_ERR_WORKSPACE,
- * M > 65535 * 64 or more than 2^31 - 8 tiles of 64 x 192 QMM_ERR_BAD_ARG,
+ * M > 65535 * 64 or more than 2^31 - 8 tiles of 64 x 128 QMM_ERR_BAD_ARG,
  * the rest as qmm_gemm_ex. */
 int qmm_gemm_mx(int kind, const void *W, const void *A, int a_dtype, float *C,
                 int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,

@@ -124,3 +124,17 @@ def test_ffn_all_slots_skipped_and_determinism(oracle_mod):
     assert np.all(outs[0][2] == 0.0)
     y, tol = oracle_mod.moe_ffn(kind, W_gu, W_d, E, N_ff, K, ids, w, X)
     check(outs[0], y, tol, "skipped row")
+
+
+def test_ffn_one_expert_top1(oracle_mod):
+    """E = 1, top-1: every token takes the single expert with weight 1."""
+    kind, N_ff, K, M = "Q8_0", 64, 96, 3
+    g = wl.rng("gpu_ffn_e1", kind)
+    W_gu = wl.random_weights(kind, 2 * N_ff, K, g)
+    W_d = wl.random_weights(kind, K, N_ff, g)
+    ids = np.zeros((M, 1), dtype=np.int32)
+    w = np.ones((M, 1), dtype=np.float32)
+    X = wl.activations((M, K), np.float16, g)
+    got = run_ffn(kind, W_gu, W_d, 1, ids, w, X, N_ff)
+    y, tol = oracle_mod.moe_ffn(kind, W_gu, W_d, 1, N_ff, K, ids, w, X)
+    check(got, y, tol, "E=1 top-1")

@@ -150,3 +150,16 @@ def test_gemm_mx_large_grid(oracle_mod):
     Y, B = oracle_mod.matmul(KIND, W, K, X, rows=rows)
     assert not np.any(got == SENTINEL)
     assert_within_bound(got[:, rows], Y, B, "M=512 N=7680")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (65, 17, 128), (3, 129, 384), (64, 193, 2048)])
+def test_gemm_mx_edge_shapes(oracle_mod, M, N, K):
+    """One 128-k step, a single weight row, ragged token and row tiles, and
+    a K of whole aligned groups with fewer steps than the aligned path needs
+    ahead: small-integer activations, so the 1e-3 bar applies."""
+    g = wl.rng("gpu_mx_edge", f"{M}_{N}_{K}")
+    W = wl.random_weights(KIND, N, K, g)
+    X = g.integers(-16, 17, size=(M, K)).astype(np.float32)
+    got = run(W, X, N)
+    Y, B = oracle_mod.matmul(KIND, W, K, X)
+    assert_within_bound(got, Y, B, f"M={M} N={N} K={K}")

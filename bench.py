@@ -7,6 +7,12 @@ f32 outputs -- four GEMV launches through the C ABI.  The reported value is
 the quantized-weight bytes those launches read per second (each weight byte
 counted once per launch), over exactly --steps steps after --warmup steps.
 
+By default the weights are held in the load-time repacked layout
+(qmm_repack, run once before timing: the same bytes, permuted into 16-row
+records in the order the GEMV lanes load them) and the step calls
+qmm_gemv_packed; --layout native times qmm_gemv_ex on the GGUF rows as
+stored.  The step in the other layout is reported among the secondary lines.
+
 Weights are resident in HBM before timing starts.  To measure HBM rather
 than the 256 MiB Infinity Cache, every launch reads a different copy of its
 weight set; a copy is read again only after more than 1 GiB of other weights
@@ -21,9 +27,11 @@ Also printed in the same JSON line:
   cpu_baseline  the oracle (binary64 CPU reference) timed on the host cores
                 on full steps of the same workload;
   cases         each of the four GEMVs alone;
-  secondary     the other workloads (Q4_0 GEMV, prefill GEMMs, codebook
-                kinds, routed experts, the scaled MXFP4 GEMM, the routed
-                expert FFN), each timed the same way.
+  secondary     the decode step's GEMVs in the other weight layout, and the
+                other workloads (Q4_0 GEMV, prefill GEMMs, codebook kinds,
+                in both layouts where they are GEMVs, routed experts, the
+                scaled MXFP4 GEMM, the routed expert FFN), each timed the
+                same way.
 """
 from __future__ import annotations
 
@@ -99,12 +107,22 @@ def time_launches(torch, case: Case, launches: int) -> float:
     return best
 
 
-def gemv_cases(torch, qmm, wl):
+def packed_copies(torch, qmm, w, min_copies: int = 2):
+    """Rotating copies of w's weights in the load-time repacked layout: the
+    repack runs once, here, before anything is timed."""
+    base = qmm.repack(w.kind, torch.from_numpy(w.weights()).cuda(), w.N, w.K)
+    torch.cuda.synchronize()
+    n = max(min_copies, math.ceil(MALL_DEFEAT_BYTES / base.numel()) + 1)
+    return [base] + [base.clone() for _ in range(n - 1)]
+
+
+def gemv_cases(torch, qmm, wl, layout: str = "packed"):
+    """The decode step: Q4_K and Q6_K at M = 1 and 8, their weights in the
+    repacked layout (qmm_gemv_packed) or as native GGUF rows (qmm_gemv_ex)."""
     cases = []
     for kind in ("Q4_K", "Q6_K"):
         w1 = next(w for w in wl.C2 if w.kind == kind and w.M == 1)
-        W = w1.weights()
-        copies = make_copies(torch, W)
+        copies = packed_copies(torch, qmm, w1) if layout == "packed" else make_copies(torch, w1.weights())
         for M in (1, 8):
             w = next(w for w in wl.C2 if w.kind == kind and w.M == M)
             x = torch.from_numpy(w.x()).cuda()
@@ -114,14 +132,31 @@ def gemv_cases(torch, qmm, wl):
 
             def launch(i, kind=kind, x=x, y=y, M=M, w=w, copies=copies, par=par):
                 c = copies[(2 * i + par) % len(copies)]
-                qmm.qmm_gemv_ex(kind, c, x, y, M, w.N, w.K)
+                if layout == "packed":
+                    qmm.qmm_gemv_packed(kind, c, x, y, M, w.N, w.K)
+                else:
+                    qmm.qmm_gemv_ex(kind, c, x, y, M, w.N, w.K)
 
-            cases.append(Case(w.name, kind, launch, copies, w.weight_bytes, w.flops))
+            name = w.name + ("_packed" if layout == "packed" else "")
+            cases.append(Case(name, kind, launch, copies, w.weight_bytes, w.flops))
     return cases
 
 
-def secondary_cases(torch, qmm, wl):
+def secondary_cases(torch, qmm, wl, layout: str = "packed"):
     cases = []
+    # The decode step in the other weight layout.
+    cases += gemv_cases(torch, qmm, wl, "native" if layout == "packed" else "packed")
+    # The other decode workloads over repacked weights (their native-layout
+    # lines follow below).
+    for w in [w for w in wl.C1 + wl.C4 if w.M <= 8]:
+        copies = packed_copies(torch, qmm, w)
+        x = torch.from_numpy(w.x()).cuda()
+        y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+
+        def launch(i, w=w, x=x, y=y, copies=copies):
+            qmm.qmm_gemv_packed(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
+
+        cases.append(Case(w.name + "_packed", w.kind, launch, copies, w.weight_bytes, w.flops))
     for w in wl.C1 + wl.C3 + wl.C4:
         copies = make_copies(torch, w.weights())
         x = torch.from_numpy(w.x()).cuda()
@@ -297,6 +332,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
+    ap.add_argument("--layout", choices=("packed", "native"), default="packed",
+                    help="weight layout of the timed decode step: repacked once at load (default) or "
+                         "native GGUF rows")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0: skip)")
     ap.add_argument("--profile-case", metavar="NAME",
                     help="counter-collection mode: launch only this decode GEMV case, eagerly, --steps times")
@@ -337,7 +375,7 @@ def main():
         print(json.dumps({"copy_probe_bytes": src.numel(), "copies": args.steps}))
         return
 
-    cases = gemv_cases(torch, qmm, wl)
+    cases = gemv_cases(torch, qmm, wl, args.layout)
     if args.profile_case:
         case = next(c for c in cases if c.name == args.profile_case)
         for i in range(args.steps):
@@ -396,12 +434,16 @@ def main():
         for c in cases:
             c.copies.clear()
         torch.cuda.empty_cache()
-        for c in secondary_cases(torch, qmm, wl):
+        sec = secondary_cases(torch, qmm, wl, args.layout)
+        # Cases of one weight set share its copies: free them after the last.
+        last = {id(c.copies): i for i, c in enumerate(sec)}
+        for i, c in enumerate(sec):
             c.launch(0)
             torch.cuda.synchronize()
             secondary[c.name] = describe(c, time_launches(torch, c, 32))
-            c.copies.clear()
-            torch.cuda.empty_cache()
+            if last[id(c.copies)] == i:
+                c.copies.clear()
+                torch.cuda.empty_cache()
 
     cpu = cpu_baseline(wl, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
@@ -413,6 +455,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode GEMV, Q4_K and Q6_K weights, M=1 and M=8, N=14336, K=4096, "
                                "f32 activations, one launch per (kind, M) per step",
+                   "weight_layout": ("load-time repacked (same bytes, permuted; repacked once before "
+                                     "timing)" if args.layout == "packed" else "native GGUF rows"),
                    "weight_bytes_per_step": bytes_per_step, "hbm_frac": round(value / HBM_PEAK_GBS, 4),
                    "device": props.name, "cus": props.multi_processor_count},
         "roofline": roofline,

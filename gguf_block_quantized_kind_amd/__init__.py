@@ -59,6 +59,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         "qmm_moe_ffn_workspace_bytes": (SZ, [I64, I64, I64, I64, I64]),
         "qmm_gemm_mx_workspace_bytes": (SZ, [I64, I64]),
         "qmm_dequant": (I, [I, P, P, I64, P]),
+        "qmm_packed_bytes": (I64, [I, I64, I64]),
+        "qmm_repack": (I, [I, P, P, I64, I64, P]),
+        "qmm_gemv_packed": (I, [I, P, P, I, P, I64, I64, I64, P]),
         "qmm_row_bytes": (I64, [I, I64]),
         "qmm_block_geometry": (I, [I, ctypes.POINTER(I), ctypes.POINTER(I)]),
         "qmm_kind_from_name": (I, [ctypes.c_char_p]),
@@ -254,6 +257,32 @@ def qmm_moe(kind, W, E: int, ids, topk: int, X, x_per_slot: int, Y, M: int, N: i
                                   _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def qmm_packed_bytes(kind, N: int, K: int) -> int:
+    return int(load_library().qmm_packed_bytes(kind_id(kind), N, K))
+
+
+def qmm_repack(kind, W, P, N: int, K: int, stream=None):
+    _check_weights(kind, W, N, K)
+    pb = qmm_packed_bytes(kind, N, K)
+    if P is not None and P.element_size() != 1:
+        raise TypeError(f"P must be a byte tensor, got {P.dtype}")
+    if pb > 0:
+        _need(P, pb, "P (bytes)")
+    _check(load_library().qmm_repack(kind_id(kind), _ptr(W), _ptr(P), N, K, _stream(stream)))
+
+
+def qmm_gemv_packed(kind, P, x, y, M: int, N: int, K: int, stream=None):
+    pb = qmm_packed_bytes(kind, N, K)
+    if P is not None and P.element_size() != 1:
+        raise TypeError(f"P must be a byte tensor, got {P.dtype}")
+    if pb > 0:
+        _need(P, pb, "P (bytes)")
+    _need(x, M * K, "x", _F32_OR_F16)
+    _need(y, M * N, "y", _F32)
+    _check(load_library().qmm_gemv_packed(kind_id(kind), _ptr(P), _ptr(x), _dtype_code(x), _ptr(y),
+                                          M, N, K, _stream(stream)))
+
+
 def qmm_dequant(kind, W, out, n_elems: int, stream=None):
     bb, be = qmm_block_geometry(kind)
     if n_elems % be == 0:
@@ -337,6 +366,28 @@ def moe_ffn(kind, W_gu, W_d, E: int, ids, topk_w, X, N_ff: int, stream=None, wor
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
     qmm_moe_ffn(kind, W_gu, W_d, E, ids, topk_w, topk, X, Y, M, N_ff, K, workspace, stream)
     return Y
+
+
+def repack(kind, W, N: int, K: int, stream=None):
+    """The repacked layout of N native rows (a new uint8 tensor)."""
+    import torch
+    pb = qmm_packed_bytes(kind, N, K)
+    if pb < 0:  # the library names the reason (kind, K or shape)
+        _check(load_library().qmm_repack(kind_id(kind), None, None, N, K, None))
+        raise QmmError(5, f"kind {kind} with N={N}, K={K} has no repacked layout")
+    P = torch.empty(pb, dtype=torch.uint8, device=W.device)
+    qmm_repack(kind, W, P, N, K, stream)
+    return P
+
+
+def gemv_packed(kind, P, x, N: int, stream=None):
+    """y[M, N] for x [M, K] (M <= 8) or [K], from repacked weights."""
+    import torch
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    M, K = x2.shape
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    qmm_gemv_packed(kind, P, x2, y, M, N, K, stream)
+    return y
 
 
 def dequant(kind, W, n_elems: int | None = None, stream=None):

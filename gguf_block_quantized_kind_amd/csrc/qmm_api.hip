@@ -232,6 +232,51 @@ QMM_EXPORT int qmm_moe(int kind, const void *W, int64_t E, const int32_t *ids, i
                     "moe launch");
 }
 
+QMM_EXPORT int64_t qmm_packed_bytes(int kind, int64_t N, int64_t K) {
+  if (!qmm::packed_supported(kind)) return -1;
+  return qmm::packed_bytes_of(kind, N, K);
+}
+
+// Kind, then K % 256 (the repacked layout's k-block), after the usual shape
+// checks.
+static int check_packed(int kind, int64_t M, int64_t N, int64_t K) {
+  const KindInfo *k;
+  int st = check_shape(kind, M, N, K, &k);
+  if (st) return st;
+  if (!qmm::packed_supported(kind))
+    return fail(QMM_ERR_UNSUPPORTED_KIND, "%s has no repacked layout", k->name);
+  if (K % 256 != 0)
+    return fail(QMM_ERR_K_NOT_BLOCK_ALIGNED, "the repacked layout needs K a multiple of 256, got K=%lld",
+                (long long)K);
+  if (qmm::packed_bytes_of(kind, N, K) > ((int64_t)1 << 40))
+    return fail(QMM_ERR_BAD_ARG, "N=%lld, K=%lld exceed the supported range", (long long)N, (long long)K);
+  return QMM_OK;
+}
+
+QMM_EXPORT int qmm_repack(int kind, const void *W, void *P, int64_t N, int64_t K, void *stream) {
+  int st = check_packed(kind, 1, N, K);
+  if (st) return st;
+  if (!W || !P) return fail(QMM_ERR_BAD_ARG, "W or P is NULL");
+  if (!aligned(P, 16)) return fail(QMM_ERR_BAD_ARG, "P is not 16-byte aligned");
+  return hip_status(qmm::launch_repack(kind, (const uint8_t *)W, P, N, K, (hipStream_t)stream), "repack launch");
+}
+
+QMM_EXPORT int qmm_gemv_packed(int kind, const void *P, const void *x, int x_dtype, float *y, int64_t M, int64_t N,
+                               int64_t K, void *stream) {
+  int st = check_packed(kind, M, N, K);
+  if (st) return st;
+  if ((st = check_dtype(x_dtype))) return st;
+  if (!P || !y) return fail(QMM_ERR_BAD_ARG, "P or y is NULL");
+  if (!aligned(P, 16)) return fail(QMM_ERR_BAD_ARG, "P is not 16-byte aligned");
+  if ((st = check_act(x, x_dtype, "x"))) return st;
+  if (!aligned(y, 4)) return fail(QMM_ERR_BAD_ARG, "y is not 4-byte aligned");
+  if (M > QMM_GEMV_MAX_M) return fail(QMM_ERR_BAD_ARG, "GEMV takes 1..%d tokens, got M=%lld", QMM_GEMV_MAX_M, (long long)M);
+  if (M * K >= ((int64_t)1 << 31)) return fail(QMM_ERR_BAD_ARG, "M*K=%lld exceeds 2^31-1", (long long)(M * K));
+  return hip_status(qmm::launch_gemv_packed(kind, (const uint8_t *)P, x, x_dtype == QMM_F16, y, (int)M, N, K,
+                                            (hipStream_t)stream),
+                    "gemv_packed launch");
+}
+
 QMM_EXPORT int qmm_dequant(int kind, const void *W, float *out, int64_t n_elems, void *stream) {
   if (n_elems <= 0) return fail(QMM_ERR_EMPTY_SHAPE, "empty shape: n_elems=%lld", (long long)n_elems);
   const KindInfo *k = find_kind(kind);

@@ -454,5 +454,162 @@ template <> struct Dec<IQ4_NL> : DecIQ4NL {};
 template <> struct Dec<MXFP4> : DecMXFP4 {};
 template <> struct Dec<IQ4_XS> : DecIQ4XS {};
 
+// ---------------------------------------------------------------------------
+// The repacked layout written by qmm_repack.  Tile t (rows 16t .. 16t+15) and
+// k-block b form one record of 16 * BYTES bytes at (t * n_kblocks + b) * 16 *
+// BYTES.  A record is a run of sections: a lane section is 1024 bytes, slot
+// 16 G + j holding the 16 bytes that lane (j, G) decodes; a row section holds
+// one field run per row, read alike by the four lanes of that row.  Every
+// load below is aligned, and a wave's load of a lane section is 1024
+// contiguous bytes.  Rec<KIND>::Packed is what a lane holds between issue and
+// decode; unpack() rebuilds the decoder's Raw from it with register moves and
+// shifts only.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 lda16(const uint8_t *p) {
+  return *reinterpret_cast<const u32x4 *>(__builtin_assume_aligned(p, 16));
+}
+__device__ __forceinline__ u32x2 lda8(const uint8_t *p) {
+  return *reinterpret_cast<const u32x2 *>(__builtin_assume_aligned(p, 8));
+}
+
+// Two lane sections of 4-bit codes (Q4_0, IQ4_NL, MXFP4, Q5_0, IQ4_XS): slot
+// (G, j) of section c holds code bytes 4G .. 4G+3 of blocks 4c .. 4c+3, one
+// dword per block.
+struct NibCodes {
+  u32x4 c0, c1;
+  __device__ void load(const uint8_t *rec, int lane) {
+    c0 = lda16(rec + 16 * lane);
+    c1 = lda16(rec + 1024 + 16 * lane);
+  }
+  __device__ uint32_t q(int s) const { return s < 4 ? c0[s] : c1[s - 4]; }
+};
+
+template <int KIND> struct Rec;
+
+// Q4_0 and IQ4_NL: codes, then a row section of the eight f16 scales.
+template <typename Dd>
+struct RecD16 {
+  struct Packed { NibCodes c; u32x4 d; };
+  __device__ static void load(const uint8_t *rec, int lane, int j, int, Packed &p) {
+    p.c.load(rec, lane);
+    p.d = lda16(rec + 2048 + 16 * j);
+  }
+  __device__ static typename Dd::Raw unpack(const Packed &p, int) {
+    typename Dd::Raw r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r.q[s] = p.c.q(s);
+      r.d[s] = p.d[s >> 1] >> (16 * (s & 1));  // the decoder reads the low half
+    }
+    return r;
+  }
+};
+template <> struct Rec<Q4_0> : RecD16<DecQ4_0> {};
+template <> struct Rec<IQ4_NL> : RecD16<DecIQ4NL> {};
+
+// MXFP4: codes, then a row section of the eight E8M0 bytes.
+template <> struct Rec<MXFP4> {
+  struct Packed { NibCodes c; u32x2 e; };
+  __device__ static void load(const uint8_t *rec, int lane, int j, int, Packed &p) {
+    p.c.load(rec, lane);
+    p.e = lda8(rec + 2048 + 8 * j);
+  }
+  __device__ static DecMXFP4::Raw unpack(const Packed &p, int) {
+    DecMXFP4::Raw r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r.q[s] = p.c.q(s);
+      r.e[s] = (p.e[s >> 2] >> (8 * (s & 3))) & 0xFFu;
+    }
+    return r;
+  }
+};
+
+// Q5_0: codes, the eight 32-bit qh words of the row, then the f16 scales.
+template <> struct Rec<Q5_0> {
+  struct Packed { NibCodes c; u32x4 h0, h1, d; };
+  __device__ static void load(const uint8_t *rec, int lane, int j, int, Packed &p) {
+    p.c.load(rec, lane);
+    p.h0 = lda16(rec + 2048 + 32 * j);
+    p.h1 = lda16(rec + 2048 + 32 * j + 16);
+    p.d = lda16(rec + 2560 + 16 * j);
+  }
+  __device__ static DecQ5_0::Raw unpack(const Packed &p, int G) {
+    DecQ5_0::Raw r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r.q[s] = p.c.q(s);
+      r.qh[s] = (s < 4 ? p.h0[s] : p.h1[s - 4]) >> (4 * G);
+      r.d[s] = p.d[s >> 1] >> (16 * (s & 1));
+    }
+    return r;
+  }
+};
+
+// Q8_0: four lane sections, section c holding code bytes 8G .. 8G+7 of
+// blocks 2c and 2c+1; then the f16 scales.
+template <> struct Rec<Q8_0> {
+  struct Packed { u32x4 c[4]; u32x4 d; };
+  __device__ static void load(const uint8_t *rec, int lane, int j, int, Packed &p) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) p.c[c] = lda16(rec + 1024 * c + 16 * lane);
+    p.d = lda16(rec + 4096 + 16 * j);
+  }
+  __device__ static DecQ8_0::Raw unpack(const Packed &p, int) {
+    DecQ8_0::Raw r;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r.q[s] = u32x2{p.c[s >> 1][2 * (s & 1)], p.c[s >> 1][2 * (s & 1) + 1]};
+      r.d[s] = p.d[s >> 1] >> (16 * (s & 1));
+    }
+    return r;
+  }
+};
+
+// IQ4_XS: codes of the eight groups, then the row's 8-byte header (d,
+// scales_h, scales_l).
+template <> struct Rec<IQ4_XS> {
+  struct Packed { NibCodes c; u32x2 h; };
+  __device__ static void load(const uint8_t *rec, int lane, int j, int, Packed &p) {
+    p.c.load(rec, lane);
+    p.h = lda8(rec + 2048 + 8 * j);
+  }
+  __device__ static DecIQ4XS::Raw unpack(const Packed &p, int) {
+    DecIQ4XS::Raw r;
+    r.h = p.h;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r.q[s] = p.c.q(s);
+    return r;
+  }
+};
+
+// Q4_K: code bytes 32G .. 32G+15 and 32G+16 .. 32G+31 (sections 0, 1), then
+// the row's 16-byte header (d, dmin, the packed scales and mins).
+template <> struct Rec<Q4_K> {
+  using Packed = DecQ4K::Raw;
+  __device__ static void load(const uint8_t *rec, int lane, int j, int, Packed &p) {
+    p.q0 = lda16(rec + 16 * lane);
+    p.q1 = lda16(rec + 1024 + 16 * lane);
+    p.hdr = lda16(rec + 2048 + 16 * j);
+  }
+  __device__ static Packed unpack(const Packed &p, int) { return p; }
+};
+
+// Q6_K: for half h = G/2 and byte lane a = G%2, the low-nibble runs
+// 64h + 16a and 64h + 32 + 16a and the high-bit run 128 + 32h + 16a
+// (sections 0-2); then the row's sixteen int8 scales and its f16 d.
+template <> struct Rec<Q6_K> {
+  using Packed = DecQ6K::Raw;
+  __device__ static void load(const uint8_t *rec, int lane, int j, int G, Packed &p) {
+    p.ql0 = lda16(rec + 16 * lane);
+    p.ql1 = lda16(rec + 1024 + 16 * lane);
+    p.qh = lda16(rec + 2048 + 16 * lane);
+    p.sc = lda8(rec + 3072 + 16 * j + 8 * (G >> 1));
+    p.d = *reinterpret_cast<const uint16_t *>(__builtin_assume_aligned(rec + 3328 + 2 * j, 2));
+  }
+  __device__ static Packed unpack(const Packed &p, int) { return p; }
+};
+
+
 }  // namespace gv
 }  // namespace qmm

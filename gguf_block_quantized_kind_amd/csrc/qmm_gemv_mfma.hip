@@ -48,14 +48,18 @@ struct Chunks {
   struct Held { u32x4 c[L]; };
   __device__ static int offset(int c) { return c < C - 1 ? 16 * c : Dd::BYTES - 16; }
 };
-template <typename Dd>
-using Held = typename std::conditional<Dd::CHUNKED, typename Chunks<Dd>::Held, typename Dd::Raw>::type;
+template <int KIND, bool PACKED, typename Dd = Dec<KIND>>
+using Held = typename std::conditional<
+    PACKED, typename Rec<KIND>::Packed,
+    typename std::conditional<Dd::CHUNKED, typename Chunks<Dd>::Held, typename Dd::Raw>::type>::type;
 
 template <typename XT> struct XVec;
 template <> struct XVec<float> { typedef float type __attribute__((ext_vector_type(4))); };
 template <> struct XVec<_Float16> { typedef _Float16 type __attribute__((ext_vector_type(4))); };
 
-template <int KIND, typename XT, int MT, int S, int R, int PD, int OCC, bool ROUTED>
+// PACKED: W is the repacked layout (the records above Rec in
+// qmm_gemv_mfma.h) instead of native rows; row_bytes is then unused.
+template <int KIND, typename XT, int MT, int S, int R, int PD, int OCC, bool ROUTED, bool PACKED>
 __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void gemv_mfma_kernel(
     const uint8_t *__restrict__ W, int64_t row_bytes, const XT *__restrict__ X, float *__restrict__ Y, int M,
     int64_t N, int K, MoeRoute rt) {
@@ -98,12 +102,20 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   if (threadIdx.x == 0) lds[S * (PD + 1) * kFrag] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
+  constexpr int64_t kRec = 16 * Dd::BYTES;  // one repacked record
   const uint8_t *wr[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    int64_t row = row0 + 16 * r + j;
-    if (row >= N) row = N - 1;  // decode a real row; its outputs are not stored
-    wr[r] = W + row * row_bytes;
+    if constexpr (PACKED) {
+      // Tiles past the last one decode the last (padded) tile; their
+      // outputs are not stored.
+      const int64_t tile = min(row0 / 16 + r, (N - 1) / 16);
+      wr[r] = W + tile * nkb * kRec;
+    } else {
+      int64_t row = row0 + 16 * r + j;
+      if (row >= N) row = N - 1;  // decode a real row; its outputs are not stored
+      wr[r] = W + row * row_bytes;
+    }
   }
   floatx4 acc[R];
 #pragma unroll
@@ -132,7 +144,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   // decoded, so the memory pipe stays busy through every compute phase.
   constexpr int NS = PD + 1;
   const int kb0 = (int)((int64_t)wave * nkb / S), kb1 = (int)((int64_t)(wave + 1) * nkb / S);
-  Held<Dd> raw[NS][R];
+  Held<KIND, PACKED> raw[NS][R];
   X4 xv[NS][XS::kPerLane];
   auto issue = [&](int kb, int slot) {
 #pragma unroll
@@ -143,7 +155,9 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if constexpr (Dd::CHUNKED) {
+      if constexpr (PACKED) {
+        Rec<KIND>::load(wr[r] + kb * kRec, lane, j, G, raw[slot][r]);
+      } else if constexpr (Dd::CHUNKED) {
 #pragma unroll
         for (int i = 0; i < CK::L; ++i)  // past the last chunk: a harmless re-read of it
           raw[slot][r].c[i] = ld16(wr[r] + (int64_t)kb * Dd::BYTES + CK::offset(min(4 * i + G, CK::C - 1)));
@@ -192,7 +206,9 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         typename Dd::Raw fr;  // the decoder's fields for this tile and k-block
-        if constexpr (Dd::CHUNKED) {
+        if constexpr (PACKED) {
+          fr = Rec<KIND>::unpack(raw[d][r], G);
+        } else if constexpr (Dd::CHUNKED) {
           // Stage the tile's k-block in LDS, then read the decoder's fields.
           uint8_t *row = stage + j * CK::RS;
           constexpr int rem = Dd::BYTES - 16 * (CK::C - 1);  // new bytes in the last chunk
@@ -238,7 +254,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
             for (int p = 0; p < Dd::NPART; ++p) D[p] = mfma16(a[st], Dd::bop(fr, sc, st, p), D[p]);
           acc[r] = Dd::post(acc[r], D, xsum, sc);
         }
-        if constexpr (Dd::CHUNKED) {
+        if constexpr (Dd::CHUNKED && !PACKED) {
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();  // the staging is rewritten by the next tile
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -276,20 +292,20 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   }
 }
 
-template <int KIND, int MT, int S, int R, int PD, int OCC = 1, bool ROUTED = false>
+template <int KIND, int MT, int S, int R, int PD, int OCC = 1, bool ROUTED = false, bool PACKED = false>
 static hipError_t run(const uint8_t *W, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,
                       hipStream_t s, MoeRoute rt = MoeRoute{}, int items = 0) {
   const int64_t row_bytes = (K / Geometry<KIND>::elems) * Geometry<KIND>::bytes;
   const size_t ring = (size_t)S * (PD + 1) * XSlice<KIND, MT>::kFrag * 16 + 16 +
-                      (Dec<KIND>::CHUNKED ? (size_t)S * 16 * Chunks<Dec<KIND>>::RS : 0);
+                      (Dec<KIND>::CHUNKED && !PACKED ? (size_t)S * 16 * Chunks<Dec<KIND>>::RS : 0);
   const size_t lds = std::max<size_t>(ring, (size_t)(S - 1) * R * 64 * sizeof(floatx4));
   const unsigned tiles = (unsigned)((N + 16 * R - 1) / (16 * R));
   const dim3 grid = ROUTED ? dim3((unsigned)items, tiles) : dim3(tiles), block(64 * S);
   if (x_f16)
-    hipLaunchKernelGGL((gemv_mfma_kernel<KIND, _Float16, MT, S, R, PD, OCC, ROUTED>), grid, block, lds, s, W,
+    hipLaunchKernelGGL((gemv_mfma_kernel<KIND, _Float16, MT, S, R, PD, OCC, ROUTED, PACKED>), grid, block, lds, s, W,
                        row_bytes, (const _Float16 *)x, y, M, N, (int)K, rt);
   else
-    hipLaunchKernelGGL((gemv_mfma_kernel<KIND, float, MT, S, R, PD, OCC, ROUTED>), grid, block, lds, s, W,
+    hipLaunchKernelGGL((gemv_mfma_kernel<KIND, float, MT, S, R, PD, OCC, ROUTED, PACKED>), grid, block, lds, s, W,
                        row_bytes, (const float *)x, y, M, N, (int)K, rt);
   return hipGetLastError();
 }
@@ -342,7 +358,77 @@ static hipError_t run_routed(const uint8_t *W, const void *x, int x_f16, float *
   return run<KIND, 16, 1, 4, 1, 1, true>(W, x, x_f16, y, 16, N, K, s, rt, items);
 }
 
+// Launch shapes over the repacked layout (no staging).  One token: the
+// folded decoders keep the native shape; the step-scaled ones split K over
+// more waves (8, or 16 with one k-block in flight when there are at most 256
+// tiles), as measured best at 4096 and 11008 rows.
+template <int KIND>
+static hipError_t run_packed(const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,
+                             hipStream_t s, int cfg) {
+#ifdef QMM_TUNING
+  switch (cfg) {
+    case 21: if (M <= 1) return run<KIND, 1, 4, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 22: if (M <= 1) return run<KIND, 1, 2, 1, 3, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 23: if (M <= 1) return run<KIND, 1, 4, 1, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 24: if (M <= 1) return run<KIND, 1, 1, 1, 3, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 25: if (M <= 1) return run<KIND, 1, 2, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 26: if (M > 4) return run<KIND, 8, 4, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 27: if (M > 4) return run<KIND, 8, 2, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 28: if (M <= 1) return run<KIND, 1, 8, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 29: if (M <= 1) return run<KIND, 1, 8, 1, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 30: if (M <= 1) return run<KIND, 1, 16, 1, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 31: if (M <= 1) return run<KIND, 1, 4, 1, 3, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    default: break;
+  }
+#else
+  (void)cfg;
+#endif
+  if constexpr (Dec<KIND>::STEP_SCALE) {
+    if (M <= 1) {
+      if (N <= 4096) return run<KIND, 1, 16, 1, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s);
+      return run<KIND, 1, 8, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
+    }
+  }
+  if (M <= 1) return run<KIND, 1, 2, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
+  if (M <= 2) return run<KIND, 2, 2, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
+  if (M <= 4) return run<KIND, 4, 2, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
+  return run<KIND, 8, 2, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
+}
+
 }  // namespace gv
+
+bool packed_supported(int kind) {
+  switch (kind) {
+    case Q4_K: case Q6_K: case IQ4_XS: case Q4_0: case Q5_0: case Q8_0: case IQ4_NL: case MXFP4:
+      return true;
+    default:
+      return false;
+  }
+}
+
+hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
+                              int64_t K, hipStream_t s) {
+#ifdef QMM_TUNING
+  static const int cfg = [] {
+    const char *e = getenv("QMM_GEMV_CFG");
+    return e ? atoi(e) : 0;
+  }();
+#else
+  constexpr int cfg = 0;
+#endif
+  switch (kind) {
+    case Q4_K: return gv::run_packed<Q4_K>(P, x, x_f16, y, M, N, K, s, cfg);
+    case Q6_K: return gv::run_packed<Q6_K>(P, x, x_f16, y, M, N, K, s, cfg);
+    case IQ4_XS: return gv::run_packed<IQ4_XS>(P, x, x_f16, y, M, N, K, s, cfg);
+    case Q4_0: return gv::run_packed<Q4_0>(P, x, x_f16, y, M, N, K, s, cfg);
+    case Q5_0: return gv::run_packed<Q5_0>(P, x, x_f16, y, M, N, K, s, cfg);
+    case Q8_0: return gv::run_packed<Q8_0>(P, x, x_f16, y, M, N, K, s, cfg);
+    case IQ4_NL: return gv::run_packed<IQ4_NL>(P, x, x_f16, y, M, N, K, s, cfg);
+    case MXFP4: return gv::run_packed<MXFP4>(P, x, x_f16, y, M, N, K, s, cfg);
+    default: break;
+  }
+  return hipErrorNotSupported;
+}
 
 bool moe_mfma_supported(int kind, int64_t K) {
   switch (kind) {

@@ -20,6 +20,15 @@ hipError_t launch_gemv(int kind, const uint8_t *W, const void *x, int x_f16, flo
 hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16, float *y,
                             int M, int64_t N, int64_t K, hipStream_t s);
 
+// The repacked layout (qmm_repack): its size in bytes, or -1 for a kind
+// without one or K not a multiple of 256; the repack launch; the GEMV over
+// it (1 <= M <= 8).
+int64_t packed_bytes_of(int kind, int64_t N, int64_t K);
+bool packed_supported(int kind);
+hipError_t launch_repack(int kind, const uint8_t *W, void *P, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
+                              int64_t K, hipStream_t s);
+
 // C[M][N] = A[M][K] . W^T, any M >= 1, A f32 (a_f16 == 0) or f16.
 hipError_t launch_gemm(int kind, const uint8_t *W, const void *A, int a_f16, float *C,
                        int64_t M, int64_t N, int64_t K, hipStream_t s);

@@ -185,6 +185,41 @@ int qmm_moe(int kind, const void *W, int64_t E, const int32_t *ids, int64_t topk
             void *stream);
 size_t qmm_moe_workspace_bytes(int64_t E, int64_t M, int64_t topk);
 
+/* Load-time repack (Vulkore quant_test.cpp, section 4, "repacked fast
+ * path": weights are transformed once when loaded so the decode matvec reads
+ * aligned planes; values rebuilt from the repacked bytes must equal the
+ * native dequantization bit for bit).  The layout is this library's: rows
+ * in tiles of 16 (the last padded with zero rows), K in k-blocks of 256
+ * elements; tile t and k-block b form one record of 16 * B bytes at
+ * (t * K/256 + b) * 16 * B, B being one row's k-block in native bytes (144
+ * for Q4_0, IQ4_NL, Q4_K; 136 for MXFP4, IQ4_XS; 176 Q5_0; 272 Q8_0; 210
+ * Q6_K).  A record holds exactly the bytes of its sixteen native row pieces,
+ * permuted: first lane sections of 1024 bytes (16-byte slot 16 G + j holds
+ * the code bytes that lane j + 16 G of a wave decodes for row j), then row
+ * sections (per row: its scales and headers).  The per-kind byte tables are
+ * in qmm_repack.hip.
+ *
+ * Kinds: Q4_0, Q5_0, Q8_0, IQ4_NL, MXFP4, IQ4_XS, Q4_K, Q6_K.  Size in bytes of
+ * the repacked tensor of N rows of K elements: qmm_packed_bytes (-1 for any
+ * other kind, K not a multiple of 256, or N <= 0). */
+int64_t qmm_packed_bytes(int kind, int64_t N, int64_t K);
+
+/* Repack N native rows W (byte-aligned, N * qmm_row_bytes(kind, K) bytes)
+ * into P (qmm_packed_bytes(kind, N, K) bytes, 16-byte aligned, overwritten)
+ * on `stream`.  Errors: the shape checks of qmm_gemv_ex, then a kind without
+ * a repacked layout (QMM_ERR_UNSUPPORTED_KIND), K not a multiple of 256
+ * (QMM_ERR_K_NOT_BLOCK_ALIGNED), NULL or misaligned pointers
+ * (QMM_ERR_BAD_ARG). */
+int qmm_repack(int kind, const void *W, void *P, int64_t N, int64_t K, void *stream);
+
+/* Decode GEMV over repacked weights P (from qmm_repack with the same kind,
+ * N and K): y[M][N] = x[M][K] . W^T, 1 <= M <= QMM_GEMV_MAX_M, f32 or f16
+ * x, on `stream`; the numerics of qmm_gemv_ex (exact weights, x rounded once
+ * to f16, f32 accumulation).  Errors as qmm_repack, plus those of
+ * qmm_gemv_ex for x, y and M, and M * K >= 2^31 (QMM_ERR_BAD_ARG). */
+int qmm_gemv_packed(int kind, const void *P, const void *x, int x_dtype, float *y,
+                    int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Dequantize n_elems consecutive elements (whole blocks) of W to f32 on
  * `stream`.  Every value is the f32 rounding of the exact value, evaluated
  * scale first with IEEE signed zeros (so MXFP4 code 8 gives -0.0). */

@@ -162,6 +162,40 @@ def test_gemm_mx_refusals_in_order(lib):
     assert g(39, FAKE, FAKE, 1, FAKE, 10, 10, 256, FAKE + 8, need, None) == WS
 
 
+def test_repack_sizes_and_refusals_in_order(lib, oracle_mod):
+    from oracle import repack as rp
+    for name in rp.KINDS:
+        kid = qmm.kind_id(name)
+        for N, K in ((130, 1024), (1, 256), (14336, 4096)):
+            assert lib.qmm_packed_bytes(kid, N, K) == rp.packed_bytes(name, N, K)
+        # Whole tiles: the native size exactly.
+        assert lib.qmm_packed_bytes(kid, 32, 4096) == 32 * qmm.qmm_row_bytes(kid, 4096)
+    for kid in (10, 11, 13):   # Q2_K, Q3_K, Q5_K have no repacked layout
+        assert lib.qmm_packed_bytes(kid, 16, 256) == -1
+    assert lib.qmm_packed_bytes(2, 16, 288) == -1
+    assert lib.qmm_packed_bytes(2, 0, 256) == -1
+    r = lib.qmm_repack
+    assert r(2, FAKE, FAKE, 0, 256, None) == EMPTY
+    assert r(13, FAKE, FAKE, 16, 256, None) == KIND
+    assert "repacked" in qmm.qmm_last_error()
+    assert r(2, FAKE, FAKE, 16, 48, None) == KALIGN     # not whole Q4_0 blocks
+    assert r(2, FAKE, FAKE, 16, 288, None) == KALIGN    # whole blocks, not whole k-blocks
+    assert "256" in qmm.qmm_last_error()
+    assert r(2, None, FAKE, 16, 256, None) == ARG
+    assert r(2, FAKE, FAKE + 8, 16, 256, None) == ARG   # P not 16-byte aligned
+    g = lib.qmm_gemv_packed
+    assert g(12, FAKE, FAKE, 0, FAKE, 0, 16, 256, None) == EMPTY
+    assert g(11, FAKE, FAKE, 0, FAKE, 1, 16, 256, None) == KIND
+    assert g(2, FAKE, FAKE, 0, FAKE, 1, 16, 256 + 32, None) == KALIGN
+    assert g(12, FAKE, FAKE, 2, FAKE, 1, 16, 256, None) == DTYPE
+    assert g(12, None, FAKE, 0, FAKE, 1, 16, 256, None) == ARG
+    assert g(12, FAKE + 4, FAKE, 0, FAKE, 1, 16, 256, None) == ARG
+    assert g(12, FAKE, FAKE + 2, 0, FAKE, 1, 16, 256, None) == ARG
+    assert g(12, FAKE, FAKE, 0, FAKE + 2, 1, 16, 256, None) == ARG
+    assert g(12, FAKE, FAKE, 0, FAKE, 9, 16, 256, None) == ARG
+    assert g(12, FAKE, FAKE, 0, FAKE, 8, 16, 1 << 28, None) == ARG   # M * K >= 2^31
+
+
 def test_moe_ffn_refusals_in_order(lib):
     g = lib.qmm_moe_ffn
     need = lib.qmm_moe_ffn_workspace_bytes(8, 4, 2, 256, 512)

@@ -62,6 +62,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         "qmm_packed_bytes": (I64, [I, I64, I64]),
         "qmm_repack": (I, [I, P, P, I64, I64, P]),
         "qmm_gemv_packed": (I, [I, P, P, I, P, I64, I64, I64, P]),
+        "qmm_gemv_i8": (I, [I, P, P, I, P, I64, I64, I64, P, SZ, P]),
+        "qmm_gemv_i8_workspace_bytes": (SZ, [I64, I64]),
         "qmm_row_bytes": (I64, [I, I64]),
         "qmm_block_geometry": (I, [I, ctypes.POINTER(I), ctypes.POINTER(I)]),
         "qmm_kind_from_name": (I, [ctypes.c_char_p]),
@@ -283,6 +285,25 @@ def qmm_gemv_packed(kind, P, x, y, M: int, N: int, K: int, stream=None):
                                           M, N, K, _stream(stream)))
 
 
+def qmm_gemv_i8_workspace_bytes(M: int, K: int) -> int:
+    return int(load_library().qmm_gemv_i8_workspace_bytes(M, K))
+
+
+def qmm_gemv_i8(kind, P, x, y, M: int, N: int, K: int, workspace, stream=None):
+    pb = qmm_packed_bytes(kind, N, K)
+    if P is not None and P.element_size() != 1:
+        raise TypeError(f"P must be a byte tensor, got {P.dtype}")
+    if pb > 0:
+        _need(P, pb, "P (bytes)")
+    _need(x, M * K, "x", _F32_OR_F16)
+    _need(y, M * N, "y", _F32)
+    if workspace is not None and workspace.element_size() != 1:
+        raise TypeError(f"workspace must be a byte tensor, got {workspace.dtype}")
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(load_library().qmm_gemv_i8(kind_id(kind), _ptr(P), _ptr(x), _dtype_code(x), _ptr(y), M, N, K,
+                                      _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def qmm_dequant(kind, W, out, n_elems: int, stream=None):
     bb, be = qmm_block_geometry(kind)
     if n_elems % be == 0:
@@ -387,6 +408,18 @@ def gemv_packed(kind, P, x, N: int, stream=None):
     M, K = x2.shape
     y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     qmm_gemv_packed(kind, P, x2, y, M, N, K, stream)
+    return y
+
+
+def gemv_i8(kind, P, x, N: int, stream=None, workspace=None):
+    """y[M, N] from repacked Q8_0 / Q4_0 weights with int8-quantized x."""
+    import torch
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    M, K = x2.shape
+    if workspace is None:
+        workspace = torch.empty(max(qmm_gemv_i8_workspace_bytes(M, K), 1), dtype=torch.uint8, device=x.device)
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    qmm_gemv_i8(kind, P, x2, y, M, N, K, workspace, stream)
     return y
 
 

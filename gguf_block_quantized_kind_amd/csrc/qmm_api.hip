@@ -277,6 +277,35 @@ QMM_EXPORT int qmm_gemv_packed(int kind, const void *P, const void *x, int x_dty
                     "gemv_packed launch");
 }
 
+QMM_EXPORT size_t qmm_gemv_i8_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
+  return qmm::gemv_i8_workspace_bytes(M, K);
+}
+
+QMM_EXPORT int qmm_gemv_i8(int kind, const void *P, const void *x, int x_dtype, float *y, int64_t M, int64_t N,
+                           int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_packed(kind, M, N, K);
+  if (st) return st;
+  if (!qmm::gemv_i8_supported(kind))
+    return fail(QMM_ERR_UNSUPPORTED_KIND, "the int8-activation GEMV takes Q8_0 or Q4_0 weights, not kind %d", kind);
+  if ((st = check_dtype(x_dtype))) return st;
+  if (!P || !y) return fail(QMM_ERR_BAD_ARG, "P or y is NULL");
+  if (!aligned(P, 16)) return fail(QMM_ERR_BAD_ARG, "P is not 16-byte aligned");
+  if ((st = check_act(x, x_dtype, "x"))) return st;
+  if (!aligned(y, 4)) return fail(QMM_ERR_BAD_ARG, "y is not 4-byte aligned");
+  if (M > QMM_GEMV_MAX_M) return fail(QMM_ERR_BAD_ARG, "GEMV takes 1..%d tokens, got M=%lld", QMM_GEMV_MAX_M, (long long)M);
+  if (M * K > (int64_t)QMM_GEMV_I8_MAX_MK)
+    return fail(QMM_ERR_BAD_ARG, "M*K=%lld exceeds %d (the block scales are staged in LDS)", (long long)(M * K),
+                QMM_GEMV_I8_MAX_MK);
+  const size_t need = qmm::gemv_i8_workspace_bytes(M, K);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(QMM_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  return hip_status(qmm::launch_gemv_i8(kind, (const uint8_t *)P, x, x_dtype == QMM_F16, y, (int)M, N, K, workspace,
+                                        (hipStream_t)stream),
+                    "gemv_i8 launch");
+}
+
 QMM_EXPORT int qmm_dequant(int kind, const void *W, float *out, int64_t n_elems, void *stream) {
   if (n_elems <= 0) return fail(QMM_ERR_EMPTY_SHAPE, "empty shape: n_elems=%lld", (long long)n_elems);
   const KindInfo *k = find_kind(kind);

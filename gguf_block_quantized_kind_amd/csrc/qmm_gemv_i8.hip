@@ -1,0 +1,265 @@
+// qmm_gemv_i8.hip -- the integer-activation decode GEMV: activations
+// quantized per 32-element block to int8, weight codes multiplied as int8 on
+// the matrix cores (v_mfma_i32_16x16x64_i8), one f32 scale product per block.
+// This is the integer dot-product path that the ferrox-cuda mul_mm page names
+// (llama.cpp's mmq) and leaves out; here it reads repacked Q8_0 or Q4_0
+// weights (the records of qmm_repack).
+//
+// Quantization (one thread per token and block): amax = max |x|,
+// d = amax / 127 and each x / d rounded to f32 (both through binary64, whose
+// 53 bits make the double rounding to f32 exact for a quotient of two f32
+// values), then to the nearest integer, ties to even.  An all-zero block has
+// d = 0 and zero codes.  The codes are stored per block in the order the
+// weight codes sit in a lane (below), with the block's scale and code sum.
+//
+// Product.  A k-block (eight blocks) is four MFMA steps of 64 k.  In step c,
+// bytes 0-7 of every lane's operands belong to block 2c and bytes 8-15 to
+// block 2c+1 of the k-block, in both operands, so each k index pairs the
+// same element of x and w whatever the instruction's k order.  A row 2t + p
+// holds token t's codes in the half of block 2c + p and zeros in the other
+// half; D row 2t + p is then token t's exact integer dot product with block
+// 2c + p alone.  Lane (j, G) holds D rows 4G .. 4G+3 of weight row j, i.e.
+// tokens 2G and 2G+1, both blocks: it subtracts the code bias (Q4_0's 8 times
+// the block's code sum, in integers) and adds d_w d_x times the sum in f32.
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "qmm_gemv_mfma.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace i8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+using gv::floatx4;
+using gv::u32x2;
+using gv::u32x4;
+
+// Element of block position 8G + e (the lane order of the weight codes).
+template <int KIND>
+__device__ __forceinline__ int element_of(int pos) {
+  if constexpr (KIND == Q8_0) {
+    return pos;  // code bytes 8G .. 8G+7
+  } else {
+    const int G = pos >> 3, e = pos & 7;  // low nibbles 4G.., high nibbles 16 + 4G..
+    return e < 4 ? 4 * G + e : 16 + 4 * G + (e - 4);
+  }
+}
+
+template <int KIND, typename XT>
+__global__ __launch_bounds__(256) void quantize_kernel(const XT *__restrict__ X, int8_t *__restrict__ q,
+                                                       float *__restrict__ d, int32_t *__restrict__ s,
+                                                       int64_t blocks, int nb) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= blocks) return;
+  const int64_t t = i / nb, b = i - t * nb;
+  const XT *x = X + t * (int64_t)nb * 32 + 32 * b;
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    v[e] = (float)x[e];
+    amax = fmaxf(amax, fabsf(v[e]));
+  }
+  const float db = (float)((double)amax / 127.0);
+  uint32_t w[8] = {};
+  int sum = 0;
+#pragma unroll
+  for (int p = 0; p < 32; ++p) {
+    const float r = db > 0.f ? (float)((double)v[element_of<KIND>(p)] / (double)db) : 0.f;
+    const int c = (int)__builtin_rintf(r);
+    sum += c;
+    w[p >> 2] |= (uint32_t)(c & 0xFF) << (8 * (p & 3));
+  }
+  u32x4 *dst = reinterpret_cast<u32x4 *>(q + i * 32);
+  dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+  dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+  d[i] = db;
+  s[i] = sum;
+}
+
+// B operand of step c: the 8 codes of block 2c, then the 8 of block 2c+1.
+template <int KIND>
+__device__ __forceinline__ v4i bop(const typename gv::Rec<KIND>::Packed &p, int c) {
+  if constexpr (KIND == Q8_0) {
+    return __builtin_bit_cast(v4i, p.c[c]);
+  } else {
+    const uint32_t w0 = p.c.q(2 * c), w1 = p.c.q(2 * c + 1);
+    return v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+               (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+  }
+}
+
+template <int KIND> __device__ __forceinline__ u32x4 dvec(const typename gv::Rec<KIND>::Packed &p) { return p.d; }
+
+template <int KIND, int S, int PD>
+__global__ __launch_bounds__(64 * S) void gemv_i8_kernel(const uint8_t *__restrict__ P, const int8_t *__restrict__ q,
+                                                        const float *__restrict__ dx, const int32_t *__restrict__ sx,
+                                                        float *__restrict__ Y, int M, int64_t N, int K) {
+  using Rc = gv::Rec<KIND>;
+  using Packed = typename Rc::Packed;
+  constexpr int kBias = KIND == Q8_0 ? 0 : 8;
+  constexpr int64_t kRec = 16 * gv::Dec<KIND>::BYTES;
+  extern __shared__ u32x4 lds[];
+  const int nb = K / 32, nkb = K / 256;
+  float *ldx = reinterpret_cast<float *>(lds);       // [M][nb] scales, then [M][nb] code sums
+  int32_t *lsx = reinterpret_cast<int32_t *>(ldx + M * nb);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 15, G = lane >> 4;
+  const int64_t tile = blockIdx.x;
+  const uint8_t *wt = P + tile * nkb * kRec;
+
+  // A-row of this lane: token ta, block parity pa.
+  const int ta = j >> 1, pa = j & 1;
+  const bool alive = ta < M;
+  const int8_t *xa = q + (int64_t)(alive ? ta : 0) * K + 8 * G;
+
+  constexpr int NS = PD + 1;
+  const int kb0 = (int)((int64_t)wave * nkb / S), kb1 = (int)((int64_t)(wave + 1) * nkb / S);
+  Packed raw[NS];
+  u32x2 xq[NS][4];
+  auto issue = [&](int kb, int slot) {
+    Rc::load(wt + kb * kRec, lane, j, G, raw[slot]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x2 v = {0u, 0u};
+      if (alive) v = *reinterpret_cast<const u32x2 *>(xa + 32 * (8 * kb + 2 * c + pa));
+      xq[slot][c] = v;
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < PD; ++d)
+    if (kb0 + d < kb1) issue(kb0 + d, d);
+  // The scales and code sums of every token's blocks, staged once.
+  for (int i = threadIdx.x; i < M * nb; i += 64 * S) {
+    ldx[i] = dx[i];
+    lsx[i] = sx[i];
+  }
+  __syncthreads();
+
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int t0 = min(2 * G, M - 1), t1 = min(2 * G + 1, M - 1);  // tokens of D rows 4G.., clamped
+  for (int kb = kb0; kb < kb1; kb += NS) {
+#pragma unroll
+    for (int d = 0; d < NS; ++d) {
+      if (kb + d >= kb1) break;
+      if (kb + d + PD < kb1) issue(kb + d + PD, (d + PD) % NS);
+      const int k = kb + d;
+      const u32x4 dw = dvec<KIND>(raw[d]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x2 xv = xq[d][c];
+        const v4i a = pa == 0 ? v4i{(int)xv.x, (int)xv.y, 0, 0} : v4i{0, 0, (int)xv.x, (int)xv.y};
+        const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop<KIND>(raw[d], c), v4i{0, 0, 0, 0}, 0, 0, 0);
+        const int b0 = 8 * k + 2 * c;
+        // d_w of blocks 2c and 2c+1: the two halves of dword c of the scales.
+        const float w0 = gv::lo_f16(dw[c]), w1 = gv::hi_f16(dw[c]);
+        const int i00 = t0 * nb + b0, i10 = t1 * nb + b0;
+        acc[0] += (w0 * ldx[i00]) * (float)(D[0] - kBias * lsx[i00]);
+        acc[1] += (w1 * ldx[i00 + 1]) * (float)(D[1] - kBias * lsx[i00 + 1]);
+        acc[2] += (w0 * ldx[i10]) * (float)(D[2] - kBias * lsx[i10]);
+        acc[3] += (w1 * ldx[i10 + 1]) * (float)(D[3] - kBias * lsx[i10 + 1]);
+      }
+    }
+  }
+  // Tokens 2G and 2G+1 of row j: both block parities.
+  float y0 = acc[0] + acc[1], y1 = acc[2] + acc[3];
+  if constexpr (S > 1) {
+    __syncthreads();  // every wave is done with the staged scales
+    float *red = reinterpret_cast<float *>(lds);
+    if (wave > 0) {
+      red[((wave - 1) * 64 + lane) * 2] = y0;
+      red[((wave - 1) * 64 + lane) * 2 + 1] = y1;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < S - 1; ++w) {
+      y0 += red[(w * 64 + lane) * 2];
+      y1 += red[(w * 64 + lane) * 2 + 1];
+    }
+  }
+  const int64_t row = tile * 16 + j;
+  if (row >= N) return;
+  if (2 * G < M) Y[(int64_t)(2 * G) * N + row] = y0;
+  if (2 * G + 1 < M) Y[(int64_t)(2 * G + 1) * N + row] = y1;
+}
+
+template <int KIND, int S, int PD>
+hipError_t run(const uint8_t *P, const int8_t *q, const float *d, const int32_t *s, float *y, int M, int64_t N,
+               int64_t K, hipStream_t st) {
+  const size_t stage = (size_t)M * (K / 32) * 8;
+  const size_t red = (size_t)(S - 1) * 64 * 8;
+  const size_t lds = std::max(stage, red);
+  const unsigned tiles = (unsigned)((N + 15) / 16);
+  hipLaunchKernelGGL((gemv_i8_kernel<KIND, S, PD>), dim3(tiles), dim3(64 * S), lds, st, P, q, d, s, y, M, N, (int)K);
+  return hipGetLastError();
+}
+
+// Launch shape: S waves split K, PD k-blocks in flight.  A tuning build
+// (-DQMM_TUNING) can pick another from QMM_GEMV_I8_CFG.
+template <int KIND>
+hipError_t run_shape(const uint8_t *P, const int8_t *q, const float *d, const int32_t *s, float *y, int M,
+                     int64_t N, int64_t K, hipStream_t st) {
+#ifdef QMM_TUNING
+  static const int cfg = [] {
+    const char *e = getenv("QMM_GEMV_I8_CFG");
+    return e ? atoi(e) : 0;
+  }();
+  switch (cfg) {
+    case 1: return run<KIND, 2, 2>(P, q, d, s, y, M, N, K, st);
+    case 2: return run<KIND, 8, 1>(P, q, d, s, y, M, N, K, st);
+    case 3: return run<KIND, 4, 1>(P, q, d, s, y, M, N, K, st);
+    case 4: return run<KIND, 16, 1>(P, q, d, s, y, M, N, K, st);
+    case 5: return run<KIND, 8, 2>(P, q, d, s, y, M, N, K, st);
+    case 6: return run<KIND, 2, 3>(P, q, d, s, y, M, N, K, st);
+    default: break;
+  }
+#endif
+  // Measured at 4096 and 14336 rows: more waves per tile when tiles are few.
+  if (N <= 4096) return run<KIND, 16, 1>(P, q, d, s, y, M, N, K, st);
+  return run<KIND, 4, 1>(P, q, d, s, y, M, N, K, st);
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+template <int KIND>
+void quantize(const void *x, int x_f16, int8_t *q, float *d, int32_t *s, int64_t blocks, int nb, unsigned grid,
+              hipStream_t st) {
+  if (x_f16)
+    hipLaunchKernelGGL((quantize_kernel<KIND, _Float16>), dim3(grid), dim3(256), 0, st, (const _Float16 *)x, q, d, s,
+                       blocks, nb);
+  else
+    hipLaunchKernelGGL((quantize_kernel<KIND, float>), dim3(grid), dim3(256), 0, st, (const float *)x, q, d, s,
+                       blocks, nb);
+}
+
+}  // namespace i8
+
+bool gemv_i8_supported(int kind) { return kind == Q8_0 || kind == Q4_0; }
+
+size_t gemv_i8_workspace_bytes(int64_t M, int64_t K) {
+  return i8::align256((size_t)M * K) + 2 * i8::align256((size_t)M * (K / 32) * 4);
+}
+
+hipError_t launch_gemv_i8(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
+                          int64_t K, void *ws, hipStream_t st) {
+  int8_t *q = static_cast<int8_t *>(ws);
+  float *d = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + i8::align256((size_t)M * K));
+  int32_t *s = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(d) + i8::align256((size_t)M * (K / 32) * 4));
+  const int nb = (int)(K / 32);
+  const int64_t blocks = (int64_t)M * nb;
+  const unsigned grid = (unsigned)((blocks + 255) / 256);
+  switch (kind) {
+    case Q8_0: i8::quantize<Q8_0>(x, x_f16, q, d, s, blocks, nb, grid, st); break;
+    case Q4_0: i8::quantize<Q4_0>(x, x_f16, q, d, s, blocks, nb, grid, st); break;
+    default: return hipErrorNotSupported;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return kind == Q8_0 ? i8::run_shape<Q8_0>(P, q, d, s, y, M, N, K, st)
+                      : i8::run_shape<Q4_0>(P, q, d, s, y, M, N, K, st);
+}
+
+}  // namespace qmm

@@ -29,6 +29,14 @@ hipError_t launch_repack(int kind, const uint8_t *W, void *P, int64_t N, int64_t
 hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
                               int64_t K, hipStream_t s);
 
+// The int8-activation GEMV over repacked Q8_0 / Q4_0 weights (1 <= M <= 8):
+// activations quantized into `ws` (gemv_i8_workspace_bytes(M, K) bytes,
+// 256-byte aligned), then the integer matrix-core product.
+bool gemv_i8_supported(int kind);
+size_t gemv_i8_workspace_bytes(int64_t M, int64_t K);
+hipError_t launch_gemv_i8(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
+                          int64_t K, void *ws, hipStream_t s);
+
 // C[M][N] = A[M][K] . W^T, any M >= 1, A f32 (a_f16 == 0) or f16.
 hipError_t launch_gemm(int kind, const uint8_t *W, const void *A, int a_f16, float *C,
                        int64_t M, int64_t N, int64_t K, hipStream_t s);

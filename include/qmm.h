@@ -220,6 +220,38 @@ int qmm_repack(int kind, const void *W, void *P, int64_t N, int64_t K, void *str
 int qmm_gemv_packed(int kind, const void *P, const void *x, int x_dtype, float *y,
                     int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Largest M * K of qmm_gemv_i8 (its per-block scales and code sums are
+ * staged in 64 KiB of LDS). */
+#define QMM_GEMV_I8_MAX_MK 262144
+
+/* Decode GEMV with integer activations, a separately toleranced variant of
+ * qmm_gemv_packed for repacked Q8_0 or Q4_0 weights (the integer dot-product
+ * path that the ferrox-cuda mul_mm page names and leaves out).  x (f32 or
+ * f16, [M][K], finite) is first quantized into `workspace`, per token and
+ * 32-element block: amax = max |x|, d = amax / 127 and x / d each rounded to
+ * f32 (correctly rounded), then q = x / d rounded to the nearest integer,
+ * ties to even (|q| <= 127); an all-zero block has d = 0.  Then
+ *   y[t][n] = sum over blocks b of d_w[n][b] d[t][b] (sum_i w_i q_i)
+ * with each block's integer dot product exact (Q4_0 as (code - 8)) and the
+ * scaling and accumulation in f32: y is within 2e-5 * sum |w| |d q| + 1e-6
+ * of the exact product with the rebuilt activations d q (K <= 16384), and
+ * those lie within d / 2 of x.  Workspace layout (qmm_gemv_i8_workspace_bytes(M, K) bytes,
+ * 256-byte aligned, overwritten; calls sharing it must not overlap): the codes
+ * [M][K] int8, each block's 32 codes in the lane order of the weight codes
+ * (Q8_0: element order; Q4_0: position 8G + e holds element 4G + e for e < 4
+ * and 16 + 4G + e - 4 otherwise, G = 0..3); at the next multiple of 256
+ * bytes the scales d [M][K/32] f32; at the next, the code sums [M][K/32]
+ * int32.  1 <= M <= QMM_GEMV_MAX_M and M * K <= QMM_GEMV_I8_MAX_MK.  Errors:
+ * as qmm_gemv_packed, other kinds QMM_ERR_UNSUPPORTED_KIND, a larger M * K
+ * QMM_ERR_BAD_ARG, a missing, short or misaligned workspace
+ * QMM_ERR_WORKSPACE. */
+int qmm_gemv_i8(int kind, const void *P, const void *x, int x_dtype, float *y,
+                int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                void *stream);
+/* Bytes of workspace qmm_gemv_i8 needs; 0 for M <= 0, K <= 0 or K not a
+ * multiple of 32. */
+size_t qmm_gemv_i8_workspace_bytes(int64_t M, int64_t K);
+
 /* Dequantize n_elems consecutive elements (whole blocks) of W to f32 on
  * `stream`.  Every value is the f32 rounding of the exact value, evaluated
  * scale first with IEEE signed zeros (so MXFP4 code 8 gives -0.0). */

@@ -196,6 +196,28 @@ def test_repack_sizes_and_refusals_in_order(lib, oracle_mod):
     assert g(12, FAKE, FAKE, 0, FAKE, 8, 16, 1 << 28, None) == ARG   # M * K >= 2^31
 
 
+def test_gemv_i8_refusals_in_order(lib):
+    g = lib.qmm_gemv_i8
+    need = lib.qmm_gemv_i8_workspace_bytes(3, 512)
+    assert need == 1536 + 2 * 256
+    assert lib.qmm_gemv_i8_workspace_bytes(8, 4096) == 32768 + 2 * 4096
+    assert lib.qmm_gemv_i8_workspace_bytes(0, 512) == 0 and lib.qmm_gemv_i8_workspace_bytes(3, 48) == 0
+    assert g(8, FAKE, FAKE, 0, FAKE, 0, 16, 512, FAKE, need, None) == EMPTY
+    assert g(10, FAKE, FAKE, 0, FAKE, 3, 16, 512, FAKE, need, None) == KIND    # Q2_K: no repacked layout
+    assert g(12, FAKE, FAKE, 0, FAKE, 3, 16, 512, FAKE, need, None) == KIND    # Q4_K: not an integer-code kind
+    assert "Q8_0 or Q4_0" in qmm.qmm_last_error()
+    assert g(8, FAKE, FAKE, 0, FAKE, 3, 16, 288, FAKE, need, None) == KALIGN
+    assert g(8, FAKE, FAKE, 2, FAKE, 3, 16, 512, FAKE, need, None) == DTYPE
+    assert g(8, None, FAKE, 0, FAKE, 3, 16, 512, FAKE, need, None) == ARG
+    assert g(8, FAKE + 8, FAKE, 0, FAKE, 3, 16, 512, FAKE, need, None) == ARG
+    assert g(8, FAKE, FAKE + 2, 0, FAKE, 3, 16, 512, FAKE, need, None) == ARG
+    assert g(8, FAKE, FAKE, 0, FAKE, 9, 16, 512, FAKE, need, None) == ARG
+    assert g(8, FAKE, FAKE, 0, FAKE, 8, 16, 65536, FAKE, 1 << 30, None) == ARG  # M*K > 262144
+    assert g(8, FAKE, FAKE, 0, FAKE, 3, 16, 512, None, need, None) == WS
+    assert g(8, FAKE, FAKE, 0, FAKE, 3, 16, 512, FAKE, need - 1, None) == WS
+    assert g(8, FAKE, FAKE, 0, FAKE, 3, 16, 512, FAKE + 16, need, None) == WS
+
+
 def test_moe_ffn_refusals_in_order(lib):
     g = lib.qmm_moe_ffn
     need = lib.qmm_moe_ffn_workspace_bytes(8, 4, 2, 256, 512)

@@ -212,6 +212,17 @@ def secondary_cases(torch, qmm, wl, layout: str = "packed"):
 
             cases.append(Case(f"{e.name}_{mat}", e.kind, launch, copies, distinct * N * row_b,
                               2 * e.M * e.topk * N * K))
+            # The same products over the experts repacked once at load.
+            base = qmm.repack_experts(e.kind, copies[0], e.E, N, K)
+            torch.cuda.synchronize()
+            pcopies = [base] + [base.clone() for _ in range(len(copies) - 1)]
+
+            def launch_p(i, e=e, N=N, K=K, Xd=Xd, Y=Y, ws=ws, per_slot=per_slot, pcopies=pcopies, ids=ids):
+                qmm.qmm_moe_packed(e.kind, pcopies[i % len(pcopies)], e.E, ids, e.topk, Xd, per_slot, Y,
+                                   e.M, N, K, ws)
+
+            cases.append(Case(f"{e.name}_{mat}_packed", e.kind, launch_p, pcopies, distinct * N * row_b,
+                              2 * e.M * e.topk * N * K))
         del touched
     # The whole routed expert FFN (gate/up, SiLU-product, down, weighted
     # combine) on the same experts and routing; bytes are the touched

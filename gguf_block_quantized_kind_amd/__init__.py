@@ -63,6 +63,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         "qmm_repack": (I, [I, P, P, I64, I64, P]),
         "qmm_gemv_packed": (I, [I, P, P, I, P, I64, I64, I64, P]),
         "qmm_gemv_i8": (I, [I, P, P, I, P, I64, I64, I64, P, SZ, P]),
+        "qmm_moe_packed": (I, [I, P, I64, P, I64, P, I, I, P, I64, I64, I64, P, SZ, P]),
         "qmm_gemv_i8_workspace_bytes": (SZ, [I64, I64]),
         "qmm_row_bytes": (I64, [I, I64]),
         "qmm_block_geometry": (I, [I, ctypes.POINTER(I), ctypes.POINTER(I)]),
@@ -285,6 +286,22 @@ def qmm_gemv_packed(kind, P, x, y, M: int, N: int, K: int, stream=None):
                                           M, N, K, _stream(stream)))
 
 
+def qmm_moe_packed(kind, P, E: int, ids, topk: int, X, x_per_slot: int, Y, M: int, N: int, K: int,
+                   workspace, stream=None):
+    pb = qmm_packed_bytes(kind, N, K)
+    if P is not None and P.element_size() != 1:
+        raise TypeError(f"P must be a byte tensor, got {P.dtype}")
+    if pb > 0:
+        _need(P, E * pb, "P (bytes)")
+    _need(ids, M * topk, "ids", _I32)
+    _need(X, (M * topk if x_per_slot else M) * K, "X", _F32_OR_F16)
+    _need(Y, M * topk * N, "Y", _F32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().qmm_moe_packed(kind_id(kind), _ptr(P), E, _ptr(ids), topk, _ptr(X), _dtype_code(X),
+                                         int(bool(x_per_slot)), _ptr(Y), M, N, K, _ptr(workspace), ws_bytes,
+                                         _stream(stream)))
+
+
 def qmm_gemv_i8_workspace_bytes(M: int, K: int) -> int:
     return int(load_library().qmm_gemv_i8_workspace_bytes(M, K))
 
@@ -409,6 +426,35 @@ def gemv_packed(kind, P, x, N: int, stream=None):
     y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     qmm_gemv_packed(kind, P, x2, y, M, N, K, stream)
     return y
+
+
+def repack_experts(kind, W, E: int, N: int, K: int, stream=None):
+    """E experts of N native rows each, repacked one by one (expert e's
+    records at e * qmm_packed_bytes(kind, N, K))."""
+    import torch
+    pb = qmm_packed_bytes(kind, N, K)
+    if pb < 0:
+        _check(load_library().qmm_repack(kind_id(kind), None, None, N, K, None))
+        raise QmmError(5, f"kind {kind} with N={N}, K={K} has no repacked layout")
+    rb = qmm_row_bytes(kind, K)
+    _check_weights(kind, W, E * N, K)
+    P = torch.empty(E * pb, dtype=torch.uint8, device=W.device)
+    Wf = W.reshape(-1)
+    for e in range(E):
+        qmm_repack(kind, Wf[e * N * rb:(e + 1) * N * rb], P[e * pb:(e + 1) * pb], N, K, stream)
+    return P
+
+
+def moe_packed(kind, P, E: int, ids, X, N: int, K: int, x_per_slot: bool, stream=None, workspace=None):
+    """Y[M, topk, N] of the routed expert products over repacked experts."""
+    import torch
+    M, topk = ids.shape
+    Y = torch.empty((M, topk, N), dtype=torch.float32, device=X.device)
+    if workspace is None:
+        nbytes = qmm_moe_workspace_bytes(E, M, topk)
+        workspace = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=X.device)
+    qmm_moe_packed(kind, P, E, ids, topk, X, int(x_per_slot), Y, M, N, K, workspace, stream)
+    return Y
 
 
 def gemv_i8(kind, P, x, N: int, stream=None, workspace=None):

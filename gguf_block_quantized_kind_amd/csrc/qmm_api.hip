@@ -306,6 +306,34 @@ QMM_EXPORT int qmm_gemv_i8(int kind, const void *P, const void *x, int x_dtype, 
                     "gemv_i8 launch");
 }
 
+QMM_EXPORT int qmm_moe_packed(int kind, const void *P, int64_t E, const int32_t *ids, int64_t topk, const void *X,
+                              int x_dtype, int x_per_slot, float *Y, int64_t M, int64_t N, int64_t K, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  if (E <= 0 || topk <= 0)
+    return fail(QMM_ERR_EMPTY_SHAPE, "empty shape: E=%lld topk=%lld", (long long)E, (long long)topk);
+  int st = check_packed(kind, M, N, K);
+  if (st) return st;
+  if ((st = check_dtype(x_dtype))) return st;
+  if (!P || !ids || !Y) return fail(QMM_ERR_BAD_ARG, "P, ids or Y is NULL");
+  if (!aligned(P, 16)) return fail(QMM_ERR_BAD_ARG, "P is not 16-byte aligned");
+  if ((st = check_act(X, x_dtype, "X"))) return st;
+  if (!aligned(ids, 4) || !aligned(Y, 4)) return fail(QMM_ERR_BAD_ARG, "ids or Y is not 4-byte aligned");
+  if (x_per_slot != 0 && x_per_slot != 1) return fail(QMM_ERR_BAD_ARG, "x_per_slot must be 0 or 1");
+  if (E > qmm::kMoeMaxExperts) return fail(QMM_ERR_BAD_ARG, "E=%lld exceeds %lld experts", (long long)E, (long long)qmm::kMoeMaxExperts);
+  if (M * topk > ((int64_t)1 << 31) - 1 || M * topk * K >= ((int64_t)1 << 31))
+    return fail(QMM_ERR_BAD_ARG, "M*topk*K=%lld exceeds 2^31-1", (long long)(M * topk * K));
+  if (N > ((int64_t)1 << 31) / 4) return fail(QMM_ERR_BAD_ARG, "N=%lld exceeds the supported range", (long long)N);
+  if (E * qmm::packed_bytes_of(kind, N, K) > ((int64_t)1 << 40))
+    return fail(QMM_ERR_BAD_ARG, "E=%lld experts of N=%lld, K=%lld exceed the supported range", (long long)E,
+                (long long)N, (long long)K);
+  const size_t need = qmm::moe_workspace_bytes(E, M, topk);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 4))
+    return fail(QMM_ERR_WORKSPACE, "workspace needs %zu bytes (4-byte aligned), got %zu", need, workspace_bytes);
+  return hip_status(qmm::launch_moe(kind, (const uint8_t *)P, E, ids, topk, X, x_dtype == QMM_F16, x_per_slot, Y, M,
+                                    N, K, workspace, (hipStream_t)stream, true),
+                    "moe_packed launch");
+}
+
 QMM_EXPORT int qmm_dequant(int kind, const void *W, float *out, int64_t n_elems, void *stream) {
   if (n_elems <= 0) return fail(QMM_ERR_EMPTY_SHAPE, "empty shape: n_elems=%lld", (long long)n_elems);
   const KindInfo *k = find_kind(kind);

@@ -91,7 +91,8 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
       order = rt.ws + rt.order_at;
       M = min(MT, rt.ws[rt.offsets_at + e + 1] - c0);
     }
-    W += (int64_t)e * N * row_bytes;
+    // Expert e's rows (repacked: its records, N padded to whole tiles).
+    W += (int64_t)e * (PACKED ? (N + 15) / 16 * 16 : N) * row_bytes;
   }
   // Pair of token slot t of this item.
   auto pair_of = [&](int t) { return order != nullptr ? order[c0 + t] : c0 + t; };
@@ -348,14 +349,14 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
   return run<KIND, 8, 2, 2, 2>(W, x, x_f16, y, M, N, K, s);
 }
 
-template <int KIND>
+template <int KIND, bool PACKED>
 static hipError_t run_routed(const uint8_t *W, const void *x, int x_f16, float *y, int mt, int64_t N, int64_t K,
                              hipStream_t s, const MoeRoute &rt, int items) {
-  if (mt == 1) return run<KIND, 1, 2, 1, 2, 1, true>(W, x, x_f16, y, 1, N, K, s, rt, items);
-  if (mt == 8) return run<KIND, 8, 2, 2, 2, 1, true>(W, x, x_f16, y, 8, N, K, s, rt, items);
+  if (mt == 1) return run<KIND, 1, 2, 1, 2, 1, true, PACKED>(W, x, x_f16, y, 1, N, K, s, rt, items);
+  if (mt == 8) return run<KIND, 8, 2, 2, 2, 1, true, PACKED>(W, x, x_f16, y, 8, N, K, s, rt, items);
   // Sixteen pairs per item: the activation k-block staged by a wave serves
   // four 16-row tiles.
-  return run<KIND, 16, 1, 4, 1, 1, true>(W, x, x_f16, y, 16, N, K, s, rt, items);
+  return run<KIND, 16, 1, 4, 1, 1, true, PACKED>(W, x, x_f16, y, 16, N, K, s, rt, items);
 }
 
 // Launch shapes over the repacked layout (no staging).  One token: the
@@ -440,16 +441,29 @@ bool moe_mfma_supported(int kind, int64_t K) {
 }
 
 hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int mt, int64_t N,
-                           int64_t K, const MoeRoute &rt, int items, hipStream_t s) {
+                           int64_t K, const MoeRoute &rt, int items, hipStream_t s, bool packed) {
+  if (packed) {
+    switch (kind) {
+      case Q4_K: return gv::run_routed<Q4_K, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      case Q6_K: return gv::run_routed<Q6_K, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      case IQ4_XS: return gv::run_routed<IQ4_XS, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      case Q4_0: return gv::run_routed<Q4_0, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      case Q5_0: return gv::run_routed<Q5_0, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      case Q8_0: return gv::run_routed<Q8_0, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      case IQ4_NL: return gv::run_routed<IQ4_NL, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      case MXFP4: return gv::run_routed<MXFP4, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      default: return hipErrorNotSupported;
+    }
+  }
   switch (kind) {
-    case Q4_K: return gv::run_routed<Q4_K>(W, X, x_f16, Y, mt, N, K, s, rt, items);
-    case Q6_K: return gv::run_routed<Q6_K>(W, X, x_f16, Y, mt, N, K, s, rt, items);
-    case IQ4_XS: return gv::run_routed<IQ4_XS>(W, X, x_f16, Y, mt, N, K, s, rt, items);
-    case Q4_0: return gv::run_routed<Q4_0>(W, X, x_f16, Y, mt, N, K, s, rt, items);
-    case Q5_0: return gv::run_routed<Q5_0>(W, X, x_f16, Y, mt, N, K, s, rt, items);
-    case Q8_0: return gv::run_routed<Q8_0>(W, X, x_f16, Y, mt, N, K, s, rt, items);
-    case IQ4_NL: return gv::run_routed<IQ4_NL>(W, X, x_f16, Y, mt, N, K, s, rt, items);
-    case MXFP4: return gv::run_routed<MXFP4>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q4_K: return gv::run_routed<Q4_K, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q6_K: return gv::run_routed<Q6_K, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case IQ4_XS: return gv::run_routed<IQ4_XS, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q4_0: return gv::run_routed<Q4_0, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q5_0: return gv::run_routed<Q5_0, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q8_0: return gv::run_routed<Q8_0, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case IQ4_NL: return gv::run_routed<IQ4_NL, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case MXFP4: return gv::run_routed<MXFP4, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
     default: break;
   }
   return hipErrorNotSupported;

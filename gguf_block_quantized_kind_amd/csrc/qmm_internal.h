@@ -58,9 +58,12 @@ hipError_t launch_gemm_mx(const uint8_t *W, const void *A, int a_f16, float *C, 
 // Routed expert products; see qmm_moe in qmm.h.  `ws` holds
 // moe_workspace_bytes(E, M, topk) bytes.
 size_t moe_workspace_bytes(int64_t E, int64_t M, int64_t topk);
+// packed: W is E experts in the repacked layout (qmm_moe_packed); the
+// matrix-core kernel must then apply (moe_mfma_supported and 32-bit
+// activation offsets), which the caller has checked.
 hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids, int64_t topk,
                       const void *X, int x_f16, int x_per_slot, float *Y, int64_t M, int64_t N,
-                      int64_t K, void *ws, hipStream_t s);
+                      int64_t K, void *ws, hipStream_t s, bool packed = false);
 
 // Largest expert count the routing prologue handles.
 constexpr int64_t kMoeMaxExperts = 4096;
@@ -81,7 +84,9 @@ struct MoeRoute {
 // The matrix-core expert kernel: one workgroup per (work item, 16-row
 // tile); a work item is up to `mt` (1, 8 or 16) pairs of one expert.
 bool moe_mfma_supported(int kind, int64_t K);
+// packed: W holds the experts' repacked records (expert e at
+// e * packed_bytes_of(kind, N, K)).
 hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int mt, int64_t N,
-                           int64_t K, const MoeRoute &rt, int items, hipStream_t s);
+                           int64_t K, const MoeRoute &rt, int items, hipStream_t s, bool packed = false);
 
 }  // namespace qmm

@@ -220,6 +220,16 @@ int qmm_repack(int kind, const void *W, void *P, int64_t N, int64_t K, void *str
 int qmm_gemv_packed(int kind, const void *P, const void *x, int x_dtype, float *y,
                     int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Routed expert products (as qmm_moe) over repacked experts: P holds E
+ * experts, expert e's records (qmm_repack of its N rows) at byte
+ * e * qmm_packed_bytes(kind, N, K).  Kinds and K as qmm_gemv_packed; every
+ * pair runs on the matrix cores, so M * topk * K must stay below 2^31.
+ * Semantics, workspace and the remaining errors as qmm_moe. */
+int qmm_moe_packed(int kind, const void *P, int64_t E, const int32_t *ids, int64_t topk,
+                   const void *X, int x_dtype, int x_per_slot, float *Y,
+                   int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
 /* Largest M * K of qmm_gemv_i8 (its per-block scales and code sums are
  * staged in 64 KiB of LDS). */
 #define QMM_GEMV_I8_MAX_MK 262144

@@ -218,6 +218,28 @@ def test_gemv_i8_refusals_in_order(lib):
     assert g(8, FAKE, FAKE, 0, FAKE, 3, 16, 512, FAKE + 16, need, None) == WS
 
 
+def test_moe_packed_refusals_in_order(lib):
+    f = lib.qmm_moe_packed
+    need = lib.qmm_moe_workspace_bytes(8, 4, 2)
+    args = lambda **k: [k.get("kind", 12), k.get("P", FAKE), k.get("E", 8), k.get("ids", FAKE), k.get("topk", 2),
+                        k.get("X", FAKE), k.get("dt", 1), k.get("ps", 0), k.get("Y", FAKE), k.get("M", 4),
+                        k.get("N", 16), k.get("K", 256), k.get("ws", FAKE), k.get("wsb", need), None]
+    assert f(*args(E=0)) == EMPTY
+    assert f(*args(M=0)) == EMPTY
+    assert f(*args(kind=13)) == KIND                      # Q5_K: no repacked layout
+    assert f(*args(kind=2, K=288)) == KALIGN
+    assert f(*args(dt=5)) == DTYPE
+    assert f(*args(P=None)) == ARG
+    assert f(*args(P=FAKE + 8)) == ARG
+    assert f(*args(X=FAKE + 1)) == ARG
+    assert f(*args(ids=FAKE + 2)) == ARG
+    assert f(*args(ps=2)) == ARG
+    assert f(*args(E=5000)) == ARG
+    assert f(*args(M=1 << 20, topk=8, K=512, wsb=1 << 40)) == ARG     # M*topk*K >= 2^31
+    assert f(*args(ws=None)) == WS
+    assert f(*args(wsb=need - 1)) == WS
+
+
 def test_moe_ffn_refusals_in_order(lib):
     g = lib.qmm_moe_ffn
     need = lib.qmm_moe_ffn_workspace_bytes(8, 4, 2, 256, 512)

@@ -122,3 +122,52 @@ def test_gemv_packed_full_size_sampled(oracle_mod, w):
         rows_t = Wr[16 * t:16 * t + 16]
         want = rp.repack(w.kind, rows_t, rows_t.shape[0], w.K)
         assert np.array_equal(Ph[t * rec:(t + 1) * rec], want), f"tile {t}"
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_moe_packed_parity(oracle_mod, kind):
+    """Routed expert products over repacked experts (qmm_moe_packed), against
+    the oracle's products over the native experts: N = 130 rows per expert
+    (each expert's last tile padded), items of one pair (M = 2, 5), eight
+    (M = 9) and sixteen (M = 40), an id outside [0, E) skipped."""
+    E, N, topk, K = 6, 130, 3, 1280
+    for M in (5, 2, 9, 40):
+        g = wl.rng("gpu_moe_packed", f"{kind}_{M}")
+        W = wl.random_weights(kind, E * N, K, g)
+        ids = wl.routing(M, E, topk, g)
+        ids[0] = [1, 2, 3]
+        ids[1] = [1, 4, -1]   # skipped: its Y row keeps the sentinel
+        if M == 9:
+            ids[:, 0] = 0
+        P = qmm.repack_experts(kind, dev(W), E, N, K)
+        idd = dev(ids)
+        for per_slot, xdt in ((False, np.float16), (True, np.float32)):
+            X = wl.activations((M, topk, K) if per_slot else (M, K), xdt, g)
+            Y = filled((M, topk, N))
+            nbytes = qmm.qmm_moe_workspace_bytes(E, M, topk)
+            ws = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device="cuda")
+            qmm.qmm_moe_packed(kind, P, E, idd, topk, dev(X), int(per_slot), Y, M, N, K, ws)
+            got = host(Y)
+            assert np.all(got[1, 2] == SENTINEL)
+            got[1, 2] = 0.0
+            ids_ok = ids.copy()
+            ids_ok[1, 2] = 0      # the oracle takes only valid ids; that slot is compared as zero
+            Yr, Br = oracle_mod.moe(kind, W, E, N, K, ids_ok, X, per_slot)
+            Yr[1, 2] = 0.0
+            Br[1, 2] = 0.0
+            assert_within_bound(got, Yr, Br, f"{kind} M={M} per_slot={per_slot}")
+
+
+@pytest.mark.parametrize("e", [x for x in wl.C5 if x.M in (1, 16)], ids=lambda e: e.name)
+def test_moe_packed_full_size_sampled(oracle_mod, e):
+    """The expert workload's gate/up matrices (128 experts of 1536 x 2048
+    Q4_K), repacked, at 1 and 16 tokens, on sampled rows."""
+    ids = e.ids()
+    W = e.w_gu()
+    X = e.x()
+    P = qmm.repack_experts(e.kind, dev(W), e.E, e.N_gu, e.K_gu)
+    Y = qmm.moe_packed(e.kind, P, e.E, dev(ids), dev(X), e.N_gu, e.K_gu, False)
+    got = host(Y)
+    rows = _sample_rows(e.N_gu, wl.rng(e.name, "sample_moe_packed"), n=24)
+    Yr, Br = oracle_mod.moe(e.kind, W, e.E, e.N_gu, e.K_gu, ids, X, False, rows=rows)
+    assert_within_bound(got[:, :, rows], Yr, Br, e.name)

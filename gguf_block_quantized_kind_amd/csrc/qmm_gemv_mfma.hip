@@ -362,7 +362,8 @@ static hipError_t run_routed(const uint8_t *W, const void *x, int x_f16, float *
 // Launch shapes over the repacked layout (no staging).  One token: the
 // folded decoders keep the native shape; the step-scaled ones split K over
 // more waves (8, or 16 with one k-block in flight when there are at most 256
-// tiles), as measured best at 4096 and 11008 rows.
+// tiles), as measured best at 4096 and 11008 rows.  Fewer waves per tile
+// (two tiles per wave) measured 40-70% slower at one token.
 template <int KIND>
 static hipError_t run_packed(const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,
                              hipStream_t s, int cfg) {
@@ -379,6 +380,13 @@ static hipError_t run_packed(const uint8_t *P, const void *x, int x_f16, float *
     case 29: if (M <= 1) return run<KIND, 1, 8, 1, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
     case 30: if (M <= 1) return run<KIND, 1, 16, 1, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
     case 31: if (M <= 1) return run<KIND, 1, 4, 1, 3, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 32: if (M > 4) return run<KIND, 8, 2, 2, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 33: if (M > 4) return run<KIND, 8, 4, 2, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 34: if (M > 4) return run<KIND, 8, 2, 3, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 35: if (M > 4) return run<KIND, 8, 1, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 36: if (M <= 1) return run<KIND, 1, 2, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 37: if (M <= 1) return run<KIND, 1, 1, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 38: if (M <= 1) return run<KIND, 1, 4, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
     default: break;
   }
 #else
@@ -393,7 +401,9 @@ static hipError_t run_packed(const uint8_t *P, const void *x, int x_f16, float *
   if (M <= 1) return run<KIND, 1, 2, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
   if (M <= 2) return run<KIND, 2, 2, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
   if (M <= 4) return run<KIND, 4, 2, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
-  return run<KIND, 8, 2, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
+  // Eight tokens: one k-block in flight (the activation ring of eight
+  // tokens is most of the registers; measured 3-4% faster than two).
+  return run<KIND, 8, 2, 2, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s);
 }
 
 }  // namespace gv

@@ -247,6 +247,19 @@ def secondary_cases(torch, qmm, wl, layout: str = "packed"):
 
         cases.append(Case(f"{e.name}_ffn", e.kind, launch, gu + dn, e.touched_bytes(ids_np),
                           2 * e.M * e.topk * (e.N_gu * e.K_gu + e.N_d * e.K_d)))
+        # The same FFN over the experts repacked once at load.
+        pgu0 = qmm.repack_experts(e.kind, gu[0], e.E, e.N_gu, e.K_gu)
+        pdn0 = qmm.repack_experts(e.kind, dn[0], e.E, e.N_d, e.K_d)
+        torch.cuda.synchronize()
+        pgu = [pgu0] + [pgu0.clone() for _ in range(n - 1)]
+        pdn = [pdn0] + [pdn0.clone() for _ in range(n - 1)]
+
+        def launch_p(i, e=e, ids=ids, w=w, Xd=Xd, Y=Y, ws=ws, pgu=pgu, pdn=pdn, n=n, N_ff=N_ff):
+            qmm.qmm_moe_ffn_packed(e.kind, pgu[i % n], pdn[i % n], e.E, ids, w, e.topk, Xd, Y, e.M, N_ff,
+                                   e.K_gu, ws)
+
+        cases.append(Case(f"{e.name}_ffn_packed", e.kind, launch_p, pgu + pdn, e.touched_bytes(ids_np),
+                          2 * e.M * e.topk * (e.N_gu * e.K_gu + e.N_d * e.K_d)))
     return cases
 
 

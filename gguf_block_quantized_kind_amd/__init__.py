@@ -56,6 +56,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         "qmm_moe_workspace_bytes": (SZ, [I64, I64, I64]),
         "qmm_gemm_mx": (I, [I, P, P, I, P, I64, I64, I64, P, SZ, P]),
         "qmm_moe_ffn": (I, [I, P, P, I64, P, P, I64, P, I, P, I64, I64, I64, P, SZ, P]),
+        "qmm_moe_ffn_packed": (I, [I, P, P, I64, P, P, I64, P, I, P, I64, I64, I64, P, SZ, P]),
         "qmm_moe_ffn_workspace_bytes": (SZ, [I64, I64, I64, I64, I64]),
         "qmm_gemm_mx_workspace_bytes": (SZ, [I64, I64]),
         "qmm_dequant": (I, [I, P, P, I64, P]),
@@ -248,6 +249,28 @@ def qmm_moe_ffn(kind, W_gu, W_d, E: int, ids, topk_w, topk: int, X, Y, M: int, N
                                       _stream(stream)))
 
 
+def _check_packed_bytes(kind, P, count: int, N: int, K: int, what: str):
+    pb = qmm_packed_bytes(kind, N, K)
+    if P is not None and P.element_size() != 1:
+        raise TypeError(f"{what} must be a byte tensor, got {P.dtype}")
+    if pb > 0:
+        _need(P, count * pb, f"{what} (bytes)")
+
+
+def qmm_moe_ffn_packed(kind, P_gu, P_d, E: int, ids, topk_w, topk: int, X, Y, M: int, N_ff: int, K: int,
+                       workspace, stream=None):
+    _check_packed_bytes(kind, P_gu, E, 2 * N_ff, K, "P_gu")
+    _check_packed_bytes(kind, P_d, E, K, N_ff, "P_d")
+    _need(ids, M * topk, "ids", _I32)
+    _need(topk_w, M * topk, "topk_w", _F32)
+    _need(X, M * K, "X", _F32_OR_F16)
+    _need(Y, M * K, "Y", _F32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().qmm_moe_ffn_packed(kind_id(kind), _ptr(P_gu), _ptr(P_d), E, _ptr(ids), _ptr(topk_w),
+                                             topk, _ptr(X), _dtype_code(X), _ptr(Y), M, N_ff, K, _ptr(workspace),
+                                             ws_bytes, _stream(stream)))
+
+
 def qmm_moe(kind, W, E: int, ids, topk: int, X, x_per_slot: int, Y, M: int, N: int, K: int,
             workspace, stream=None):
     _check_weights(kind, W, E * N, K)
@@ -403,6 +426,20 @@ def moe_ffn(kind, W_gu, W_d, E: int, ids, topk_w, X, N_ff: int, stream=None, wor
         nbytes = qmm_moe_ffn_workspace_bytes(E, M, topk, N_ff, K)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
     qmm_moe_ffn(kind, W_gu, W_d, E, ids, topk_w, topk, X, Y, M, N_ff, K, workspace, stream)
+    return Y
+
+
+def moe_ffn_packed(kind, P_gu, P_d, E: int, ids, topk_w, X, N_ff: int, stream=None, workspace=None):
+    """moe_ffn over experts repacked with repack_experts (gate/up: E experts of
+    2 N_ff rows of K; down: E experts of K rows of N_ff)."""
+    import torch
+    M, topk = ids.shape
+    K = X.shape[1]
+    Y = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    if workspace is None:
+        nbytes = qmm_moe_ffn_workspace_bytes(E, M, topk, N_ff, K)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
+    qmm_moe_ffn_packed(kind, P_gu, P_d, E, ids, topk_w, topk, X, Y, M, N_ff, K, workspace, stream)
     return Y
 
 

@@ -141,9 +141,26 @@ QMM_EXPORT size_t qmm_moe_ffn_workspace_bytes(int64_t E, int64_t M, int64_t topk
   return qmm::moe_ffn_workspace_bytes(E, M, topk, N_ff, K);
 }
 
-QMM_EXPORT int qmm_moe_ffn(int kind, const void *W_gu, const void *W_d, int64_t E, const int32_t *ids,
+// Kind, then K % 256 (the repacked layout's k-block), after the usual shape
+// checks.
+static int check_packed(int kind, int64_t M, int64_t N, int64_t K) {
+  const KindInfo *k;
+  int st = check_shape(kind, M, N, K, &k);
+  if (st) return st;
+  if (!qmm::packed_supported(kind))
+    return fail(QMM_ERR_UNSUPPORTED_KIND, "%s has no repacked layout", k->name);
+  if (K % 256 != 0)
+    return fail(QMM_ERR_K_NOT_BLOCK_ALIGNED, "the repacked layout needs K a multiple of 256, got K=%lld",
+                (long long)K);
+  if (qmm::packed_bytes_of(kind, N, K) > ((int64_t)1 << 40))
+    return fail(QMM_ERR_BAD_ARG, "N=%lld, K=%lld exceed the supported range", (long long)N, (long long)K);
+  return QMM_OK;
+}
+
+static int moe_ffn_checked(int kind, const void *W_gu, const void *W_d, int64_t E, const int32_t *ids,
                            const float *topk_w, int64_t topk, const void *X, int x_dtype, float *Y, int64_t M,
-                           int64_t N_ff, int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+                           int64_t N_ff, int64_t K, void *workspace, size_t workspace_bytes, void *stream,
+                           bool packed) {
   const KindInfo *k;
   if (E <= 0 || topk <= 0 || N_ff <= 0)
     return fail(QMM_ERR_EMPTY_SHAPE, "empty shape: E=%lld topk=%lld N_ff=%lld", (long long)E, (long long)topk,
@@ -151,8 +168,14 @@ QMM_EXPORT int qmm_moe_ffn(int kind, const void *W_gu, const void *W_d, int64_t 
   int st = check_shape(kind, M, 2 * N_ff, K, &k);  // gate/up: 2 N_ff rows of K
   if (st) return st;
   if ((st = check_shape(kind, M, K, N_ff, &k))) return st;  // down: K rows of N_ff
+  if (packed) {
+    if ((st = check_packed(kind, M, 2 * N_ff, K))) return st;
+    if ((st = check_packed(kind, M, K, N_ff))) return st;
+  }
   if ((st = check_dtype(x_dtype))) return st;
   if (!W_gu || !W_d || !ids || !topk_w || !Y) return fail(QMM_ERR_BAD_ARG, "W_gu, W_d, ids, topk_w or Y is NULL");
+  if (packed && (!aligned(W_gu, 16) || !aligned(W_d, 16)))
+    return fail(QMM_ERR_BAD_ARG, "the repacked W_gu or W_d is not 16-byte aligned");
   if ((st = check_act(X, x_dtype, "X"))) return st;
   if (!aligned(ids, 4) || !aligned(topk_w, 4)) return fail(QMM_ERR_BAD_ARG, "ids or topk_w is not 4-byte aligned");
   if (!aligned(Y, 16)) return fail(QMM_ERR_BAD_ARG, "Y is not 16-byte aligned");
@@ -162,13 +185,31 @@ QMM_EXPORT int qmm_moe_ffn(int kind, const void *W_gu, const void *W_d, int64_t 
       2 * N_ff > ((int64_t)1 << 31) / 4 || K > ((int64_t)1 << 31) / 4)
     return fail(QMM_ERR_BAD_ARG, "M*topk=%lld with N_ff=%lld, K=%lld exceeds the supported range", (long long)P,
                 (long long)N_ff, (long long)K);
+  // Repacked experts always run on the matrix cores, whose activation
+  // offsets are 32-bit.
+  if (packed && P * (N_ff > K ? N_ff : K) >= ((int64_t)1 << 31))
+    return fail(QMM_ERR_BAD_ARG, "M*topk*max(K, N_ff)=%lld exceeds 2^31-1", (long long)(P * (N_ff > K ? N_ff : K)));
   const size_t need = qmm::moe_ffn_workspace_bytes(E, M, topk, N_ff, K);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(QMM_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
   return hip_status(qmm::launch_moe_ffn(kind, (const uint8_t *)W_gu, (const uint8_t *)W_d, E, ids, topk_w, topk, X,
-                                        x_dtype == QMM_F16, Y, M, N_ff, K, workspace, (hipStream_t)stream),
+                                        x_dtype == QMM_F16, Y, M, N_ff, K, workspace, (hipStream_t)stream, packed),
                     "moe_ffn launch");
+}
+
+QMM_EXPORT int qmm_moe_ffn(int kind, const void *W_gu, const void *W_d, int64_t E, const int32_t *ids,
+                           const float *topk_w, int64_t topk, const void *X, int x_dtype, float *Y, int64_t M,
+                           int64_t N_ff, int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+  return moe_ffn_checked(kind, W_gu, W_d, E, ids, topk_w, topk, X, x_dtype, Y, M, N_ff, K, workspace,
+                         workspace_bytes, stream, false);
+}
+
+QMM_EXPORT int qmm_moe_ffn_packed(int kind, const void *P_gu, const void *P_d, int64_t E, const int32_t *ids,
+                                  const float *topk_w, int64_t topk, const void *X, int x_dtype, float *Y, int64_t M,
+                                  int64_t N_ff, int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+  return moe_ffn_checked(kind, P_gu, P_d, E, ids, topk_w, topk, X, x_dtype, Y, M, N_ff, K, workspace,
+                         workspace_bytes, stream, true);
 }
 
 QMM_EXPORT size_t qmm_gemm_mx_workspace_bytes(int64_t M, int64_t K) {
@@ -235,22 +276,6 @@ QMM_EXPORT int qmm_moe(int kind, const void *W, int64_t E, const int32_t *ids, i
 QMM_EXPORT int64_t qmm_packed_bytes(int kind, int64_t N, int64_t K) {
   if (!qmm::packed_supported(kind)) return -1;
   return qmm::packed_bytes_of(kind, N, K);
-}
-
-// Kind, then K % 256 (the repacked layout's k-block), after the usual shape
-// checks.
-static int check_packed(int kind, int64_t M, int64_t N, int64_t K) {
-  const KindInfo *k;
-  int st = check_shape(kind, M, N, K, &k);
-  if (st) return st;
-  if (!qmm::packed_supported(kind))
-    return fail(QMM_ERR_UNSUPPORTED_KIND, "%s has no repacked layout", k->name);
-  if (K % 256 != 0)
-    return fail(QMM_ERR_K_NOT_BLOCK_ALIGNED, "the repacked layout needs K a multiple of 256, got K=%lld",
-                (long long)K);
-  if (qmm::packed_bytes_of(kind, N, K) > ((int64_t)1 << 40))
-    return fail(QMM_ERR_BAD_ARG, "N=%lld, K=%lld exceed the supported range", (long long)N, (long long)K);
-  return QMM_OK;
 }
 
 QMM_EXPORT int qmm_repack(int kind, const void *W, void *P, int64_t N, int64_t K, void *stream) {

@@ -46,7 +46,7 @@ hipError_t launch_gemm(int kind, const uint8_t *W, const void *A, int a_f16, flo
 size_t moe_ffn_workspace_bytes(int64_t E, int64_t M, int64_t topk, int64_t N_ff, int64_t K);
 hipError_t launch_moe_ffn(int kind, const uint8_t *W_gu, const uint8_t *W_d, int64_t E, const int32_t *ids,
                           const float *topk_w, int64_t topk, const void *X, int x_f16, float *Y, int64_t M,
-                          int64_t N_ff, int64_t K, void *ws, hipStream_t s);
+                          int64_t N_ff, int64_t K, void *ws, hipStream_t s, bool packed = false);
 
 // MXFP4 weights on the scaled FP8 x FP4 matrix cores (activations quantized
 // to MX FP8 into `ws`, gemm_mx_workspace_bytes(M, K) bytes); K not a multiple

@@ -109,7 +109,7 @@ size_t moe_ffn_workspace_bytes(int64_t E, int64_t M, int64_t topk, int64_t N_ff,
 
 hipError_t launch_moe_ffn(int kind, const uint8_t *W_gu, const uint8_t *W_d, int64_t E, const int32_t *ids,
                           const float *topk_w, int64_t topk, const void *X, int x_f16, float *Y, int64_t M,
-                          int64_t N_ff, int64_t K, void *ws, hipStream_t s) {
+                          int64_t N_ff, int64_t K, void *ws, hipStream_t s, bool packed) {
   const FfnLayout L(E, M, topk, N_ff, K);
   uint8_t *base = static_cast<uint8_t *>(ws);
   float *G = reinterpret_cast<float *>(base + L.g);
@@ -117,11 +117,11 @@ hipError_t launch_moe_ffn(int kind, const uint8_t *W_gu, const uint8_t *W_d, int
   float *D = reinterpret_cast<float *>(base + L.d);
   float *S = reinterpret_cast<float *>(base + L.sc);
   const int64_t P = M * topk;
-  hipError_t e = launch_moe(kind, W_gu, E, ids, topk, X, x_f16, 0, G, M, 2 * N_ff, K, base + L.route, s);
+  hipError_t e = launch_moe(kind, W_gu, E, ids, topk, X, x_f16, 0, G, M, 2 * N_ff, K, base + L.route, s, packed);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)P), dim3(256), 0, s, G, H, S, (int)N_ff);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  e = launch_moe(kind, W_d, E, ids, topk, H, 0, 1, D, M, K, N_ff, base + L.route, s);
+  e = launch_moe(kind, W_d, E, ids, topk, H, 0, 1, D, M, K, N_ff, base + L.route, s, packed);
   if (e != hipSuccess) return e;
   const int64_t n2 = M * (K / 4);
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, D, S, ids, topk_w, Y, M,

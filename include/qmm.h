@@ -135,6 +135,16 @@ int qmm_moe_ffn(int kind, const void *W_gu, const void *W_d, int64_t E, const in
                 const float *topk_w, int64_t topk, const void *X, int x_dtype, float *Y,
                 int64_t M, int64_t N_ff, int64_t K, void *workspace, size_t workspace_bytes,
                 void *stream);
+/* qmm_moe_ffn over repacked experts: P_gu holds E experts' gate/up records
+ * (expert e at e * qmm_packed_bytes(kind, 2 N_ff, K)), P_d their down
+ * records (at e * qmm_packed_bytes(kind, K, N_ff)), each from qmm_repack of
+ * that expert's rows; both 16-byte aligned.  Kinds as qmm_gemv_packed; K
+ * and N_ff multiples of 256; M * topk * max(K, N_ff) below 2^31.  Semantics,
+ * numerics, workspace and the remaining errors as qmm_moe_ffn. */
+int qmm_moe_ffn_packed(int kind, const void *P_gu, const void *P_d, int64_t E, const int32_t *ids,
+                       const float *topk_w, int64_t topk, const void *X, int x_dtype, float *Y,
+                       int64_t M, int64_t N_ff, int64_t K, void *workspace, size_t workspace_bytes,
+                       void *stream);
 /* Workspace of qmm_moe_ffn: the routing words of qmm_moe plus f32 gate/up,
  * h, per-slot down outputs and per-pair scales; 0 for a non-positive
  * argument. */

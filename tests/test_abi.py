@@ -240,6 +240,19 @@ def test_moe_packed_refusals_in_order(lib):
     assert f(*args(wsb=need - 1)) == WS
 
 
+def test_moe_ffn_packed_refusals(lib):
+    f = lib.qmm_moe_ffn_packed
+    need = lib.qmm_moe_ffn_workspace_bytes(4, 2, 2, 256, 512)
+    args = lambda **k: [k.get("kind", 12), k.get("Pg", FAKE), k.get("Pd", FAKE), 4, FAKE, FAKE, 2,
+                        FAKE, 1, FAKE, k.get("M", 2), k.get("Nff", 256), k.get("K", 512), FAKE, need, None]
+    assert f(*args(Nff=0)) == EMPTY
+    assert f(*args(kind=10)) == KIND                  # Q2_K has no repacked layout
+    assert f(*args(kind=2, K=288)) == KALIGN          # K not whole k-blocks
+    assert f(*args(kind=2, Nff=288)) == KALIGN        # N_ff (the down matrix's K) not whole k-blocks
+    assert f(*args(Pg=FAKE + 8)) == ARG
+    assert f(*args(Pd=None)) == ARG
+
+
 def test_moe_ffn_refusals_in_order(lib):
     g = lib.qmm_moe_ffn
     need = lib.qmm_moe_ffn_workspace_bytes(8, 4, 2, 256, 512)

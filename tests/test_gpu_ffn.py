@@ -138,3 +138,28 @@ def test_ffn_one_expert_top1(oracle_mod):
     got = run_ffn(kind, W_gu, W_d, 1, ids, w, X, N_ff)
     y, tol = oracle_mod.moe_ffn(kind, W_gu, W_d, 1, N_ff, K, ids, w, X)
     check(got, y, tol, "E=1 top-1")
+
+
+@pytest.mark.parametrize("kind,N_ff,K", [("Q4_K", 256, 512), ("Q6_K", 512, 256), ("Q8_0", 256, 256),
+                                         ("MXFP4", 256, 512), ("IQ4_XS", 256, 256)])
+def test_ffn_packed_parity(oracle_mod, kind, N_ff, K):
+    """The FFN over repacked experts (qmm_moe_ffn_packed) against the oracle
+    over the native experts, one-pair and grouped items, a skipped slot."""
+    E, topk = 6, 3
+    g = wl.rng("gpu_ffn_packed", f"{kind}_{N_ff}_{K}")
+    W_gu = wl.random_weights(kind, E * 2 * N_ff, K, g)
+    W_d = wl.random_weights(kind, E * K, N_ff, g)
+    P_gu = qmm.repack_experts(kind, dev(W_gu), E, 2 * N_ff, K)
+    P_d = qmm.repack_experts(kind, dev(W_d), E, K, N_ff)
+    for M in (1, 5, 40):
+        ids = wl.routing(M, E, topk, g)
+        if M > 1:
+            ids[1, 2] = -1
+        w = _weights(g, M, topk)
+        X = wl.activations((M, K), np.float16, g)
+        Y = torch.full((M, K), SENTINEL, dtype=torch.float32, device="cuda")
+        ws = torch.empty(qmm.qmm_moe_ffn_workspace_bytes(E, M, topk, N_ff, K), dtype=torch.uint8, device="cuda")
+        qmm.qmm_moe_ffn_packed(kind, P_gu, P_d, E, dev(ids), dev(w), topk, dev(X), Y, M, N_ff, K, ws)
+        got = host(Y)
+        y, tol = oracle_mod.moe_ffn(kind, W_gu, W_d, E, N_ff, K, ids, w, X)
+        check(got, y, tol, f"{kind} M={M} packed")

@@ -352,7 +352,12 @@ static hipError_t run_m(const uint8_t *W, const void *x, int x_f16, float *y, in
 template <int KIND, bool PACKED>
 static hipError_t run_routed(const uint8_t *W, const void *x, int x_f16, float *y, int mt, int64_t N, int64_t K,
                              hipStream_t s, const MoeRoute &rt, int items) {
-  if (mt == 1) return run<KIND, 1, 2, 1, 2, 1, true, PACKED>(W, x, x_f16, y, 1, N, K, s, rt, items);
+  if (mt == 1) {
+    // Three k-blocks (an expert down matrix of 768 columns): one per wave
+    // rather than one and two.
+    if (K == 3 * Dec<KIND>::KB) return run<KIND, 1, 3, 1, 1, 1, true, PACKED>(W, x, x_f16, y, 1, N, K, s, rt, items);
+    return run<KIND, 1, 2, 1, 2, 1, true, PACKED>(W, x, x_f16, y, 1, N, K, s, rt, items);
+  }
   if (mt == 8) return run<KIND, 8, 2, 2, 2, 1, true, PACKED>(W, x, x_f16, y, 8, N, K, s, rt, items);
   // Sixteen pairs per item: the activation k-block staged by a wave serves
   // four 16-row tiles.

@@ -142,7 +142,13 @@ def kind_id(kind) -> int:
 # Tensor marshalling
 # ---------------------------------------------------------------------------
 def _ptr(t) -> int:
-    return 0 if t is None else int(t.data_ptr())
+    """Device address of a tensor; a host tensor is refused (the kernels
+    would fault on its address)."""
+    if t is None:
+        return 0
+    if t.device.type != "cuda":
+        raise ValueError(f"a {tuple(t.shape)} tensor is on {t.device}: the library takes device memory only")
+    return int(t.data_ptr())
 
 
 def _dtype_code(t) -> int:

@@ -338,3 +338,15 @@ def test_binding_refuses_wrong_element_types(lib):
                         None)
     with pytest.raises(TypeError, match="out must be float32"):
         qmm.qmm_dequant("Q4_0", u8, torch.zeros(32, dtype=torch.float16), 32)
+
+
+def test_binding_refuses_host_tensors(lib):
+    """Correctly typed host tensors are refused before the library is called:
+    the kernels would fault on a host address."""
+    torch = pytest.importorskip("torch")
+    u8 = torch.zeros(18 * 4, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device memory only"):
+        qmm.qmm_gemv_ex("Q4_0", u8, torch.zeros(32), torch.zeros(4), 1, 4, 32)
+    with pytest.raises(ValueError, match="device memory only"):
+        qmm.qmm_repack("Q4_K", torch.zeros(144 * 16, dtype=torch.uint8), torch.zeros(144 * 16, dtype=torch.uint8),
+                       16, 256)

@@ -5,7 +5,7 @@
 // (llama.cpp's mmq) and leaves out; here it reads repacked Q8_0 or Q4_0
 // weights (the records of qmm_repack).
 //
-// Quantization (one thread per token and block): amax = max |x|,
+// Quantization (32 lanes per token and block): amax = max |x|,
 // d = amax / 127 and each x / d rounded to f32 (both through binary64, whose
 // 53 bits make the double rounding to f32 exact for a quotient of two f32
 // values), then to the nearest integer, ties to even.  An all-zero block has
@@ -36,47 +36,49 @@ using gv::floatx4;
 using gv::u32x2;
 using gv::u32x4;
 
-// Element of block position 8G + e (the lane order of the weight codes).
+// Position of element e of a block in the lane order of the weight codes:
+// Q8_0 keeps element order (lane group G holds code bytes 8G .. 8G+7); for
+// Q4_0, position 8G + j holds element 4G + j (j < 4, the low nibbles of code
+// bytes 4G ..) and position 8G + 4 + j element 16 + 4G + j (their high
+// nibbles).
 template <int KIND>
-__device__ __forceinline__ int element_of(int pos) {
+__device__ __forceinline__ int position_of(int e) {
   if constexpr (KIND == Q8_0) {
-    return pos;  // code bytes 8G .. 8G+7
+    return e;
   } else {
-    const int G = pos >> 3, e = pos & 7;  // low nibbles 4G.., high nibbles 16 + 4G..
-    return e < 4 ? 4 * G + e : 16 + 4 * G + (e - 4);
+    const int h = e >> 4, r = e & 15;  // low nibbles (h = 0) or high nibbles (h = 1)
+    return 8 * (r >> 2) + 4 * h + (r & 3);
   }
 }
 
+// One thread per element, 32 consecutive threads per (token, block): the
+// block maximum and the code sum are reduced across the 32 lanes, so the
+// quantization takes a few steps instead of a 32-element loop per thread.
 template <int KIND, typename XT>
 __global__ __launch_bounds__(256) void quantize_kernel(const XT *__restrict__ X, int8_t *__restrict__ q,
                                                        float *__restrict__ d, int32_t *__restrict__ s,
                                                        int64_t blocks, int nb) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= blocks) return;
-  const int64_t t = i / nb, b = i - t * nb;
-  const XT *x = X + t * (int64_t)nb * 32 + 32 * b;
-  float v[32];
-  float amax = 0.f;
+  const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = gi >> 5;  // (token, block)
+  const int e = (int)(gi & 31);
+  const bool live = i < blocks;
+  const int64_t t = live ? i / nb : 0, b = live ? i - t * nb : 0;
+  const float v = live ? (float)X[t * (int64_t)nb * 32 + 32 * b + e] : 0.f;
+  float amax = fabsf(v);
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    v[e] = (float)x[e];
-    amax = fmaxf(amax, fabsf(v[e]));
-  }
+  for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
   const float db = (float)((double)amax / 127.0);
-  uint32_t w[8] = {};
-  int sum = 0;
+  const float r = db > 0.f ? (float)((double)v / (double)db) : 0.f;
+  const int c = (int)__builtin_rintf(r);
+  int sum = c;
 #pragma unroll
-  for (int p = 0; p < 32; ++p) {
-    const float r = db > 0.f ? (float)((double)v[element_of<KIND>(p)] / (double)db) : 0.f;
-    const int c = (int)__builtin_rintf(r);
-    sum += c;
-    w[p >> 2] |= (uint32_t)(c & 0xFF) << (8 * (p & 3));
+  for (int m = 16; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 32);
+  if (!live) return;
+  q[i * 32 + position_of<KIND>(e)] = (int8_t)c;
+  if (e == 0) {
+    d[i] = db;
+    s[i] = sum;
   }
-  u32x4 *dst = reinterpret_cast<u32x4 *>(q + i * 32);
-  dst[0] = u32x4{w[0], w[1], w[2], w[3]};
-  dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-  d[i] = db;
-  s[i] = sum;
 }
 
 // B operand of step c: the 8 codes of block 2c, then the 8 of block 2c+1.
@@ -250,7 +252,7 @@ hipError_t launch_gemv_i8(int kind, const uint8_t *P, const void *x, int x_f16, 
   int32_t *s = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(d) + i8::align256((size_t)M * (K / 32) * 4));
   const int nb = (int)(K / 32);
   const int64_t blocks = (int64_t)M * nb;
-  const unsigned grid = (unsigned)((blocks + 255) / 256);
+  const unsigned grid = (unsigned)((blocks * 32 + 255) / 256);
   switch (kind) {
     case Q8_0: i8::quantize<Q8_0>(x, x_f16, q, d, s, blocks, nb, grid, st); break;
     case Q4_0: i8::quantize<Q4_0>(x, x_f16, q, d, s, blocks, nb, grid, st); break;

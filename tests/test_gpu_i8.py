@@ -151,3 +151,15 @@ def test_gemv_i8_full_size_sampled(oracle_mod, kind, M):
     rows = _sample_rows(N, g)
     yq, Bq = oi.matmul_quantized(kind, W, K, X, rows=rows)
     assert_within_bound(got[:, rows], yq, Bq, f"{kind} M={M}", rtol=RTOL)
+
+
+def test_gemv_i8_largest_staged_shape(oracle_mod):
+    """M * K at its limit (8 tokens x 32768: 64 KiB of staged scales and
+    code sums per workgroup), on sampled rows."""
+    kind, M, N, K = "Q8_0", 8, 48, 32768
+    g = wl.rng("gpu_i8_max", "x")
+    W = wl.random_weights(kind, N, K, g)
+    X = wl.activations((M, K), np.float16, g)
+    got, _ = run(kind, W, X, N)
+    yq, Bq = oi.matmul_quantized(kind, W, K, X)
+    assert_within_bound(got, yq, Bq, "M*K = 262144", rtol=RTOL)

@@ -2,8 +2,9 @@
 // quantized per 32-element block to int8, weight codes multiplied as int8 on
 // the matrix cores (v_mfma_i32_16x16x64_i8), one f32 scale product per block.
 // This is the integer dot-product path that the ferrox-cuda mul_mm page names
-// (llama.cpp's mmq) and leaves out; here it reads repacked Q8_0 or Q4_0
-// weights (the records of qmm_repack).
+// (llama.cpp's mmq) and leaves out; here it reads repacked Q8_0, Q4_0, Q5_0
+// or IQ4_NL weights (the records of qmm_repack): the 32-element kinds whose
+// codes, or table values, are integers that fit in int8.
 //
 // Quantization (32 lanes per token and block): amax = max |x|,
 // d = amax / 127 and each x / d rounded to f32 (both through binary64, whose
@@ -82,14 +83,30 @@ __global__ __launch_bounds__(256) void quantize_kernel(const XT *__restrict__ X,
 }
 
 // B operand of step c: the 8 codes of block 2c, then the 8 of block 2c+1.
+// Q4_0 and Q5_0 codes enter unsigned (their bias is applied through the
+// activation code sums); IQ4_NL enters as the signed table value.
 template <int KIND>
-__device__ __forceinline__ v4i bop(const typename gv::Rec<KIND>::Packed &p, int c) {
+__device__ __forceinline__ v4i bop(const typename gv::Rec<KIND>::Packed &p, int c, int G) {
   if constexpr (KIND == Q8_0) {
     return __builtin_bit_cast(v4i, p.c[c]);
   } else {
-    const uint32_t w0 = p.c.q(2 * c), w1 = p.c.q(2 * c + 1);
-    return v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
-               (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+    uint32_t lo[2], hi[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int blk = 2 * c + h;
+      const uint32_t w = p.c.q(blk);
+      lo[h] = w & 0x0F0F0F0Fu;          // elements 4G .. 4G+3
+      hi[h] = (w >> 4) & 0x0F0F0F0Fu;   // elements 16 + 4G ..
+      if constexpr (KIND == Q5_0) {     // fifth bits: qh bits 4G.. and 16 + 4G..
+        const uint32_t qh = (blk < 4 ? p.h0[blk] : p.h1[blk - 4]) >> (4 * G);
+        lo[h] |= spread4(qh) << 4;
+        hi[h] |= spread4(qh >> 16) << 4;
+      } else if constexpr (KIND == IQ4_NL) {  // table value + 128, made signed
+        lo[h] = iq4_lookup(lo[h]) ^ 0x80808080u;
+        hi[h] = iq4_lookup(hi[h]) ^ 0x80808080u;
+      }
+    }
+    return v4i{(int)lo[0], (int)hi[0], (int)lo[1], (int)hi[1]};
   }
 }
 
@@ -101,7 +118,7 @@ __global__ __launch_bounds__(64 * S) void gemv_i8_kernel(const uint8_t *__restri
                                                         float *__restrict__ Y, int M, int64_t N, int K) {
   using Rc = gv::Rec<KIND>;
   using Packed = typename Rc::Packed;
-  constexpr int kBias = KIND == Q8_0 ? 0 : 8;
+  constexpr int kBias = KIND == Q4_0 ? 8 : KIND == Q5_0 ? 16 : 0;
   constexpr int64_t kRec = 16 * gv::Dec<KIND>::BYTES;
   extern __shared__ u32x4 lds[];
   const int nb = K / 32, nkb = K / 256;
@@ -153,7 +170,7 @@ __global__ __launch_bounds__(64 * S) void gemv_i8_kernel(const uint8_t *__restri
       for (int c = 0; c < 4; ++c) {
         const u32x2 xv = xq[d][c];
         const v4i a = pa == 0 ? v4i{(int)xv.x, (int)xv.y, 0, 0} : v4i{0, 0, (int)xv.x, (int)xv.y};
-        const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop<KIND>(raw[d], c), v4i{0, 0, 0, 0}, 0, 0, 0);
+        const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop<KIND>(raw[d], c, G), v4i{0, 0, 0, 0}, 0, 0, 0);
         const int b0 = 8 * k + 2 * c;
         // d_w of blocks 2c and 2c+1: the two halves of dword c of the scales.
         const float w0 = gv::lo_f16(dw[c]), w1 = gv::hi_f16(dw[c]);
@@ -239,7 +256,7 @@ void quantize(const void *x, int x_f16, int8_t *q, float *d, int32_t *s, int64_t
 
 }  // namespace i8
 
-bool gemv_i8_supported(int kind) { return kind == Q8_0 || kind == Q4_0; }
+bool gemv_i8_supported(int kind) { return kind == Q8_0 || kind == Q4_0 || kind == Q5_0 || kind == IQ4_NL; }
 
 size_t gemv_i8_workspace_bytes(int64_t M, int64_t K) {
   return i8::align256((size_t)M * K) + 2 * i8::align256((size_t)M * (K / 32) * 4);
@@ -253,15 +270,22 @@ hipError_t launch_gemv_i8(int kind, const uint8_t *P, const void *x, int x_f16, 
   const int nb = (int)(K / 32);
   const int64_t blocks = (int64_t)M * nb;
   const unsigned grid = (unsigned)((blocks * 32 + 255) / 256);
-  switch (kind) {
-    case Q8_0: i8::quantize<Q8_0>(x, x_f16, q, d, s, blocks, nb, grid, st); break;
-    case Q4_0: i8::quantize<Q4_0>(x, x_f16, q, d, s, blocks, nb, grid, st); break;
-    default: return hipErrorNotSupported;
-  }
+  // The quantizer's code order: Q8_0's, or the nibble order the other
+  // three kinds share.
+  if (kind == Q8_0)
+    i8::quantize<Q8_0>(x, x_f16, q, d, s, blocks, nb, grid, st);
+  else
+    i8::quantize<Q4_0>(x, x_f16, q, d, s, blocks, nb, grid, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return kind == Q8_0 ? i8::run_shape<Q8_0>(P, q, d, s, y, M, N, K, st)
-                      : i8::run_shape<Q4_0>(P, q, d, s, y, M, N, K, st);
+  switch (kind) {
+    case Q8_0: return i8::run_shape<Q8_0>(P, q, d, s, y, M, N, K, st);
+    case Q4_0: return i8::run_shape<Q4_0>(P, q, d, s, y, M, N, K, st);
+    case Q5_0: return i8::run_shape<Q5_0>(P, q, d, s, y, M, N, K, st);
+    case IQ4_NL: return i8::run_shape<IQ4_NL>(P, q, d, s, y, M, N, K, st);
+    default: break;
+  }
+  return hipErrorNotSupported;
 }
 
 }  // namespace qmm

@@ -29,9 +29,9 @@ Also printed in the same JSON line:
   cases         each of the four GEMVs alone;
   secondary     the decode step's GEMVs in the other weight layout, and the
                 other workloads (Q4_0 GEMV, prefill GEMMs, codebook kinds,
-                in both layouts where they are GEMVs, the Q4_0 GEMV with
-                int8 activations, routed experts, the scaled MXFP4 GEMM, the
-                routed expert FFN), each timed the same way.
+                in both layouts where they are GEMVs, the Q4_0 and MXFP4
+                GEMVs with int8 activations, routed experts, the scaled
+                MXFP4 GEMM, the routed expert FFN), each timed the same way.
 """
 from __future__ import annotations
 
@@ -157,10 +157,10 @@ def secondary_cases(torch, qmm, wl, layout: str = "packed"):
             qmm.qmm_gemv_packed(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
 
         cases.append(Case(w.name + "_packed", w.kind, launch, copies, w.weight_bytes, w.flops))
-    # The Q4_0 decode workload on the int8-activation path (its own
-    # tolerance; the call quantizes x, then multiplies on the int8 matrix
-    # cores, over repacked weights).
-    for w in wl.C1:
+    # The Q4_0 and MXFP4 decode workloads on the int8-activation path (its
+    # own tolerance; the call quantizes x, then multiplies on the int8
+    # matrix cores, over repacked weights).
+    for w in wl.C1 + [w for w in wl.C4 if w.kind == "MXFP4" and w.M == 1]:
         copies = packed_copies(torch, qmm, w)
         x = torch.from_numpy(w.x()).cuda()
         y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")

@@ -312,8 +312,8 @@ QMM_EXPORT int qmm_gemv_i8(int kind, const void *P, const void *x, int x_dtype, 
   int st = check_packed(kind, M, N, K);
   if (st) return st;
   if (!qmm::gemv_i8_supported(kind))
-    return fail(QMM_ERR_UNSUPPORTED_KIND, "the int8-activation GEMV takes Q8_0, Q4_0, Q5_0 or IQ4_NL weights, not kind %d",
-                kind);
+    return fail(QMM_ERR_UNSUPPORTED_KIND,
+                "the int8-activation GEMV takes Q8_0, Q4_0, Q5_0, IQ4_NL or MXFP4 weights, not kind %d", kind);
   if ((st = check_dtype(x_dtype))) return st;
   if (!P || !y) return fail(QMM_ERR_BAD_ARG, "P or y is NULL");
   if (!aligned(P, 16)) return fail(QMM_ERR_BAD_ARG, "P is not 16-byte aligned");

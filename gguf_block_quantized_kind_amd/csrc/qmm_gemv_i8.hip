@@ -3,8 +3,9 @@
 // the matrix cores (v_mfma_i32_16x16x64_i8), one f32 scale product per block.
 // This is the integer dot-product path that the ferrox-cuda mul_mm page names
 // (llama.cpp's mmq) and leaves out; here it reads repacked Q8_0, Q4_0, Q5_0
-// or IQ4_NL weights (the records of qmm_repack): the 32-element kinds whose
-// codes, or table values, are integers that fit in int8.
+// IQ4_NL or MXFP4 weights (the records of qmm_repack): the 32-element kinds
+// whose codes, table values or doubled E2M1 values are integers that fit in
+// int8.
 //
 // Quantization (32 lanes per token and block): amax = max |x|,
 // d = amax / 127 and each x / d rounded to f32 (both through binary64, whose
@@ -83,8 +84,21 @@ __global__ __launch_bounds__(256) void quantize_kernel(const XT *__restrict__ X,
 }
 
 // B operand of step c: the 8 codes of block 2c, then the 8 of block 2c+1.
+// Twice the E2M1 value of each of four 4-bit codes (one per byte), as signed
+// bytes: 0, 1, 2, 3, 4, 6, 8, 12 and their negatives (code 8, -0, gives 0).
+// Entries 0..7 and 8..15 are looked up with v_perm; bit 3 of each code picks.
+constexpr uint32_t kE2T0 = 0x03020100u, kE2T1 = 0x0C080604u, kE2T2 = 0xFDFEFF00u, kE2T3 = 0xF4F8FAFCu;
+__device__ __forceinline__ uint32_t e2m1x2_lookup(uint32_t idx) {
+  const uint32_t low3 = idx & 0x07070707u;
+  const uint32_t a = perm(kE2T1, kE2T0, low3);
+  const uint32_t b = perm(kE2T3, kE2T2, low3);
+  const uint32_t m = perm(0u, 0u, ((idx >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+  return (b & m) | (a & ~m);
+}
+
 // Q4_0 and Q5_0 codes enter unsigned (their bias is applied through the
-// activation code sums); IQ4_NL enters as the signed table value.
+// activation code sums); IQ4_NL enters as the signed table value, MXFP4 as
+// twice its E2M1 value (the block scale is halved to match).
 template <int KIND>
 __device__ __forceinline__ v4i bop(const typename gv::Rec<KIND>::Packed &p, int c, int G) {
   if constexpr (KIND == Q8_0) {
@@ -104,13 +118,28 @@ __device__ __forceinline__ v4i bop(const typename gv::Rec<KIND>::Packed &p, int 
       } else if constexpr (KIND == IQ4_NL) {  // table value + 128, made signed
         lo[h] = iq4_lookup(lo[h]) ^ 0x80808080u;
         hi[h] = iq4_lookup(hi[h]) ^ 0x80808080u;
+      } else if constexpr (KIND == MXFP4) {
+        lo[h] = e2m1x2_lookup(lo[h]);
+        hi[h] = e2m1x2_lookup(hi[h]);
       }
     }
     return v4i{(int)lo[0], (int)hi[0], (int)lo[1], (int)hi[1]};
   }
 }
 
-template <int KIND> __device__ __forceinline__ u32x4 dvec(const typename gv::Rec<KIND>::Packed &p) { return p.d; }
+// f32 scales of blocks 2c and 2c+1 of a record: the f16 d of each block, or
+// for MXFP4 2^(e-127) / 2 (its codes enter doubled).
+template <int KIND>
+__device__ __forceinline__ void block_scales(const typename gv::Rec<KIND>::Packed &p, int c, float &w0, float &w1) {
+  if constexpr (KIND == MXFP4) {
+    const uint32_t e = p.e[c >> 1] >> (16 * (c & 1));
+    w0 = e8m0_to_f32(e & 0xFFu) * 0.5f;
+    w1 = e8m0_to_f32((e >> 8) & 0xFFu) * 0.5f;
+  } else {
+    w0 = gv::lo_f16(p.d[c]);
+    w1 = gv::hi_f16(p.d[c]);
+  }
+}
 
 template <int KIND, int S, int PD>
 __global__ __launch_bounds__(64 * S) void gemv_i8_kernel(const uint8_t *__restrict__ P, const int8_t *__restrict__ q,
@@ -165,15 +194,14 @@ __global__ __launch_bounds__(64 * S) void gemv_i8_kernel(const uint8_t *__restri
       if (kb + d >= kb1) break;
       if (kb + d + PD < kb1) issue(kb + d + PD, (d + PD) % NS);
       const int k = kb + d;
-      const u32x4 dw = dvec<KIND>(raw[d]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const u32x2 xv = xq[d][c];
         const v4i a = pa == 0 ? v4i{(int)xv.x, (int)xv.y, 0, 0} : v4i{0, 0, (int)xv.x, (int)xv.y};
         const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop<KIND>(raw[d], c, G), v4i{0, 0, 0, 0}, 0, 0, 0);
         const int b0 = 8 * k + 2 * c;
-        // d_w of blocks 2c and 2c+1: the two halves of dword c of the scales.
-        const float w0 = gv::lo_f16(dw[c]), w1 = gv::hi_f16(dw[c]);
+        float w0, w1;  // d_w of blocks 2c and 2c+1
+        block_scales<KIND>(raw[d], c, w0, w1);
         const int i00 = t0 * nb + b0, i10 = t1 * nb + b0;
         acc[0] += (w0 * ldx[i00]) * (float)(D[0] - kBias * lsx[i00]);
         acc[1] += (w1 * ldx[i00 + 1]) * (float)(D[1] - kBias * lsx[i00 + 1]);
@@ -256,7 +284,9 @@ void quantize(const void *x, int x_f16, int8_t *q, float *d, int32_t *s, int64_t
 
 }  // namespace i8
 
-bool gemv_i8_supported(int kind) { return kind == Q8_0 || kind == Q4_0 || kind == Q5_0 || kind == IQ4_NL; }
+bool gemv_i8_supported(int kind) {
+  return kind == Q8_0 || kind == Q4_0 || kind == Q5_0 || kind == IQ4_NL || kind == MXFP4;
+}
 
 size_t gemv_i8_workspace_bytes(int64_t M, int64_t K) {
   return i8::align256((size_t)M * K) + 2 * i8::align256((size_t)M * (K / 32) * 4);
@@ -271,7 +301,7 @@ hipError_t launch_gemv_i8(int kind, const uint8_t *P, const void *x, int x_f16, 
   const int64_t blocks = (int64_t)M * nb;
   const unsigned grid = (unsigned)((blocks * 32 + 255) / 256);
   // The quantizer's code order: Q8_0's, or the nibble order the other
-  // three kinds share.
+  // kinds share.
   if (kind == Q8_0)
     i8::quantize<Q8_0>(x, x_f16, q, d, s, blocks, nb, grid, st);
   else
@@ -283,6 +313,7 @@ hipError_t launch_gemv_i8(int kind, const uint8_t *P, const void *x, int x_f16, 
     case Q4_0: return i8::run_shape<Q4_0>(P, q, d, s, y, M, N, K, st);
     case Q5_0: return i8::run_shape<Q5_0>(P, q, d, s, y, M, N, K, st);
     case IQ4_NL: return i8::run_shape<IQ4_NL>(P, q, d, s, y, M, N, K, st);
+    case MXFP4: return i8::run_shape<MXFP4>(P, q, d, s, y, M, N, K, st);
     default: break;
   }
   return hipErrorNotSupported;

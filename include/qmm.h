@@ -245,8 +245,9 @@ int qmm_moe_packed(int kind, const void *P, int64_t E, const int32_t *ids, int64
 #define QMM_GEMV_I8_MAX_MK 262144
 
 /* Decode GEMV with integer activations, a separately toleranced variant of
- * qmm_gemv_packed for repacked Q8_0, Q4_0, Q5_0 or IQ4_NL weights, whose
- * codes or table values are integers that fit in int8 (the integer dot-product
+ * qmm_gemv_packed for repacked Q8_0, Q4_0, Q5_0, IQ4_NL or MXFP4 weights,
+ * whose codes, table values or doubled E2M1 values are integers that fit in
+ * int8 (the integer dot-product
  * path that the ferrox-cuda mul_mm page names and leaves out).  x (f32 or
  * f16, [M][K], finite) is first quantized into `workspace`, per token and
  * 32-element block: amax = max |x|, d = amax / 127 and x / d each rounded to
@@ -254,14 +255,15 @@ int qmm_moe_packed(int kind, const void *P, int64_t E, const int32_t *ids, int64
  * ties to even (|q| <= 127); an all-zero block has d = 0.  Then
  *   y[t][n] = sum over blocks b of d_w[n][b] d[t][b] (sum_i w_i q_i)
  * with each block's integer dot product exact (Q4_0 as code - 8, Q5_0 as
- * code - 16, IQ4_NL as the table value) and the scaling and accumulation in
+ * code - 16, IQ4_NL as the table value, MXFP4 as twice its E2M1 value with
+ * half the block scale) and the scaling and accumulation in
  * f32: for K <= 32768, y is within 2e-5 * sum |w| |d q| + 1e-6 of the exact
  * product with the rebuilt activations d q (the f32 accumulation adds about
  * K * 2^-31 of that sum beyond), and those lie within d / 2 of x.
  * Workspace (qmm_gemv_i8_workspace_bytes(M, K) bytes, 256-byte aligned,
  * overwritten; calls sharing it must not overlap): the codes [M][K] int8,
  * each block's 32 codes in the lane order of the weight codes (Q8_0: element
- * order; Q4_0, Q5_0, IQ4_NL: position 8G + e holds element 4G + e for e < 4
+ * order; the others: position 8G + e holds element 4G + e for e < 4
  * and 16 + 4G + e - 4 otherwise, G = 0..3); at the next multiple of 256
  * bytes the scales d [M][K/32] f32; at the next, the code sums [M][K/32]
  * int32.  1 <= M <= QMM_GEMV_MAX_M and M * K <= QMM_GEMV_I8_MAX_MK.  Errors:

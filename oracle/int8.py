@@ -10,8 +10,8 @@ path of llama.cpp's mmq (activations quantized to 8-bit integers, products on
 integer dot units) and leaves it out.  The pages give no activation format
 for it, so the plainest reading is taken:
 
-* per token and 32-element block (the weight block of Q8_0, Q4_0, Q5_0 and
-  IQ4_NL, whose codes or table values are integers),
+* per token and 32-element block (the weight block of Q8_0, Q4_0, Q5_0,
+  IQ4_NL and MXFP4, whose values are integers up to the block scale),
   amax = max |x|, the scale d = amax / 127 rounded to f32, and each code
   q = x / d rounded to f32, then to the nearest integer, ties to even;
   an all-zero block has d = 0 and q = 0;

@@ -205,7 +205,7 @@ def test_gemv_i8_refusals_in_order(lib):
     assert g(8, FAKE, FAKE, 0, FAKE, 0, 16, 512, FAKE, need, None) == EMPTY
     assert g(10, FAKE, FAKE, 0, FAKE, 3, 16, 512, FAKE, need, None) == KIND    # Q2_K: no repacked layout
     assert g(12, FAKE, FAKE, 0, FAKE, 3, 16, 512, FAKE, need, None) == KIND    # Q4_K: not an integer-code kind
-    assert "Q5_0 or IQ4_NL" in qmm.qmm_last_error()
+    assert "IQ4_NL or MXFP4" in qmm.qmm_last_error()
     assert g(8, FAKE, FAKE, 0, FAKE, 3, 16, 288, FAKE, need, None) == KALIGN
     assert g(8, FAKE, FAKE, 2, FAKE, 3, 16, 512, FAKE, need, None) == DTYPE
     assert g(8, None, FAKE, 0, FAKE, 3, 16, 512, FAKE, need, None) == ARG

@@ -23,7 +23,7 @@ from oracle import int8 as oi  # noqa: E402
 
 from test_gpu_parity import SENTINEL, assert_within_bound, dev, filled, host, _sample_rows  # noqa: E402
 
-KINDS = ["Q8_0", "Q4_0", "Q5_0", "IQ4_NL"]
+KINDS = ["Q8_0", "Q4_0", "Q5_0", "IQ4_NL", "MXFP4"]
 RTOL = 2e-5
 
 
@@ -35,8 +35,8 @@ def _gpu():
 
 
 def lane_order(kind):
-    """Element held at block position 8G + e (Q5_0 and IQ4_NL share Q4_0's
-    nibble order)."""
+    """Element held at block position 8G + e (Q5_0, IQ4_NL and MXFP4 share
+    Q4_0's nibble order)."""
     if kind == "Q8_0":
         return np.arange(32)
     return np.array([4 * G + e if e < 4 else 16 + 4 * G + e - 4 for G in range(4) for e in range(8)])

@@ -171,3 +171,16 @@ def test_moe_packed_full_size_sampled(oracle_mod, e):
     rows = _sample_rows(e.N_gu, wl.rng(e.name, "sample_moe_packed"), n=24)
     Yr, Br = oracle_mod.moe(e.kind, W, e.E, e.N_gu, e.K_gu, ids, X, False, rows=rows)
     assert_within_bound(got[:, :, rows], Yr, Br, e.name)
+
+
+@pytest.mark.parametrize("kind", ["MXFP4", "Q6_K", "Q5_0"])
+def test_repack_reads_byte_aligned_weights(kind):
+    """W may sit at any byte offset (17-, 22- and 210-byte blocks make odd
+    offsets normal): the repack of W one byte into a buffer equals the
+    oracle's repack."""
+    N, K = 33, 512
+    W = wl.random_weights(kind, N, K, wl.rng("gpu_repack_odd", kind)).reshape(-1)
+    buf = torch.zeros(W.size + 1, dtype=torch.uint8, device="cuda")
+    buf[1:] = dev(W)
+    got = host(packed(kind, buf[1:], N, K))
+    assert np.array_equal(got, rp.repack(kind, W, N, K))

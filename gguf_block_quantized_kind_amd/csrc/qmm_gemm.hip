@@ -295,6 +295,12 @@ static hipError_t run_m(const uint8_t *W, const void *A, int a_f16, float *C, in
 
 hipError_t launch_gemm(int kind, const uint8_t *W, const void *A, int a_f16, float *C, int64_t M,
                        int64_t N, int64_t K, hipStream_t s) {
+  if (gemm_ks_supported(kind, M, N, K, a_f16)) return launch_gemm_ks(kind, W, A, a_f16, C, M, N, K, s);
+  return launch_gemm_lds(kind, W, A, a_f16, C, M, N, K, s);
+}
+
+hipError_t launch_gemm_lds(int kind, const uint8_t *W, const void *A, int a_f16, float *C, int64_t M,
+                           int64_t N, int64_t K, hipStream_t s) {
   // Launch shapes are fixed by the rules in run_m.  A tuning build
   // (-DQMM_TUNING) can pick an alternative shape from QMM_GEMM_CFG.
 #ifdef QMM_TUNING

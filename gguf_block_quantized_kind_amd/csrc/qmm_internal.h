@@ -37,7 +37,14 @@ size_t gemv_i8_workspace_bytes(int64_t M, int64_t K);
 hipError_t launch_gemv_i8(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
                           int64_t K, void *ws, hipStream_t s);
 
-// C[M][N] = A[M][K] . W^T, any M >= 1, A f32 (a_f16 == 0) or f16.
+// C[M][N] = A[M][K] . W^T, any M >= 1, A f32 (a_f16 == 0) or f16.  Runs
+// the wave-private GEMM (qmm_gemm_ks.hip) where gemm_ks_supported, else the
+// LDS-tiled GEMM (qmm_gemm.hip, launch_gemm_lds).
+bool gemm_ks_supported(int kind, int64_t M, int64_t N, int64_t K, int a_f16);
+hipError_t launch_gemm_ks(int kind, const uint8_t *W, const void *A, int a_f16, float *C, int64_t M, int64_t N,
+                          int64_t K, hipStream_t s);
+hipError_t launch_gemm_lds(int kind, const uint8_t *W, const void *A, int a_f16, float *C, int64_t M, int64_t N,
+                           int64_t K, hipStream_t s);
 hipError_t launch_gemm(int kind, const uint8_t *W, const void *A, int a_f16, float *C,
                        int64_t M, int64_t N, int64_t K, hipStream_t s);
 

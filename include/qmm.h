@@ -93,6 +93,10 @@ enum qmm_status {
 int qmm_gemv(int kind, const void *W, const float *x, float *y, int64_t N, int64_t K);
 
 /* Decode GEMV, 1 <= M <= QMM_GEMV_MAX_M tokens, f32 or f16 x, on `stream`.
+ * The few-token product below the GEMM threshold of ferrox-cuda mul_mm.rs
+ * (worth_a_gemm: a batch that small stays on the matvec arm) and the
+ * one-row-per-output decode matvec of inferencelayer cublas_prefill.rs (the
+ * q4_0 GEMV family, y[row] = sum over blocks of scale * code . x).
  * Every weight is decoded exactly; f32 x may be rounded once to f16;
  * products accumulate in f32. */
 int qmm_gemv_ex(int kind, const void *W, const void *x, int x_dtype, float *y,
@@ -106,11 +110,18 @@ int qmm_gemv_ex(int kind, const void *W, const void *x, int x_dtype, float *y,
  * weight exact instead. */
 int qmm_gemm(int kind, const void *W, const void *A, float *C, int64_t M, int64_t N, int64_t K);
 
-/* Prefill GEMM for any M >= 1 with f32 or f16 A, on `stream`. */
+/* Prefill GEMM for any M >= 1 with f32 or f16 A, on `stream`: the same
+ * contract (inferencelayer cublas_prefill.rs, CublasPrefill::gemm: y = x . W^T,
+ * beta 0, f32 accumulate), and ferrox-cuda mul_mm.rs's batched product
+ * (BODY_SRC: every token of the batch against every row, dst[token * n_rows
+ * + row]).  f32 A is split into two f16 parts (see Numerics above). */
 int qmm_gemm_ex(int kind, const void *W, const void *A, int a_dtype, float *C,
                 int64_t M, int64_t N, int64_t K, void *stream);
 
-/* Either path: the GEMV for M <= QMM_GEMV_MAX_M, the GEMM above. */
+/* Either path, chosen by the number of tokens as ferrox-cuda mul_mm.rs
+ * worth_a_gemm chooses between its matvec arm and its GEMM: the GEMV for
+ * M <= QMM_GEMV_MAX_M, the GEMM above.  Numerics and errors as the path
+ * taken. */
 int qmm_matmul(int kind, const void *W, const void *A, int a_dtype, float *C,
                int64_t M, int64_t N, int64_t K, void *stream);
 
@@ -179,7 +190,13 @@ int qmm_gemm_mx(int kind, const void *W, const void *A, int a_dtype, float *C,
 size_t qmm_gemm_mx_workspace_bytes(int64_t M, int64_t K);
 
 /* Routed expert products, every expert in one grouped launch (plus a small
- * routing prologue when an expert may receive several pairs).  W holds E experts of N rows each, back to back: expert
+ * routing prologue when an expert may receive several pairs).  No page
+ * defines this operation: the pages name expert routing only as model
+ * context (ferrox-cuda 0.20.0 codebook.rs, the MXFP4 row: gpt-oss expert
+ * weights; inferencelayer cublas_prefill.rs, the Qwen3-30B-A3B decode
+ * estimate).  It is the batched/expert product of a 128-expert top-8
+ * mixture with per-pair semantics and nothing more (no gating weights, no
+ * combine).  W holds E experts of N rows each, back to back: expert
  * e's row n starts at byte (e * N + n) * qmm_row_bytes(kind, K).
  * ids is [M][topk] int32 in [0, E).  For token t and slot s with
  * e = ids[t][s]:  Y[t][s][:] = W_e . x, where x is X[t] when x_per_slot is 0
@@ -278,15 +295,31 @@ int qmm_gemv_i8(int kind, const void *P, const void *x, int x_dtype, float *y,
 size_t qmm_gemv_i8_workspace_bytes(int64_t M, int64_t K);
 
 /* Dequantize n_elems consecutive elements (whole blocks) of W to f32 on
- * `stream`.  Every value is the f32 rounding of the exact value, evaluated
- * scale first with IEEE signed zeros (so MXFP4 code 8 gives -0.0). */
+ * `stream`: the GPU dequantization that redgpu/Vulkore quant_test.cpp checks
+ * bit for bit against its CPU references (its dequant_q8_0 / _q5_0 / _q4_k /
+ * _q6_k kernels, the per-kind dequant test), and ferrox-cuda mul_mm.rs's
+ * dequant_twin, one block's elements to f32 by the kind's rule.  Every value
+ * is the f32 rounding of the exact value, evaluated scale first with IEEE
+ * signed zeros (so MXFP4 code 8 gives -0.0; codebook.rs, the E2M1 table).
+ * Errors: as qmm_gemv_ex's kind check, then n_elems not a whole number of
+ * blocks (QMM_ERR_K_NOT_BLOCK_ALIGNED), NULL pointers (QMM_ERR_BAD_ARG). */
 int qmm_dequant(int kind, const void *W, float *out, int64_t n_elems, void *stream);
 
-/* Geometry and names. */
-int64_t qmm_row_bytes(int kind, int64_t K);  /* -1: bad kind or K not block-aligned */
-int qmm_block_geometry(int kind, int *block_bytes, int *block_elems);  /* QMM_OK or error */
-int qmm_kind_from_name(const char *gguf_name); /* -1 if the name is not one of the eleven */
-const char *qmm_kind_name(int kind);           /* NULL for an unsupported kind */
+/* Geometry and names.  qmm_row_bytes is the expected row length of
+ * ferrox-cuda mul_mm.rs validate_shape ((K / block_elems) * block_bytes),
+ * -1 for a bad kind or K not a whole number of blocks.  qmm_block_geometry
+ * gives a kind's block_bytes and block_elems, the two geometry columns of
+ * mul_mm.rs's KINDS rows (QMM_OK, or QMM_ERR_UNSUPPORTED_KIND with the
+ * outputs untouched).  qmm_kind_from_name is mul_mm.rs's kind_by_name over
+ * the GGUF quant names ("Q4_0", "MXFP4", ...): -1 where kind_by_name gives
+ * None, so a caller must fall back and say so.  qmm_kind_name is its
+ * inverse (NULL for an unsupported kind).  qmm_status_string names a
+ * status; qmm_last_error gives the calling thread's most recent message
+ * (the refused check, in the order of validate_shape, or the HIP error). */
+int64_t qmm_row_bytes(int kind, int64_t K);
+int qmm_block_geometry(int kind, int *block_bytes, int *block_elems);
+int qmm_kind_from_name(const char *gguf_name);
+const char *qmm_kind_name(int kind);
 const char *qmm_status_string(int status);
 const char *qmm_last_error(void);
 

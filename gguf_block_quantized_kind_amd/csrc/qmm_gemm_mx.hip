@@ -6,12 +6,18 @@
 // tile holds weight row j, k = 32G .. 32G+31 -- exactly one MXFP4 block,
 // whose 16 code bytes are the FP4 B operand and whose E8M0 byte is the
 // lane's B scale.  The activations are quantized once, before the GEMM,
-// to MX FP8: per row and 32-element block, the shared E8M0 scale is the
-// smallest power of two 2^e with max |a| / 2^e <= 448 (E4M3's largest
-// value), so no element saturates, and each element is a / 2^e rounded to
-// E4M3 (nearest even).  That quantization is the variant's only rounding
-// besides the f32 accumulation; elements that are small integers times one
-// power of two per block (|a| <= 16 * 2^p) come through exactly.
+// to two MX FP8 terms per row and 32-element block:
+//   hi = E4M3(a / 2^e1), 2^e1 the smallest power of two with
+//        max |a| / 2^e1 <= 448 (E4M3's largest value), so no element
+//        saturates;
+//   lo = E4M3(r / 2^e2) of the residual r = a - 2^e1 hi, on the scale of the
+//        block's residuals,
+// each rounded to nearest, ties to even, and each matrix-core step runs
+// twice, on hi and on lo, into the same accumulator.  The scalings and the
+// residual are exact in f32, so the two E4M3 roundings are the only ones
+// besides the f32 accumulation: |a - 2^e1 hi - 2^e2 lo| <= 2^-8 |a| (plus
+// 2^(e1 - 14) where hi is subnormal).  A single term would lose up to 2^-4
+// of |a| (a block of 1.0625s rounds 5.9 % low).
 //
 // Operand layout of one 16 x 16 x 128 step (k counted within the step):
 //   B (FP4, 4 registers): lane (j, G) holds column j, k = 32G + p in nibble p
@@ -50,27 +56,62 @@ constexpr int kTNSmall = 2;
 constexpr int kKS = 128;  // k per matrix-core step
 constexpr int kPD = 3;    // loads run this many steps ahead
 
-// Workspace: FP8 codes [Mp][K] bytes, then E8M0 scales [Mp][K / 32] bytes.
+// Workspace: hi codes [Mp][K], lo codes [Mp][K], hi scales [Mp][K / 32], lo
+// scales [Mp][K / 32], all bytes.
 struct Layout {
   int64_t Mp, K;
   Layout(int64_t M, int64_t K_) : Mp((M + kBM - 1) / kBM * kBM), K(K_) {}
-  int64_t scales() const { return Mp * K; }
-  int64_t bytes() const { return Mp * K + Mp * (K / 32); }
+  int64_t lo_codes() const { return Mp * K; }
+  int64_t scales() const { return 2 * Mp * K; }
+  int64_t lo_scales() const { return 2 * Mp * K + Mp * (K / 32); }
+  int64_t bytes() const { return 2 * (Mp * K + Mp * (K / 32)); }
 };
 
 // Element of a 32-element block stored at position p (nibble p of the weights).
 __device__ __forceinline__ int src_of(int p) { return (p & 1) ? 16 + (p >> 1) : (p >> 1); }
 
+// The E8M0 exponent of a block whose largest magnitude is amax: the
+// smallest e with amax / 2^e <= 448, clamped to [-127, 127]; -127 for zero.
+// amax = f * 2^x with f in [0.5, 1): 2^(x - 9) brings amax to [256, 512),
+// one more step when that exceeds 448 (f > 0.875).
+__device__ __forceinline__ int mx_exponent(float amax) {
+  int e = -127;
+  if (amax > 0.f) {
+    const int x = __builtin_amdgcn_frexp_expf(amax);
+    e = x - 9 + (__builtin_amdgcn_frexp_mantf(amax) > 0.875f ? 1 : 0);
+  }
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Eight E4M3 codes per pair of words: v[i] / 2^e, clamped to +-448, each
+// rounded to nearest even (the hardware conversion); the codes of elements
+// src_of(4w + q) go to byte q of word w.
+__device__ __forceinline__ void mx_encode(const float (&v)[32], int e, uint32_t (&out)[8]) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float s[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] = fminf(fmaxf(__builtin_amdgcn_ldexpf(v[src_of(4 * w + q)], -e), -448.f), 448.f);
+    uint32_t packed = 0u;
+    packed = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], (int)packed, false);
+    packed = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], (int)packed, true);
+    out[w] = packed;
+  }
+}
+
+// One thread per (row, block): both terms' codes and scale bytes.
 template <typename AT>
 __global__ __launch_bounds__(256) void quantize_kernel(const AT *__restrict__ A, int M, int64_t Mp, int K,
-                                                       uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+                                                       uint8_t *__restrict__ codes_hi, uint8_t *__restrict__ codes_lo,
+                                                       uint8_t *__restrict__ scales_hi,
+                                                       uint8_t *__restrict__ scales_lo) {
   const int nb = K / 32;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, block)
   if (id >= Mp * nb) return;
   const int64_t m = id / nb;
   const int b = (int)(id % nb);
-  uint32_t out[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  uint32_t sbyte = 0u;  // rows past M: zero codes under the smallest scale
+  uint32_t hi[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u}, lo[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  int e1 = -127, e2 = -127;  // rows past M: zero codes under the smallest scale
   if (m < M) {
     float a[32];
     const AT *src = A + m * K + 32 * b;
@@ -79,45 +120,46 @@ __global__ __launch_bounds__(256) void quantize_kernel(const AT *__restrict__ A,
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(a[i]));
-    // amax = f * 2^x with f in [0.5, 1): 2^(x - 9) brings amax to [256, 512),
-    // one more step when that exceeds 448 (f > 0.875).
-    int e = -127;
-    if (amax > 0.f) {
-      const int x = __builtin_amdgcn_frexp_expf(amax);
-      e = x - 9 + (__builtin_amdgcn_frexp_mantf(amax) > 0.875f ? 1 : 0);
-    }
-    e = e < -127 ? -127 : (e > 127 ? 127 : e);
-    sbyte = (uint32_t)(e + 127);
+    e1 = mx_exponent(amax);
+    mx_encode(a, e1, hi);
+    // Residuals: a - 2^e1 * E4M3 value, exact in f32.
+    float r[32];
+    float rmax = 0.f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-      float v[4];
+      const float d[4] = {__builtin_amdgcn_cvt_f32_fp8((int)hi[w], 0), __builtin_amdgcn_cvt_f32_fp8((int)hi[w], 1),
+                          __builtin_amdgcn_cvt_f32_fp8((int)hi[w], 2), __builtin_amdgcn_cvt_f32_fp8((int)hi[w], 3)};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float s = __builtin_amdgcn_ldexpf(a[src_of(4 * w + q)], -e);
-        v[q] = fminf(fmaxf(s, -448.f), 448.f);
+        const int i = src_of(4 * w + q);
+        r[i] = a[i] - __builtin_amdgcn_ldexpf(d[q], e1);
+        rmax = fmaxf(rmax, fabsf(r[i]));
       }
-      uint32_t packed = 0u;
-      packed = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], (int)packed, false);
-      packed = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], (int)packed, true);
-      out[w] = packed;
     }
+    e2 = mx_exponent(rmax);
+    mx_encode(r, e2, lo);
   }
-  u32x4 *dst = reinterpret_cast<u32x4 *>(codes + m * K + 32 * b);
-  dst[0] = u32x4{out[0], out[1], out[2], out[3]};
-  dst[1] = u32x4{out[4], out[5], out[6], out[7]};
-  scales[m * nb + b] = (uint8_t)sbyte;
+  u32x4 *dh = reinterpret_cast<u32x4 *>(codes_hi + m * K + 32 * b);
+  dh[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  dh[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+  u32x4 *dl = reinterpret_cast<u32x4 *>(codes_lo + m * K + 32 * b);
+  dl[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  dl[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
+  scales_hi[m * nb + b] = (uint8_t)(e1 + 127);
+  scales_lo[m * nb + b] = (uint8_t)(e2 + 127);
 }
 
 // One workgroup: 64 tokens x 64 TN weight rows; wave w owns rows
 // 16 TN w .. 16 TN (w + 1) - 1 (TN 16-row tiles) against all 64 tokens (four
-// 16-token tiles), 4 TN scaled matrix-core steps per 128-k step.
+// 16-token tiles), 8 TN scaled matrix-core steps per 128-k step (4 TN on
+// the first activation term, then 4 TN on the second).
 //
 // Loads.  Per step a row contributes four blocks, a 68-byte span starting at
 // a multiple of 4; the wave fetches each of its rows' spans as the five
 // aligned 16-byte chunks that cover it (80 TN chunks, adjacent lanes on
 // adjacent chunks; the last lanes repeat the last chunk when 64 does not
 // divide them), and each thread fetches its share of the
-// tokens' FP8 codes and scales.  Everything is loaded PD steps ahead into a
+// tokens' FP8 codes and scales of both terms.  Everything is loaded PD steps ahead into a
 // ring of PD + 1 register slots and written to LDS one step ahead of use:
 // activations to a shared tile, weight chunks to a wave-private copy from
 // which each lane picks its 17-byte block at any byte offset.  Load
@@ -134,8 +176,9 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
   constexpr int kChunks = 5;                    // 16-byte chunks per row and step
   constexpr int kWave = 16 * TN * kChunks;      // chunks per wave and step
   constexpr int LC = (kWave + 63) / 64;         // per lane
-  __shared__ u32x4 a_lds[2][kBM * 8];  // token t, 16-byte chunk c at t * 8 + (c ^ (t & 7))
-  __shared__ uint32_t s_lds[2][kBM];   // token t: the four E8M0 bytes of the step
+  // Term h, token t, 16-byte chunk c at [h][t * 8 + (c ^ (t & 7))].
+  __shared__ u32x4 a_lds[2][2][kBM * 8];
+  __shared__ uint32_t s_lds[2][2 * kBM];  // term h, token t: the step's four E8M0 bytes at h * 64 + t
   // Wave w, row r, chunk q at [w][5r + q]; one spare chunk past the end (a
   // block read at the very end of a row window touches one dword beyond it).
   __shared__ u32x4 b_lds[2][4 * kWave + 1];
@@ -168,18 +211,24 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
   int rs16[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) rs16[tn] = (int)(row_start(16 * tn + j) & 15);
-  // This thread's share of a step's activation tile: token at, chunks ac, ac + 1.
+  // This thread's share of a step's activation tiles: token at, chunks ac,
+  // ac + 1 of both terms (the second term's codes one plane of Mp K bytes
+  // further), and the scale word of token tid % 64, term tid / 64 % 2.
+  const int64_t Mp = (int64_t)m_tiles * kBM;
   const int at = tid >> 2, ac = 2 * (tid & 3);
   const uint8_t *asrc = codes + (m0 + at) * K + 16 * ac;
-  const uint8_t *ssrc = scales + (m0 + (tid & 63)) * nb;
+  const int64_t lo_plane = Mp * K;
+  const uint8_t *ssrc = scales + ((tid >> 6) & 1) * (Mp * nb) + (m0 + (tid & 63)) * nb;
 
-  u32x4 areg[NS][2];
+  u32x4 areg[NS][4];
   uint32_t sreg[NS];
   u32x4 breg[NS][LC];
   auto load = [&](int st, int slot) {
     st = st < steps ? st : steps - 1;
     areg[slot][0] = *reinterpret_cast<const u32x4 *>(asrc + (int64_t)st * kKS);
     areg[slot][1] = *reinterpret_cast<const u32x4 *>(asrc + (int64_t)st * kKS + 16);
+    areg[slot][2] = *reinterpret_cast<const u32x4 *>(asrc + lo_plane + (int64_t)st * kKS);
+    areg[slot][3] = *reinterpret_cast<const u32x4 *>(asrc + lo_plane + (int64_t)st * kKS + 16);
     sreg[slot] = *reinterpret_cast<const uint32_t *>(ssrc + 4 * st);
 #pragma unroll
     for (int i = 0; i < LC; ++i) {
@@ -190,12 +239,15 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
     }
   };
   auto store = [&](int slot, int buf) {
-    a_lds[buf][at * 8 + (ac ^ (at & 7))] = areg[slot][0];
-    a_lds[buf][at * 8 + ((ac + 1) ^ (at & 7))] = areg[slot][1];
-    // Four threads load each token's scale word; all four store the same
-    // value, which keeps the step free of branches (a branch here lets the
-    // compiler sink the matrix-core chain past the later steps' barriers).
-    s_lds[buf][tid & (kBM - 1)] = sreg[slot];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      a_lds[buf][h][at * 8 + (ac ^ (at & 7))] = areg[slot][2 * h];
+      a_lds[buf][h][at * 8 + ((ac + 1) ^ (at & 7))] = areg[slot][2 * h + 1];
+    }
+    // Two threads load each scale word; both store the same value, which
+    // keeps the step free of branches (a branch here lets the compiler sink
+    // the matrix-core chain past the later steps' barriers).
+    s_lds[buf][tid & (2 * kBM - 1)] = sreg[slot];
 #pragma unroll
     for (int i = 0; i < LC; ++i) b_lds[buf][wave * kWave + min(lane + 64 * i, kWave - 1)] = breg[slot][i];
   };
@@ -205,6 +257,29 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
   for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // The step's products from this lane's weight blocks: the first term of
+  // all four token tiles, then the second, so that 4 TN products separate
+  // two that update one accumulator.
+  auto products = [&](const uint32_t (&bq)[TN][4], const uint32_t (&be)[TN], int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm) {
+        const int t = 16 * tm + j;
+        const u32x4 c0 = a_lds[buf][h][t * 8 + (G ^ (t & 7))];
+        const u32x4 c1 = a_lds[buf][h][t * 8 + ((G + 4) ^ (t & 7))];
+        const v8i af = v8i{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+        const int sa = (int)((s_lds[buf][h * kBM + t] >> (8 * G)) & 0xFFu);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const v8i bf = v8i{(int)bq[tn][0], (int)bq[tn][1], (int)bq[tn][2], (int)bq[tn][3], 0, 0, 0, 0};
+          // Format codes: 0 = FP8 E4M3 (A), 4 = FP4 E2M1 (B); scales are E8M0.
+          acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[tm][tn], 0, 4, 0, sa, 0,
+                                                                         (int)be[tn]);
+        }
+      }
+  };
 
   auto compute = [&](int st, int buf) {
     // This lane's weight block of each tile: E8M0 byte and 16 code bytes at
@@ -224,21 +299,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
       for (int i = 0; i < 4; ++i)
         bq[tn][i] = (uint32_t)((((uint64_t)w[i + 1] << 32) | w[i]) >> (sh + 8));
     }
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-      const int t = 16 * tm + j;
-      const u32x4 lo = a_lds[buf][t * 8 + (G ^ (t & 7))];
-      const u32x4 hi = a_lds[buf][t * 8 + ((G + 4) ^ (t & 7))];
-      const v8i af = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      const int sa = (int)((s_lds[buf][t] >> (8 * G)) & 0xFFu);
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const v8i bf = v8i{(int)bq[tn][0], (int)bq[tn][1], (int)bq[tn][2], (int)bq[tn][3], 0, 0, 0, 0};
-        // Format codes: 0 = FP8 E4M3 (A), 4 = FP4 E2M1 (B); scales are E8M0.
-        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[tm][tn], 0, 4, 0, sa, 0,
-                                                                       (int)be[tn]);
-      }
-    }
+    products(bq, be, buf);
   };
   // The same step when every row starts on a 16-byte boundary (row_bytes a
   // multiple of 16, i.e. K a multiple of 512) and st0 is a multiple of 4:
@@ -263,20 +324,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
 #pragma unroll
       for (int i = 0; i < 4; ++i) bq[tn][i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], bsh);
     }
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-      const int t = 16 * tm + j;
-      const u32x4 lo = a_lds[buf][t * 8 + (G ^ (t & 7))];
-      const u32x4 hi = a_lds[buf][t * 8 + ((G + 4) ^ (t & 7))];
-      const v8i af = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      const int sa = (int)((s_lds[buf][t] >> (8 * G)) & 0xFFu);
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const v8i bf = v8i{(int)bq[tn][0], (int)bq[tn][1], (int)bq[tn][2], (int)bq[tn][3], 0, 0, 0, 0};
-        acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[tm][tn], 0, 4, 0, sa, 0,
-                                                                       (int)be[tn]);
-      }
-    }
+    products(bq, be, buf);
   };
   // Loads of step st0 + PD + u for that case: pointers advance once per
   // group of U steps; within the group every offset is an immediate.
@@ -285,6 +333,8 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
     const uint8_t *ag = asrc + sp * kKS + u * kKS;
     areg[slot][0] = *reinterpret_cast<const u32x4 *>(ag);
     areg[slot][1] = *reinterpret_cast<const u32x4 *>(ag + 16);
+    areg[slot][2] = *reinterpret_cast<const u32x4 *>(ag + lo_plane);
+    areg[slot][3] = *reinterpret_cast<const u32x4 *>(ag + lo_plane + 16);
     sreg[slot] = *reinterpret_cast<const uint32_t *>(ssrc + 4 * sp + 4 * u);
     const int delta = 16 * ((68 * (PD + u)) >> 4);
 #pragma unroll
@@ -355,14 +405,15 @@ hipError_t launch_gemm_mx(const uint8_t *W, const void *A, int a_f16, float *C, 
   if (K % mx::kKS != 0) return launch_gemm(MXFP4, W, A, a_f16, C, M, N, K, s);
   const mx::Layout L(M, K);
   uint8_t *codes = static_cast<uint8_t *>(ws), *scales = codes + L.scales();
+  uint8_t *codes_lo = codes + L.lo_codes(), *scales_lo = codes + L.lo_scales();
   const int64_t blocks = L.Mp * (K / 32);
   const dim3 qgrid((unsigned)((blocks + 255) / 256)), block(256);
   if (a_f16)
     hipLaunchKernelGGL(mx::quantize_kernel<_Float16>, qgrid, block, 0, s, (const _Float16 *)A, (int)M, L.Mp,
-                       (int)K, codes, scales);
+                       (int)K, codes, codes_lo, scales, scales_lo);
   else
     hipLaunchKernelGGL(mx::quantize_kernel<float>, qgrid, block, 0, s, (const float *)A, (int)M, L.Mp, (int)K,
-                       codes, scales);
+                       codes, codes_lo, scales, scales_lo);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t row_bytes = (K / 32) * 17;

@@ -168,13 +168,20 @@ size_t qmm_moe_ffn_workspace_bytes(int64_t E, int64_t M, int64_t topk, int64_t N
  * 16-byte aligned, and its rows are fetched as aligned 16-byte pieces, so the
  * last piece may cover up to 12 bytes past the end of W (never past its
  * 16-byte granule, hence never onto another page).  A (f32 or f16,
- * [M][K]) is first quantized into `workspace` to MX FP8: per row and
- * 32-element block, a power-of-two scale 2^e, the smallest with
- * max|a| / 2^e <= 448, and each a / 2^e rounded to E4M3, nearest even.  That
- * rounding (relative error at most 2^-4 per element, so
- * |C - exact| <= 2^-4 . sum|w||a| plus f32 accumulation) is the only
- * difference from the exact product; blocks whose elements are integers of
- * magnitude <= 16 times one power of two come through exactly.
+ * [M][K]) is first quantized into `workspace` to two MX FP8 terms: per row
+ * and 32-element block, hi = E4M3(a / 2^e1) with 2^e1 the smallest power of
+ * two with max|a| / 2^e1 <= 448, and lo = E4M3(r / 2^e2) of the residual
+ * r = a - 2^e1 hi on its own such scale, both rounded to nearest even; the
+ * matrix cores multiply both terms by the weights into one f32 sum.  The
+ * two roundings (|a - 2^e1 hi - 2^e2 lo| <= 2^-8 |a|, plus 2^(e1 - 14) where
+ * hi is subnormal) are the only difference from the exact product besides
+ * f32 accumulation, so |C - exact| <= about 2^-8 . sum|w||a|; blocks whose
+ * elements are E4M3 values times one power of two come through exactly.
+ * Workspace layout (bytes; Mp = M rounded up to 64, rows past M are zero
+ * codes with scale byte 0): hi codes [Mp][K], lo codes [Mp][K], hi scale
+ * bytes e1 + 127 [Mp][K/32], lo scale bytes e2 + 127 [Mp][K/32]; within
+ * each 32-element block the code at position p is element p / 2 (p even)
+ * or 16 + p / 2 (p odd), the order of the MXFP4 nibbles.
  * K a multiple of 128 runs the scaled path; any other K runs qmm_gemm_ex's
  * f16 GEMM.  workspace is device memory of at least
  * qmm_gemm_mx_workspace_bytes(M, K) bytes at 16-byte alignment, overwritten by
@@ -185,8 +192,8 @@ size_t qmm_moe_ffn_workspace_bytes(int64_t E, int64_t M, int64_t topk, int64_t N
 int qmm_gemm_mx(int kind, const void *W, const void *A, int a_dtype, float *C,
                 int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
                 void *stream);
-/* Bytes of workspace qmm_gemm_mx needs: M rounded up to 64, times K * 33 / 32;
- * 0 for M <= 0, K <= 0 or K not a multiple of 32. */
+/* Bytes of workspace qmm_gemm_mx needs: M rounded up to 64, times
+ * 2 * K * 33 / 32; 0 for M <= 0, K <= 0 or K not a multiple of 32. */
 size_t qmm_gemm_mx_workspace_bytes(int64_t M, int64_t K);
 
 /* Routed expert products, every expert in one grouped launch (plus a small

@@ -142,9 +142,9 @@ def test_moe_refusals_in_order(lib):
 def test_gemm_mx_refusals_in_order(lib):
     g = lib.qmm_gemm_mx
     need = lib.qmm_gemm_mx_workspace_bytes(10, 256)
-    # FP8 codes and E8M0 scales for M rounded up to 64 rows.
-    assert need == 64 * 256 + 64 * 8
-    assert lib.qmm_gemm_mx_workspace_bytes(65, 4096) == 128 * 4096 * 33 // 32
+    # Two terms of FP8 codes and E8M0 scales for M rounded up to 64 rows.
+    assert need == 2 * (64 * 256 + 64 * 8)
+    assert lib.qmm_gemm_mx_workspace_bytes(65, 4096) == 2 * 128 * 4096 * 33 // 32
     assert lib.qmm_gemm_mx_workspace_bytes(0, 256) == 0
     assert lib.qmm_gemm_mx_workspace_bytes(10, 48) == 0
     assert g(39, FAKE, FAKE, 1, FAKE, 0, 10, 256, FAKE, need, None) == EMPTY

@@ -1,14 +1,21 @@
 """GPU parity of the scaled FP8 x FP4 matrix-core GEMM for MXFP4 weights
 (qmm_gemm_mx) against the oracle.
 
-The variant rounds each activation once, to MX FP8 (a power-of-two scale per
-32-element block, elements to E4M3), so it has a bar of its own:
+The variant splits each activation into two MX FP8 terms (oracle/mx.py:
+a power-of-two scale per 32-element block, E4M3 elements, then the same for
+the residual), so it has a bar of its own and a tighter one:
 
+* the quantized workspace bit for bit against oracle/mx.py (codes in the
+  MXFP4 nibble order, both scale planes, zero padding rows);
 * random normal activations: |C - C_ref| <= 2e-2 * sum|w||a| + 1e-6 against
-  the oracle's exact binary64 product;
+  the oracle's exact binary64 product, and the f32-accumulation bar
+  1e-3 * sum|w||a'| + 1e-6 against the exact product of the weights with
+  the rebuilt activations a' = 2^e1 hi + 2^e2 lo;
+* a block of 1.0625s (which a single E4M3 term would round 5.9 % low) times
+  weights of one sign;
 * activations that MX FP8 holds exactly (integers of magnitude <= 16, and
-  one-hot rows): the f32-accumulation bar of the other paths,
-  1e-3 * sum|w||a| + 1e-6, and for one-hot rows the f32 weight itself;
+  one-hot rows): the f32-accumulation bar of the other paths, and for
+  one-hot rows the f32 weight itself;
 * K not a multiple of 128 takes the f16 GEMM, at that path's bar.
 """
 import numpy as np
@@ -22,6 +29,7 @@ torch = pytest.importorskip("torch")
 import gguf_block_quantized_kind_amd as qmm  # noqa: E402
 
 from test_gpu_parity import SENTINEL, assert_within_bound, dev, filled, host, _sample_rows  # noqa: E402
+from oracle import mx  # noqa: E402
 
 KIND = "MXFP4"
 MX_RTOL = 2e-2
@@ -84,6 +92,57 @@ def test_gemm_mx_exact_activations(oracle_mod, K, xdt):
         assert_within_bound(got, Y, B, f"M={M} K={K} {xdt}")
 
 
+# Position p of a stored 32-element block holds element NIBBLE_ORDER[p].
+NIBBLE_ORDER = np.array([(p >> 1) + (16 if p & 1 else 0) for p in range(32)])
+
+
+def workspace_planes(ws, M, K):
+    """(hi, lo, s1, s2) of the first M rows of a quantized workspace, codes
+    put back in element order, and the padding rows' four planes."""
+    Mp = (M + 63) // 64 * 64
+    nb = K // 32
+    b = ws.cpu().numpy()
+    hi = b[:Mp * K].reshape(Mp, nb, 32)
+    lo = b[Mp * K:2 * Mp * K].reshape(Mp, nb, 32)
+    s1 = b[2 * Mp * K:2 * Mp * K + Mp * nb].reshape(Mp, nb)
+    s2 = b[2 * Mp * K + Mp * nb:2 * Mp * K + 2 * Mp * nb].reshape(Mp, nb)
+    inv = np.argsort(NIBBLE_ORDER)
+    unperm = lambda c: c[:M][:, :, inv].reshape(M, K)  # noqa: E731
+    pad = (hi[M:], lo[M:], s1[M:], s2[M:])
+    return (unperm(hi), unperm(lo), s1[:M], s2[:M]), pad
+
+
+@pytest.mark.parametrize("xdt", ["f16", "f32"])
+@pytest.mark.parametrize("dist", ["normal", "wide", "sparse"])
+def test_gemm_mx_workspace_matches_the_oracle_quantizer(xdt, dist):
+    """The two-term MX FP8 codes and scale bytes bit for bit: normal
+    activations, magnitudes spread over 2^+-12 (2^+-8 for f16), and blocks
+    that are mostly zeros, -0.0 and exact E4M3 values.  M = 70 leaves 58
+    padding rows, which must hold zero codes and scale byte 0."""
+    M, N, K = 70, 64, 512
+    g = wl.rng("gpu_mx_ws", f"{xdt}_{dist}")
+    dt = np.float16 if xdt == "f16" else np.float32
+    X = g.standard_normal((M, K))
+    if dist == "wide":
+        X = X * np.exp2(g.integers(-8 if xdt == "f16" else -12, 9 if xdt == "f16" else 13, (M, K // 32, 1))
+                        ).repeat(32, axis=2).reshape(M, K)
+    elif dist == "sparse":
+        X = np.where(g.random((M, K)) < 0.7, 0.0, X)
+        X[:, ::7] = -0.0
+        X[:, 3::32] = 448.0 * 2.0 ** -6
+    X = X.astype(dt)
+    W = wl.random_weights(KIND, N, K, g)
+    ws = torch.full((qmm.qmm_gemm_mx_workspace_bytes(M, K),), 0xA5, dtype=torch.uint8, device="cuda")
+    run(W, X, N, ws)
+    (hi, lo, s1, s2), pad = workspace_planes(ws, M, K)
+    want = mx.quantize(X)
+    for name, a, b in zip(("hi", "lo", "s1", "s2"), (hi, lo, s1, s2), want):
+        bad = np.argwhere(a != b)
+        assert bad.size == 0, f"{name}: {len(bad)} bytes differ, first at {bad[0]}: {a[tuple(bad[0])]:#x} vs {b[tuple(bad[0])]:#x}"
+    for plane in pad:
+        assert not np.any(plane)
+
+
 @pytest.mark.parametrize("xdt", ["f16", "f32"])
 def test_gemm_mx_parity_random(oracle_mod, xdt):
     M, N, K = 130, 600, 1280
@@ -94,6 +153,27 @@ def test_gemm_mx_parity_random(oracle_mod, xdt):
     Y, B = oracle_mod.matmul(KIND, W, K, X)
     ratio = assert_within_bound(got, Y, B, f"M={M} {xdt}", rtol=MX_RTOL)
     print(f"worst error / bar: {ratio:.3g}")
+    # Against the exact product with the rebuilt activations: f32 accumulation only.
+    Wd = oracle_mod.dequant(KIND, W).reshape(N, K)
+    Yr, Br = mx.matmul_rebuilt(Wd, X)
+    assert_within_bound(got, Yr, Br, f"rebuilt M={M} {xdt}")
+
+
+@pytest.mark.parametrize("xdt", ["f16", "f32"])
+def test_gemm_mx_block_of_1p0625(oracle_mod, xdt):
+    """Every activation 1.0625 and every weight code non-negative: one E4M3
+    term would give 1.0 (the tie 272 -> 256), 5.9 % low on every output; the
+    second term carries the 0.0625 and the product is exact up to f32
+    accumulation."""
+    M, N, K = 64, 128, 1024
+    g = wl.rng("gpu_mx_1p0625", xdt)
+    W = wl.random_weights(KIND, N, K, g).reshape(N, K // 32, 17).copy()
+    W[:, :, 1:] &= 0x77                                     # codes 0..7: magnitudes >= 0
+    W = W.reshape(-1)
+    X = np.full((M, K), 1.0625, dtype=np.float16 if xdt == "f16" else np.float32)
+    got = run(W, X, N)
+    Y, B = oracle_mod.matmul(KIND, W, K, X)
+    assert_within_bound(got, Y, B, f"1.0625 {xdt}")
 
 
 def test_gemm_mx_workspace_reuse_and_determinism(oracle_mod):

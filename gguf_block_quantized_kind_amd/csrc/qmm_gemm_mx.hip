@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const AT *__restrict__ A,
 // completion is counted in issue order, so both kinds of load keep one
 // distance.  Loads past the last step are clamped to it (a repeated read of
 // cached data), which keeps the loop body free of branches.
-template <int PD, int TN>
+template <int PD, int TN, int TM>
 __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict__ W, int64_t row_bytes,
                                                       const uint8_t *__restrict__ codes,
                                                       const uint8_t *__restrict__ scales, float *__restrict__ C,
@@ -176,9 +176,12 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
   constexpr int kChunks = 5;                    // 16-byte chunks per row and step
   constexpr int kWave = 16 * TN * kChunks;      // chunks per wave and step
   constexpr int LC = (kWave + 63) / 64;         // per lane
+  constexpr int BM = 16 * TM;                   // tokens per tile
+  constexpr int TPT = 256 / BM;                 // threads per token loading activations
+  constexpr int CPT = 8 / TPT;                  // 16-byte chunks per thread and term
   // Term h, token t, 16-byte chunk c at [h][t * 8 + (c ^ (t & 7))].
-  __shared__ u32x4 a_lds[2][2][kBM * 8];
-  __shared__ uint32_t s_lds[2][2 * kBM];  // term h, token t: the step's four E8M0 bytes at h * 64 + t
+  __shared__ u32x4 a_lds[2][2][BM * 8];
+  __shared__ uint32_t s_lds[2][2 * BM];  // term h, token t: the step's four E8M0 bytes at h * BM + t
   // Wave w, row r, chunk q at [w][5r + q]; one spare chunk past the end (a
   // block read at the very end of a row window touches one dword beyond it).
   __shared__ u32x4 b_lds[2][4 * kWave + 1];
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
   const int64_t tiles = (int64_t)n_tiles * m_tiles, per = (tiles + 7) / 8;
   const int64_t tile = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
   if (tile >= tiles) return;  // the whole workgroup: no barrier is reached
-  const int64_t m0 = (tile % m_tiles) * kBM;
+  const int64_t m0 = (tile % m_tiles) * BM;
   const int64_t n0 = (tile / m_tiles) * (64 * TN) + 16 * TN * wave;
   const int nb = K / 32, steps = K / kKS;
   auto row_start = [&](int r) {  // byte offset of wave row r in W; rows past N read row N - 1
@@ -211,24 +214,26 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
   int rs16[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) rs16[tn] = (int)(row_start(16 * tn + j) & 15);
-  // This thread's share of a step's activation tiles: token at, chunks ac,
-  // ac + 1 of both terms (the second term's codes one plane of Mp K bytes
-  // further), and the scale word of token tid % 64, term tid / 64 % 2.
-  const int64_t Mp = (int64_t)m_tiles * kBM;
-  const int at = tid >> 2, ac = 2 * (tid & 3);
+  // This thread's share of a step's activation tiles: token at, chunks
+  // ac .. ac + CPT - 1 of both terms (the second term's codes one plane of
+  // Mp K bytes further), and the scale word of token tid % BM, term
+  // tid / BM % 2.
+  const int64_t Mp = (int64_t)m_tiles * BM;
+  const int at = tid / TPT, ac = CPT * (tid % TPT);
   const uint8_t *asrc = codes + (m0 + at) * K + 16 * ac;
   const int64_t lo_plane = Mp * K;
-  const uint8_t *ssrc = scales + ((tid >> 6) & 1) * (Mp * nb) + (m0 + (tid & 63)) * nb;
+  const uint8_t *ssrc = scales + ((tid / BM) & 1) * (Mp * nb) + (m0 + (tid & (BM - 1))) * nb;
 
-  u32x4 areg[NS][4];
+  u32x4 areg[NS][2 * CPT];
   uint32_t sreg[NS];
   u32x4 breg[NS][LC];
   auto load = [&](int st, int slot) {
     st = st < steps ? st : steps - 1;
-    areg[slot][0] = *reinterpret_cast<const u32x4 *>(asrc + (int64_t)st * kKS);
-    areg[slot][1] = *reinterpret_cast<const u32x4 *>(asrc + (int64_t)st * kKS + 16);
-    areg[slot][2] = *reinterpret_cast<const u32x4 *>(asrc + lo_plane + (int64_t)st * kKS);
-    areg[slot][3] = *reinterpret_cast<const u32x4 *>(asrc + lo_plane + (int64_t)st * kKS + 16);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      areg[slot][c] = *reinterpret_cast<const u32x4 *>(asrc + (int64_t)st * kKS + 16 * c);
+      areg[slot][CPT + c] = *reinterpret_cast<const u32x4 *>(asrc + lo_plane + (int64_t)st * kKS + 16 * c);
+    }
     sreg[slot] = *reinterpret_cast<const uint32_t *>(ssrc + 4 * st);
 #pragma unroll
     for (int i = 0; i < LC; ++i) {
@@ -240,21 +245,20 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
   };
   auto store = [&](int slot, int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      a_lds[buf][h][at * 8 + (ac ^ (at & 7))] = areg[slot][2 * h];
-      a_lds[buf][h][at * 8 + ((ac + 1) ^ (at & 7))] = areg[slot][2 * h + 1];
-    }
-    // Two threads load each scale word; both store the same value, which
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) a_lds[buf][h][at * 8 + ((ac + c) ^ (at & 7))] = areg[slot][CPT * h + c];
+    // Several threads load each scale word; all store the same value, which
     // keeps the step free of branches (a branch here lets the compiler sink
     // the matrix-core chain past the later steps' barriers).
-    s_lds[buf][tid & (2 * kBM - 1)] = sreg[slot];
+    s_lds[buf][tid & (2 * BM - 1)] = sreg[slot];
 #pragma unroll
     for (int i = 0; i < LC; ++i) b_lds[buf][wave * kWave + min(lane + 64 * i, kWave - 1)] = breg[slot][i];
   };
 
-  floatx4 acc[4][TN];
+  floatx4 acc[TM][TN];
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm)
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -265,12 +269,12 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm) {
+      for (int tm = 0; tm < TM; ++tm) {
         const int t = 16 * tm + j;
         const u32x4 c0 = a_lds[buf][h][t * 8 + (G ^ (t & 7))];
         const u32x4 c1 = a_lds[buf][h][t * 8 + ((G + 4) ^ (t & 7))];
         const v8i af = v8i{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
-        const int sa = (int)((s_lds[buf][h * kBM + t] >> (8 * G)) & 0xFFu);
+        const int sa = (int)((s_lds[buf][h * BM + t] >> (8 * G)) & 0xFFu);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const v8i bf = v8i{(int)bq[tn][0], (int)bq[tn][1], (int)bq[tn][2], (int)bq[tn][3], 0, 0, 0, 0};
@@ -331,10 +335,11 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
   auto load_fast = [&](int st0, int u, int slot) {
     const int64_t sp = st0 + PD;  // st0 % 4 == 0, so 68 * st0 is a multiple of 16
     const uint8_t *ag = asrc + sp * kKS + u * kKS;
-    areg[slot][0] = *reinterpret_cast<const u32x4 *>(ag);
-    areg[slot][1] = *reinterpret_cast<const u32x4 *>(ag + 16);
-    areg[slot][2] = *reinterpret_cast<const u32x4 *>(ag + lo_plane);
-    areg[slot][3] = *reinterpret_cast<const u32x4 *>(ag + lo_plane + 16);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      areg[slot][c] = *reinterpret_cast<const u32x4 *>(ag + 16 * c);
+      areg[slot][CPT + c] = *reinterpret_cast<const u32x4 *>(ag + lo_plane + 16 * c);
+    }
     sreg[slot] = *reinterpret_cast<const uint32_t *>(ssrc + 4 * sp + 4 * u);
     const int delta = 16 * ((68 * (PD + u)) >> 4);
 #pragma unroll
@@ -383,7 +388,7 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
 
   // D[i][j] of a 16x16 tile sits in lane j + 16*(i/4), register i%4.
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm)
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       const int64_t n = n0 + 16 * tn + j;
@@ -394,6 +399,20 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(const uint8_t *__restrict_
         if (m < M) C[m * N + n] = acc[tm][tn][q];
       }
     }
+}
+
+// One launch of the scaled GEMM with TN 16-row weight tiles per wave and
+// TM 16-token tiles per workgroup; the grid is a multiple of 8 so that every
+// XCD gets the same number of workgroups.
+template <int TN, int TM>
+hipError_t launch_tiles(const uint8_t *W, int64_t row_bytes, const uint8_t *codes, const uint8_t *scales, float *C,
+                        int64_t M, int64_t N, int64_t K, int64_t Mp, hipStream_t s) {
+  const int64_t m_tiles = Mp / (16 * TM);
+  const int64_t n_tiles = (N + 64 * TN - 1) / (64 * TN);
+  const dim3 grid((unsigned)(8 * ((n_tiles * m_tiles + 7) / 8))), block(256);
+  hipLaunchKernelGGL((gemm_mx_kernel<kPD, TN, TM>), grid, block, 0, s, W, row_bytes, codes, scales, C, (int)M,
+                     (int)N, (int)K, (int)n_tiles, (int)m_tiles);
+  return hipGetLastError();
 }
 
 }  // namespace mx
@@ -417,20 +436,25 @@ hipError_t launch_gemm_mx(const uint8_t *W, const void *A, int a_f16, float *C, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t row_bytes = (K / 32) * 17;
-  const int64_t m_tiles = L.Mp / mx::kBM;
+#ifdef QMM_TUNING
+  static const int cfg = [] {
+    const char *e = getenv("QMM_GEMM_MX_CFG");
+    return e ? atoi(e) : 0;
+  }();
+  switch (cfg) {
+    case 1: return mx::launch_tiles<3, 4>(W, row_bytes, codes, scales, C, M, N, K, L.Mp, s);
+    case 2: return mx::launch_tiles<2, 4>(W, row_bytes, codes, scales, C, M, N, K, L.Mp, s);
+    case 3: return mx::launch_tiles<3, 2>(W, row_bytes, codes, scales, C, M, N, K, L.Mp, s);
+    case 4: return mx::launch_tiles<2, 2>(W, row_bytes, codes, scales, C, M, N, K, L.Mp, s);
+    case 5: return mx::launch_tiles<4, 2>(W, row_bytes, codes, scales, C, M, N, K, L.Mp, s);
+    default: break;
+  }
+#endif
   // 192-row tiles, or 128-row tiles when there would be fewer than 128 of
   // the larger ones (half the compute units).
-  const bool small = (N + 64 * mx::kTN - 1) / (64 * mx::kTN) * m_tiles < 128;
-  const int tn = small ? mx::kTNSmall : mx::kTN;
-  const int64_t n_tiles = (N + 64 * tn - 1) / (64 * tn);
-  const dim3 grid((unsigned)(8 * ((n_tiles * m_tiles + 7) / 8)));
-  if (small)
-    hipLaunchKernelGGL((mx::gemm_mx_kernel<mx::kPD, mx::kTNSmall>), grid, block, 0, s, W, row_bytes, codes, scales,
-                       C, (int)M, (int)N, (int)K, (int)n_tiles, (int)m_tiles);
-  else
-    hipLaunchKernelGGL((mx::gemm_mx_kernel<mx::kPD, mx::kTN>), grid, block, 0, s, W, row_bytes, codes, scales, C,
-                       (int)M, (int)N, (int)K, (int)n_tiles, (int)m_tiles);
-  return hipGetLastError();
+  const bool small = (N + 64 * mx::kTN - 1) / (64 * mx::kTN) * (L.Mp / 64) < 128;
+  if (small) return mx::launch_tiles<mx::kTNSmall, 4>(W, row_bytes, codes, scales, C, M, N, K, L.Mp, s);
+  return mx::launch_tiles<mx::kTN, 4>(W, row_bytes, codes, scales, C, M, N, K, L.Mp, s);
 }
 
 }  // namespace qmm

@@ -58,13 +58,15 @@ __device__ __forceinline__ uint32_t as_u(half2v h) { return __builtin_bit_cast(u
 
 constexpr uint32_t kMagic = 0x64006400u;  // f16 pair (1024, 1024)
 
-// (v & mask) | magic as one v_and_or_b32.  The mask and the magic are passed
-// in registers: a gfx9 VOP3 instruction cannot encode two literal constants,
-// and the compiler would otherwise split this into an AND and an OR.
+// (v & mask) | c.  A gfx9 VOP3 instruction cannot encode two literal
+// constants, so with mask and c known the compiler splits this into an AND
+// and an OR; the empty asm statements (no instruction) hide their values and
+// leave them in registers, and the compiler selects one v_and_or_b32 and
+// tracks it like any other VALU write.
 __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(mask), "v"(c));
-  return r;
+  asm("" : "+v"(mask));
+  asm("" : "+v"(c));
+  return (v & mask) | c;
 }
 // Two f16 values 1024 + field, field = v & mask.
 __device__ __forceinline__ uint32_t mag(uint32_t v, uint32_t mask) { return and_or(v, mask, kMagic); }

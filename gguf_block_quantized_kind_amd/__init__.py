@@ -64,6 +64,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         "qmm_repack": (I, [I, P, P, I64, I64, P]),
         "qmm_gemv_packed": (I, [I, P, P, I, P, I64, I64, I64, P]),
         "qmm_gemv_i8": (I, [I, P, P, I, P, I64, I64, I64, P, SZ, P]),
+        "qmm_gemv_i8_noalloc": (I, [I, P, P, I, P, I64, I64, I64, P]),
         "qmm_moe_packed": (I, [I, P, I64, P, I64, P, I, I, P, I64, I64, I64, P, SZ, P]),
         "qmm_gemv_i8_workspace_bytes": (SZ, [I64, I64]),
         "qmm_row_bytes": (I64, [I, I64]),
@@ -348,6 +349,20 @@ def qmm_gemv_i8(kind, P, x, y, M: int, N: int, K: int, workspace, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check(load_library().qmm_gemv_i8(kind_id(kind), _ptr(P), _ptr(x), _dtype_code(x), _ptr(y), M, N, K,
                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def qmm_gemv_i8_noalloc(kind, P, x, y, M: int, N: int, K: int, stream=None):
+    """qmm_gemv_i8 on the library's own device scratch (no workspace; calls
+    that overlap on one GPU race on it)."""
+    pb = qmm_packed_bytes(kind, N, K)
+    if P is not None and P.element_size() != 1:
+        raise TypeError(f"P must be a byte tensor, got {P.dtype}")
+    if pb > 0:
+        _need(P, pb, "P (bytes)")
+    _need(x, M * K, "x", _F32_OR_F16)
+    _need(y, M * N, "y", _F32)
+    _check(load_library().qmm_gemv_i8_noalloc(kind_id(kind), _ptr(P), _ptr(x), _dtype_code(x), _ptr(y), M, N, K,
+                                              _stream(stream)))
 
 
 def qmm_dequant(kind, W, out, n_elems: int, stream=None):

@@ -307,8 +307,11 @@ QMM_EXPORT size_t qmm_gemv_i8_workspace_bytes(int64_t M, int64_t K) {
   return qmm::gemv_i8_workspace_bytes(M, K);
 }
 
-QMM_EXPORT int qmm_gemv_i8(int kind, const void *P, const void *x, int x_dtype, float *y, int64_t M, int64_t N,
-                           int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+// The checks qmm_gemv_i8 and qmm_gemv_i8_noalloc share, in the documented order.
+int check_gemv_i8(int kind, const void *P, const void *x, int x_dtype, const float *y, int64_t M, int64_t N,
+                  int64_t K) {
   int st = check_packed(kind, M, N, K);
   if (st) return st;
   if (!qmm::gemv_i8_supported(kind))
@@ -323,6 +326,15 @@ QMM_EXPORT int qmm_gemv_i8(int kind, const void *P, const void *x, int x_dtype, 
   if (M * K > (int64_t)QMM_GEMV_I8_MAX_MK)
     return fail(QMM_ERR_BAD_ARG, "M*K=%lld exceeds %d (the block scales are staged in LDS)", (long long)(M * K),
                 QMM_GEMV_I8_MAX_MK);
+  return QMM_OK;
+}
+
+}  // namespace
+
+QMM_EXPORT int qmm_gemv_i8(int kind, const void *P, const void *x, int x_dtype, float *y, int64_t M, int64_t N,
+                           int64_t K, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_gemv_i8(kind, P, x, x_dtype, y, M, N, K);
+  if (st) return st;
   const size_t need = qmm::gemv_i8_workspace_bytes(M, K);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
     return fail(QMM_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need,
@@ -330,6 +342,22 @@ QMM_EXPORT int qmm_gemv_i8(int kind, const void *P, const void *x, int x_dtype, 
   return hip_status(qmm::launch_gemv_i8(kind, (const uint8_t *)P, x, x_dtype == QMM_F16, y, (int)M, N, K, workspace,
                                         (hipStream_t)stream),
                     "gemv_i8 launch");
+}
+
+QMM_EXPORT int qmm_gemv_i8_noalloc(int kind, const void *P, const void *x, int x_dtype, float *y, int64_t M,
+                                   int64_t N, int64_t K, void *stream) {
+  int st = check_gemv_i8(kind, P, x, x_dtype, y, M, N, K);
+  if (st) return st;
+  const size_t need = qmm::gemv_i8_workspace_bytes(M, K);
+  if (need > (size_t)QMM_GEMV_I8_SCRATCH_BYTES)  // excluded by the M * K limit; kept as the scratch's own bound
+    return fail(QMM_ERR_BAD_ARG, "M=%lld K=%lld needs %zu bytes of scratch, more than the %d the library holds",
+                (long long)M, (long long)K, need, QMM_GEMV_I8_SCRATCH_BYTES);
+  void *scratch = nullptr;
+  hipError_t e = qmm::gemv_i8_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "locating the gemv_i8 scratch on the current device");
+  return hip_status(qmm::launch_gemv_i8(kind, (const uint8_t *)P, x, x_dtype == QMM_F16, y, (int)M, N, K, scratch,
+                                        (hipStream_t)stream),
+                    "gemv_i8_noalloc launch");
 }
 
 QMM_EXPORT int qmm_moe_packed(int kind, const void *P, int64_t E, const int32_t *ids, int64_t topk, const void *X,

@@ -26,7 +26,10 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
+#include "qmm.h"
 #include "qmm_gemv_mfma.h"
 #include "qmm_internal.h"
 
@@ -290,6 +293,42 @@ bool gemv_i8_supported(int kind) {
 
 size_t gemv_i8_workspace_bytes(int64_t M, int64_t K) {
   return i8::align256((size_t)M * K) + 2 * i8::align256((size_t)M * (K / 32) * 4);
+}
+
+}  // namespace qmm
+
+// Device scratch of the allocation-free int8 GEMV: the largest workspace that
+// gemv_i8_workspace_bytes gives for M * K <= QMM_GEMV_I8_MAX_MK (262144 code
+// bytes, then 32768 bytes each of scales and code sums).  Every GPU holds its
+// own copy at its own address; host code reaches it only through the address
+// looked up below, never through this name.
+static __device__ __align__(256) uint8_t scratch[QMM_GEMV_I8_SCRATCH_BYTES];
+
+namespace qmm {
+
+hipError_t gemv_i8_scratch(void **ptr) {
+  static_assert(QMM_GEMV_I8_SCRATCH_BYTES == 262144 + 2 * 32768, "scratch = codes + scales + code sums at the largest M * K");
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // Once per device, with that device current (hipGetDevice above).
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_gemv_i8(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,

@@ -36,6 +36,10 @@ bool gemv_i8_supported(int kind);
 size_t gemv_i8_workspace_bytes(int64_t M, int64_t K);
 hipError_t launch_gemv_i8(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
                           int64_t K, void *ws, hipStream_t s);
+// The current device's copy of the library-owned scratch of
+// QMM_GEMV_I8_SCRATCH_BYTES bytes (256-byte aligned) that stands in for `ws`
+// in the allocation-free entry point; looked up once per device.
+hipError_t gemv_i8_scratch(void **ptr);
 
 // C[M][N] = A[M][K] . W^T, any M >= 1, A f32 (a_f16 == 0) or f16.  Runs
 // the wave-private GEMM (qmm_gemm_ks.hip) where gemm_ks_supported, else the

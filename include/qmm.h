@@ -301,6 +301,29 @@ int qmm_gemv_i8(int kind, const void *P, const void *x, int x_dtype, float *y,
  * multiple of 32. */
 size_t qmm_gemv_i8_workspace_bytes(int64_t M, int64_t K);
 
+/* Bytes of the device scratch that qmm_gemv_i8_noalloc uses on each GPU:
+ * qmm_gemv_i8_workspace_bytes at the largest M * K. */
+#define QMM_GEMV_I8_SCRATCH_BYTES 327680
+
+/* qmm_gemv_i8 without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It calls no allocating routine;
+ * the quantized activations go to a scratch of QMM_GEMV_I8_SCRATCH_BYTES
+ * that the library holds in each GPU's memory (a static device array, in
+ * place from library load until the process ends; its address on the
+ * current device is looked up on the first call there).  Same kernels,
+ * arguments, numerics and results bit for bit as qmm_gemv_i8.  Nothing in
+ * the scratch needs to start at zero: every call writes all it reads, and
+ * the scratch keeps the last call's contents.  Calls that overlap on one
+ * GPU (two streams, or two host threads) race on the scratch and must be
+ * serialized by the caller; calls on different GPUs do not share it.
+ * Errors: as qmm_gemv_i8 without its workspace checks (M * K above
+ * QMM_GEMV_I8_MAX_MK, whose workspace would exceed the scratch, gives
+ * QMM_ERR_BAD_ARG), and QMM_ERR_HIP when the scratch cannot be located on
+ * the current device. */
+int qmm_gemv_i8_noalloc(int kind, const void *P, const void *x, int x_dtype, float *y,
+                        int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Dequantize n_elems consecutive elements (whole blocks) of W to f32 on
  * `stream`: the GPU dequantization that redgpu/Vulkore quant_test.cpp checks
  * bit for bit against its CPU references (its dequant_q8_0 / _q5_0 / _q4_k /

@@ -23,10 +23,17 @@ Also printed in the same JSON line:
   roofline      the dominant kernel's algorithmic bytes per launch over its
                 average launch duration (HIP events on its stream), against
                 the 8 TB/s HBM peak, with measured HBM traffic when a
-                counter summary for the current kernel sources exists;
+                counter summary for the current kernel sources exists, and
+                the practical ceiling: a plain streaming-read kernel
+                (libqmm_probe.so) timed over the same bytes with the same
+                copy rotation (ceiling_GBps, frac_of_ceiling);
+  roofline_gemm the same for the prefill GEMM half of the metric: the slower
+                of the two 512 x 4096 x 4096 GEMMs (Q8_0, Q5_0), TFLOP/s
+                against the 2.5 PFLOP/s dense f16 matrix-core peak;
   cpu_baseline  the oracle (binary64 CPU reference) timed on the host cores
-                on full steps of the same workload;
-  cases         each of the four GEMVs alone;
+                on full steps of the same workload, and on one core over a
+                sample of rows (single_core);
+  cases         each of the four GEMVs alone (best and median of 5 rounds);
   secondary     the decode step's GEMVs in the other weight layout, and the
                 other workloads (Q4_0 GEMV, prefill GEMMs, codebook kinds,
                 in both layouts where they are GEMVs, the Q4_0 and MXFP4
@@ -61,6 +68,8 @@ def source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gguf_block_quantized_kind_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not os.path.isfile(os.path.join(csrc, name)):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -89,22 +98,69 @@ def capture(torch, fn, count: int):
     return g
 
 
-def time_launches(torch, case: Case, launches: int) -> float:
-    """Average duration of one launch of `case`, from HIP events on the
-    stream the graph of back-to-back launches replays on (seconds)."""
-    g = capture(torch, lambda i: case.launch(i), launches)
+ROUNDS = 5
+
+
+def time_graph(torch, fn, launches: int) -> tuple[float, float]:
+    """(best, median) over ROUNDS replays of the average duration of one of
+    `launches` back-to-back calls fn(i) captured in one graph, from HIP
+    events on the stream the graph replays on (seconds)."""
+    g = capture(torch, fn, launches)
     g.replay()
     torch.cuda.synchronize()
-    best = float("inf")
-    for _ in range(3):
+    per = []
+    for _ in range(ROUNDS):
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
         g.replay()
         end.record()
         end.synchronize()
-        best = min(best, start.elapsed_time(end) / 1e3 / launches)
+        per.append(start.elapsed_time(end) / 1e3 / launches)
     del g
-    return best
+    per.sort()
+    return per[0], per[len(per) // 2]
+
+
+def time_launches(torch, case: Case, launches: int) -> tuple[float, float]:
+    return time_graph(torch, lambda i: case.launch(i), launches)
+
+
+def stream_ceiling(torch, nbytes: int) -> dict:
+    """The practical HBM read ceiling for nbytes per launch: the streaming
+    probe over rotating copies (a copy is read again only after more than
+    1 GiB of others), best over a few grid sizes."""
+    import ctypes
+
+    from gguf_block_quantized_kind_amd import _build
+
+    if not os.path.exists(_build.PROBE_LIBRARY):
+        raise RuntimeError(f"{_build.PROBE_LIBRARY} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(_build.PROBE_LIBRARY)
+    lib.qmm_probe_stream_read.restype = ctypes.c_int
+    lib.qmm_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = nbytes // 16 * 16
+    n = math.ceil(MALL_DEFEAT_BYTES / nbytes) + 1
+    copies = [torch.full((nbytes,), 7, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    best = None
+    for grid in (1024, 2048, 4096, 8192):
+        out = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
+
+        def launch(i, grid=grid, out=out):
+            st = lib.qmm_probe_stream_read(copies[i % n].data_ptr(), nbytes, grid, 0x5EED1234, out.data_ptr(),
+                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"stream probe failed: {st}")
+
+        launch(0)
+        torch.cuda.synchronize()
+        b, med = time_graph(torch, launch, 32)
+        if best is None or b < best[0]:
+            best = (b, med, grid)
+    del copies
+    torch.cuda.empty_cache()
+    return {"GBps": round(nbytes / best[0] / 1e9, 1), "GBps_median": round(nbytes / best[1] / 1e9, 1),
+            "bytes_per_launch": nbytes, "grid": best[2]}
 
 
 def packed_copies(torch, qmm, w, min_copies: int = 2):
@@ -159,8 +215,19 @@ def secondary_cases(torch, qmm, wl, layout: str = "packed"):
         cases.append(Case(w.name + "_packed", w.kind, launch, copies, w.weight_bytes, w.flops))
     # The Q4_0 and MXFP4 decode workloads on the int8-activation path (its
     # own tolerance; the call quantizes x, then multiplies on the int8
-    # matrix cores, over repacked weights).
-    for w in wl.C1 + [w for w in wl.C4 if w.kind == "MXFP4" and w.M == 1]:
+    # matrix cores, over repacked weights), at one token and at eight.
+    eight = [wl.Matmul(w.name.replace("_m1", "_m8"), w.kind, 8, w.N, w.K, w.x_dtype)
+             for w in wl.C1 + [w for w in wl.C4 if w.kind == "MXFP4" and w.M == 1]]
+    for w in eight:
+        copies = packed_copies(torch, qmm, w)
+        x = torch.from_numpy(w.x()).cuda()
+        y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+
+        def launch(i, w=w, x=x, y=y, copies=copies):
+            qmm.qmm_gemv_packed(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
+
+        cases.append(Case(w.name + "_packed", w.kind, launch, copies, w.weight_bytes, w.flops))
+    for w in wl.C1 + [w for w in wl.C4 if w.kind == "MXFP4" and w.M == 1] + eight:
         copies = packed_copies(torch, qmm, w)
         x = torch.from_numpy(w.x()).cuda()
         y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
@@ -263,10 +330,12 @@ def secondary_cases(torch, qmm, wl, layout: str = "packed"):
     return cases
 
 
-def describe(case: Case, seconds: float) -> dict:
+def describe(case: Case, timing: tuple[float, float]) -> dict:
+    seconds, median = timing
     gbs = case.weight_bytes / seconds / 1e9
     tflops = case.flops / seconds / 1e12
-    out = {"us_per_launch": round(seconds * 1e6, 3), "weight_bytes": case.weight_bytes,
+    out = {"us_per_launch": round(seconds * 1e6, 3), "us_median": round(median * 1e6, 3),
+           "weight_bytes": case.weight_bytes,
            "weight_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
            "TFLOPs": round(tflops, 2)}
     if case.name.endswith("_mx"):
@@ -341,6 +410,9 @@ def write_traffic(case, case_fetch, case_write, copy_fetch, copy_write, copy_byt
 
 
 def cpu_baseline(wl, target_seconds: float) -> dict:
+    """The oracle on full steps with all host threads, then on one thread
+    over the first rows of each weight set (weight bytes of the rows it
+    decodes per second)."""
     import oracle
 
     orc = oracle.default()
@@ -357,10 +429,24 @@ def cpu_baseline(wl, target_seconds: float) -> dict:
         if time.perf_counter() - t0 >= target_seconds:
             break
     dt = time.perf_counter() - t0
+    rows = np.arange(1024)
+    one_bytes, one_steps = 0, 0
+    t1 = time.perf_counter()
+    while True:
+        for w, W, X in data:
+            orc.matmul(w.kind, W, w.K, X, rows=rows, threads=1)
+            one_bytes += w.weight_bytes * len(rows) // w.N
+        one_steps += 1
+        if time.perf_counter() - t1 >= target_seconds / 2:
+            break
+    dt1 = time.perf_counter() - t1
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": orc.max_threads(),
             "kind": "oracle",
             "sample": (f"{steps} full step(s): Q4_K and Q6_K, M=1 and M=8, N=14336, K=4096, "
-                       f"binary64 decode + matmul + bound, no cache rotation, {dt:.1f} s")}
+                       f"binary64 decode + matmul + bound, no cache rotation, {dt:.1f} s"),
+            "single_core": {"value": round(one_bytes / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                            "sample": (f"{one_steps} pass(es) over rows 0..1023 of each of the step's four "
+                                       f"GEMVs, {dt1:.1f} s")}}
 
 
 def main():
@@ -460,17 +546,46 @@ def main():
     dominant = max(cases, key=lambda c: per_case[c.name]["us_per_launch"])
     dom = per_case[dominant.name]
     achieved = dominant.weight_bytes / (dom["us_per_launch"] * 1e-6) / 1e9
+    del main_graph, rem_graph
+    for c in cases:
+        c.copies.clear()
+    torch.cuda.empty_cache()
+    ceiling = stream_ceiling(torch, dominant.weight_bytes)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dominant.name),
-                "kernel": f"qmm GEMV {dominant.name}", "algorithmic_bytes_per_launch": dominant.weight_bytes}
+                "kernel": f"qmm GEMV {dominant.name}", "algorithmic_bytes_per_launch": dominant.weight_bytes,
+                "us_median": dom["us_median"],
+                "ceiling_GBps": ceiling["GBps"], "frac_of_ceiling": round(achieved / ceiling["GBps"], 4),
+                "ceiling": ceiling}
+
+    # The prefill GEMM half of the metric: 512 x 4096 x 4096, Q8_0 and Q5_0.
+    gemm = {}
+    for w in wl.C3:
+        copies = make_copies(torch, w.weights())
+        x = torch.from_numpy(w.x()).cuda()
+        y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+
+        def launch(i, w=w, x=x, y=y, copies=copies):
+            qmm.qmm_matmul(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
+
+        c = Case(w.name, w.kind, launch, copies, w.weight_bytes, w.flops)
+        c.launch(0)
+        torch.cuda.synchronize()
+        gemm[w.name] = (c, describe(c, time_launches(torch, c, 32)))
+        copies.clear()
+        torch.cuda.empty_cache()
+    gname = max(gemm, key=lambda k: gemm[k][1]["us_per_launch"])
+    gcase, gd = gemm[gname]
+    gach = gcase.flops / (gd["us_per_launch"] * 1e-6) / 1e12
+    roofline_gemm = {"bound": "mfma", "achieved": round(gach, 2), "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gach / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": f"qmm GEMM {gname}", "algorithmic_flops_per_launch": gcase.flops,
+                     "us_per_launch": gd["us_per_launch"], "us_median": gd["us_median"],
+                     "all": {k: v[1] for k, v in gemm.items()}}
 
     secondary = {}
     if not args.no_secondary:
-        del main_graph, rem_graph
-        for c in cases:
-            c.copies.clear()
-        torch.cuda.empty_cache()
         sec = secondary_cases(torch, qmm, wl, args.layout)
         # Cases of one weight set share its copies: free them after the last.
         last = {id(c.copies): i for i, c in enumerate(sec)}
@@ -488,7 +603,9 @@ def main():
         "metric": "quantized GEMV weight GB/s (% of HBM peak); prefill GEMM TFLOP/s (% MFMA peak)",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16 x f16 matrix cores, f32 accumulate (f32 x rounded once to f16; weight codes times "
+                 "sub-block scales as exact f16 integers; super-block scales and mins applied in f32)",
         "data": "synthetic",
         "config": {"workload": "decode GEMV, Q4_K and Q6_K weights, M=1 and M=8, N=14336, K=4096, "
                                "f32 activations, one launch per (kind, M) per step",
@@ -497,6 +614,7 @@ def main():
                    "weight_bytes_per_step": bytes_per_step, "hbm_frac": round(value / HBM_PEAK_GBS, 4),
                    "device": props.name, "cus": props.multi_processor_count},
         "roofline": roofline,
+        "roofline_gemm": roofline_gemm,
         "cpu_baseline": cpu,
         "cases": per_case,
         "secondary": secondary,

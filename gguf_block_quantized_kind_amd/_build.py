@@ -17,6 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libqmm.so")
+# The streaming-read probe that measurements compare against (its own
+# library; not part of the matmul C ABI).
+PROBE_SOURCE = os.path.join(CSRC, "probe", "qmm_stream_read.hip")
+PROBE_LIBRARY = os.path.join(HERE, "libqmm_probe.so")
 OBJDIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
@@ -68,7 +72,17 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIBRARY)
+    build_probe(cc)
     return LIBRARY
+
+
+def build_probe(cc: str) -> str:
+    tmp = PROBE_LIBRARY + ".tmp"
+    r = subprocess.run([cc, *compile_flags(), "-shared", PROBE_SOURCE, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SOURCE}:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIBRARY)
+    return PROBE_LIBRARY
 
 
 if __name__ == "__main__":

@@ -298,12 +298,14 @@ int oracle_matmul(int kind, const uint8_t *W, int64_t K, const int64_t *rows, in
     if (K <= 0 || K % be != 0 || n_sel < 0 || M < 0) return -2;
     const int64_t row_bytes = (K / be) * bb;
 #ifdef _OPENMP
-    if (threads > 0) omp_set_num_threads(threads);
+    /* The count applies to this region only (omp_set_num_threads would
+     * change every later call's default). */
+    const int nt = threads > 0 ? threads : omp_get_max_threads();
 #else
     (void)threads;
 #endif
     int failed = 0;
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
     {
         double *w = (double *)malloc((size_t)K * sizeof(double));
         if (!w) {
@@ -351,12 +353,14 @@ int oracle_moe(int kind, const uint8_t *W, int64_t E, int64_t N, int64_t K, cons
     for (int64_t p = 0; p < pairs; ++p)
         if (ids[p] < 0 || ids[p] >= E) return -4;
 #ifdef _OPENMP
-    if (threads > 0) omp_set_num_threads(threads);
+    /* The count applies to this region only (omp_set_num_threads would
+     * change every later call's default). */
+    const int nt = threads > 0 ? threads : omp_get_max_threads();
 #else
     (void)threads;
 #endif
     int failed = 0;
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
     {
         double *w = (double *)malloc((size_t)K * sizeof(double));
         if (!w) {

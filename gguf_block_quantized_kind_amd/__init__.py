@@ -64,6 +64,7 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         "qmm_repack": (I, [I, P, P, I64, I64, P]),
         "qmm_gemv_packed": (I, [I, P, P, I, P, I64, I64, I64, P]),
         "qmm_gemv_i8": (I, [I, P, P, I, P, I64, I64, I64, P, SZ, P]),
+        "qmm_matmul_packed": (I, [I, P, P, I, P, I64, I64, I64, P]),
         "qmm_gemv_i8_noalloc": (I, [I, P, P, I, P, I64, I64, I64, P]),
         "qmm_moe_packed": (I, [I, P, I64, P, I64, P, I, I, P, I64, I64, I64, P, SZ, P]),
         "qmm_gemv_i8_workspace_bytes": (SZ, [I64, I64]),
@@ -314,6 +315,18 @@ def qmm_gemv_packed(kind, P, x, y, M: int, N: int, K: int, stream=None):
     _need(y, M * N, "y", _F32)
     _check(load_library().qmm_gemv_packed(kind_id(kind), _ptr(P), _ptr(x), _dtype_code(x), _ptr(y),
                                           M, N, K, _stream(stream)))
+
+
+def qmm_matmul_packed(kind, P, A, C, M: int, N: int, K: int, stream=None):
+    pb = qmm_packed_bytes(kind, N, K)
+    if P is not None and P.element_size() != 1:
+        raise TypeError(f"P must be a byte tensor, got {P.dtype}")
+    if pb > 0:
+        _need(P, pb, "P (bytes)")
+    _need(A, M * K, "A", _F32_OR_F16)
+    _need(C, M * N, "C", _F32)
+    _check(load_library().qmm_matmul_packed(kind_id(kind), _ptr(P), _ptr(A), _dtype_code(A), _ptr(C),
+                                            M, N, K, _stream(stream)))
 
 
 def qmm_moe_packed(kind, P, E: int, ids, topk: int, X, x_per_slot: int, Y, M: int, N: int, K: int,

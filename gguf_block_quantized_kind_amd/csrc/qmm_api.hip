@@ -302,6 +302,31 @@ QMM_EXPORT int qmm_gemv_packed(int kind, const void *P, const void *x, int x_dty
                     "gemv_packed launch");
 }
 
+QMM_EXPORT int qmm_matmul_packed(int kind, const void *P, const void *A, int a_dtype, float *C, int64_t M, int64_t N,
+                                 int64_t K, void *stream) {
+  int st = check_packed(kind, M, N, K);
+  if (st) return st;
+  if ((st = check_dtype(a_dtype))) return st;
+  if (!P || !C) return fail(QMM_ERR_BAD_ARG, "P or C is NULL");
+  if (!aligned(P, 16)) return fail(QMM_ERR_BAD_ARG, "P is not 16-byte aligned");
+  if ((st = check_act(A, a_dtype, "A"))) return st;
+  if (!aligned(C, 4)) return fail(QMM_ERR_BAD_ARG, "C is not 4-byte aligned");
+  if (M * K >= ((int64_t)1 << 31)) return fail(QMM_ERR_BAD_ARG, "M*K=%lld exceeds 2^31-1", (long long)(M * K));
+  if (M <= QMM_GEMV_MAX_M)
+    return hip_status(qmm::launch_gemv_packed(kind, (const uint8_t *)P, A, a_dtype == QMM_F16, C, (int)M, N, K,
+                                              (hipStream_t)stream),
+                      "matmul_packed launch (GEMV)");
+  if (!qmm::gemm_packed_supported(kind))
+    return fail(QMM_ERR_UNSUPPORTED_KIND, "the prefill GEMM over repacked weights does not take kind %d (M > %d)",
+                kind, QMM_GEMV_MAX_M);
+  if (qmm::packed_bytes_of(kind, N, K) >= ((int64_t)1 << 32) || M >= ((int64_t)1 << 24))
+    return fail(QMM_ERR_BAD_ARG, "N=%lld, K=%lld, M=%lld exceed the GEMM's 32-bit offsets", (long long)N,
+                (long long)K, (long long)M);
+  return hip_status(qmm::launch_gemm_packed(kind, (const uint8_t *)P, A, a_dtype == QMM_F16, C, M, N, K,
+                                            (hipStream_t)stream),
+                    "matmul_packed launch (GEMM)");
+}
+
 QMM_EXPORT size_t qmm_gemv_i8_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0 || K % 32 != 0) return 0;
   return qmm::gemv_i8_workspace_bytes(M, K);

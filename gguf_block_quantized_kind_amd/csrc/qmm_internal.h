@@ -29,6 +29,12 @@ hipError_t launch_repack(int kind, const uint8_t *W, void *P, int64_t N, int64_t
 hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
                               int64_t K, hipStream_t s);
 
+// The prefill GEMM over repacked weights (any M; qmm_gemm_pk.hip), for the
+// kinds gemm_packed_supported names; P offsets must fit in 32 bits.
+bool gemm_packed_supported(int kind);
+hipError_t launch_gemm_packed(int kind, const uint8_t *P, const void *A, int a_f16, float *C, int64_t M, int64_t N,
+                              int64_t K, hipStream_t s);
+
 // The int8-activation GEMV over repacked Q8_0 / Q4_0 weights (1 <= M <= 8):
 // activations quantized into `ws` (gemv_i8_workspace_bytes(M, K) bytes,
 // 256-byte aligned), then the integer matrix-core product.

@@ -33,6 +33,7 @@ namespace qmm {
 namespace pk {
 
 using gm::half2v;
+using gm::u32x2;
 using gm::u32x4;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -46,33 +47,170 @@ constexpr int kRing = 4;  // stages in flight: the one computed and three loadin
 
 __device__ __forceinline__ half8 as_h8(u32x4 v) { return __builtin_bit_cast(half8, v); }
 
-// Per-kind view of a record.  A stage is one lane section: kSteps
-// matrix-core steps of 32 elements.  For step h of section c, lane group
-// G's eight elements are k-block elements a_off(c, h, G) .. + 7 (the
-// activations read there), and b(w, s, h) builds their f16 B operand from
-// the lane's 16 section bytes w and its scale word s: dword c of the 16
-// bytes at scale_row(j) (row j's row section).
-template <int KIND> struct Pk;
+// Per-kind view of a record (qmm_repack): a k-block of 256 elements is
+// kRing stages of two matrix-core steps (32 elements, one GGUF block) each.
+// Rows<KIND, TN> holds a wave's weight registers for TN row tiles: what it
+// loads at each ring position u of a k-block (into k-block buffer p), how
+// many vector-memory operations that is per row tile (loads(u)), and the
+// f16 B operand of step h of stage u, whose eight elements per lane group
+// G are the k-block elements given by a_part(u, h, G, e) (activation parts
+// e of kParts, each kPartElems elements long).
+template <int KIND, int TN> struct Rows;
 
-// Q8_0: four sections; section c slot (G, j) holds codes 8G .. 8G+7 of
-// blocks 2c and 2c+1 of row j; the row section holds row j's eight f16
-// scales at 16 j (dword c: the scales of blocks 2c and 2c+1).
-template <> struct Pk<Q8_0> {
+__device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2 ld_b64(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// Q8_0: lane section c, slot (G, j) holds codes 8G .. 8G+7 of blocks 2c and
+// 2c+1 of row j (one section per stage); row j's row section holds its
+// eight f16 block scales at 4096 + 16 j.  Step h of stage u is block 2u + h,
+// lane group G's elements 8G .. 8G+7 of it.
+template <int TN> struct Rows<Q8_0, TN> {
   static constexpr int kRec = 16 * 272;
-  static constexpr int kSections = 4, kSteps = 2;
-  static __device__ __forceinline__ int a_off(int c, int h, int G) { return 64 * c + 32 * h + 8 * G; }
-  static __device__ __forceinline__ int scale_row(int j) { return 4096 + 16 * j; }
-  static __device__ __forceinline__ u32x4 b(const u32x4 &w, uint32_t s, int h) {
-    const half2v d = gm::splat(h ? s >> 16 : s & 0xFFFFu), off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  static constexpr int kParts = 1, kPartElems = 8;
+  static __device__ __forceinline__ int a_part(int u, int h, int G, int) { return 64 * u + 32 * h + 8 * G; }
+  static constexpr int loads(int u) { return u == 0 ? 2 : 1; }
+  u32x4 w[kRing][TN], s[2][TN];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int lane, int j, const int (&rec)[TN], int wk, int u,
+                                       int p) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) w[u][tn] = ld_b128(r, 16 * lane, rec[tn] + wk + 1024 * u);
+    if (u == 0) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) s[p][tn] = ld_b128(r, 4096 + 16 * j, rec[tn] + wk);
+    }
+  }
+  __device__ __forceinline__ u32x4 b(int u, int p, int tn, int h, int) const {
+    const uint32_t sc = s[p][tn][u];
+    const half2v d = gm::splat(h ? sc >> 16 : sc & 0xFFFFu), off = {(_Float16)1152.0f, (_Float16)1152.0f};
     u32x4 out;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       uint32_t p01, p23;
-      gm::spread(w[2 * h + q] ^ 0x80808080u, p01, p23);
+      gm::spread(w[u][tn][2 * h + q] ^ 0x80808080u, p01, p23);
       out[2 * q] = gm::affine(p01, off, d);
       out[2 * q + 1] = gm::affine(p23, off, d);
     }
     return out;
+  }
+};
+
+// The 32-element nibble kinds: lane section c, slot (G, j), dword w holds
+// code bytes 4G .. 4G+3 of block 4c + w of row j, i.e. elements 4G .. 4G+3
+// (low nibbles) and 16+4G .. 16+4G+3 (high nibbles).  Sections 0 and 1 are
+// loaded at ring positions 0 and 2; step h of stage u is block 2u + h, dword
+// 2 (u mod 2) + h of section u / 2, and lane group G's activations are the
+// two runs of four at 4G and 16 + 4G of that block.
+template <int KIND, int TN> struct NibRows {
+  static constexpr int kParts = 2, kPartElems = 4;
+  static __device__ __forceinline__ int a_part(int u, int h, int G, int e) { return 64 * u + 32 * h + 16 * e + 4 * G; }
+  u32x4 w[2][2][TN];
+  __device__ __forceinline__ void load_sections(__amdgpu_buffer_rsrc_t r, int lane, const int (&rec)[TN], int wk, int u,
+                                                int p) {
+    if (u == 0 || u == 2) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) w[p][u / 2][tn] = ld_b128(r, 16 * lane, rec[tn] + wk + 512 * u);
+    }
+  }
+  __device__ __forceinline__ uint32_t codes(int u, int p, int tn, int h) const { return w[p][u / 2][tn][2 * (u & 1) + h]; }
+  // The f16 pairs of (lo, hi): four biased integer codes per byte of each,
+  // minus `off`, times d, each rounded once.
+  static __device__ __forceinline__ u32x4 affine8(uint32_t lo, uint32_t hi, half2v off, half2v d) {
+    uint32_t a, c, e, f;
+    gm::spread(lo, a, c);
+    gm::spread(hi, e, f);
+    return u32x4{gm::affine(a, off, d), gm::affine(c, off, d), gm::affine(e, off, d), gm::affine(f, off, d)};
+  }
+};
+
+// Q4_0: row section at 2048 + 16 j, the eight f16 block scales; w = d (q - 8).
+template <int TN> struct Rows<Q4_0, TN> : NibRows<Q4_0, TN> {
+  using B = NibRows<Q4_0, TN>;
+  static constexpr int kRec = 16 * 144;
+  static constexpr int loads(int u) { return u == 0 ? 2 : u == 2 ? 1 : 0; }
+  u32x4 s[2][TN];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int lane, int j, const int (&rec)[TN], int wk, int u,
+                                       int p) {
+    B::load_sections(r, lane, rec, wk, u, p);
+    if (u == 0) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) s[p][tn] = ld_b128(r, 2048 + 16 * j, rec[tn] + wk);
+    }
+  }
+  __device__ __forceinline__ u32x4 b(int u, int p, int tn, int h, int) const {
+    const uint32_t sc = s[p][tn][u], q = B::codes(u, p, tn, h);
+    const half2v d = gm::splat(h ? sc >> 16 : sc & 0xFFFFu), off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    return B::affine8(q & 0x0F0F0F0Fu, (q >> 4) & 0x0F0F0F0Fu, off, d);
+  }
+};
+
+// IQ4_NL: as Q4_0, w = d * table[code] (the table value plus 128 is a byte).
+template <int TN> struct Rows<IQ4_NL, TN> : Rows<Q4_0, TN> {
+  using B = NibRows<IQ4_NL, TN>;
+  __device__ __forceinline__ u32x4 b(int u, int p, int tn, int h, int) const {
+    const uint32_t sc = this->s[p][tn][u], q = this->w[p][u / 2][tn][2 * (u & 1) + h];
+    const half2v d = gm::splat(h ? sc >> 16 : sc & 0xFFFFu), off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    return B::affine8(iq4_lookup(q & 0x0F0F0F0Fu), iq4_lookup((q >> 4) & 0x0F0F0F0Fu), off, d);
+  }
+};
+
+// Q5_0: row sections at 2048 + 32 j (eight 32-bit qh words, bit e the fifth
+// bit of element e) and 2560 + 16 j (eight f16 scales); w = d (q - 16).  Each
+// stage loads the two qh words of its blocks.
+template <int TN> struct Rows<Q5_0, TN> : NibRows<Q5_0, TN> {
+  using B = NibRows<Q5_0, TN>;
+  static constexpr int kRec = 16 * 176;
+  static constexpr int loads(int u) { return u == 0 ? 3 : u == 2 ? 2 : 1; }
+  u32x4 s[2][TN];
+  u32x2 qh[kRing][TN];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int lane, int j, const int (&rec)[TN], int wk, int u,
+                                       int p) {
+    B::load_sections(r, lane, rec, wk, u, p);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) qh[u][tn] = ld_b64(r, 2048 + 32 * j, rec[tn] + wk + 8 * u);
+    if (u == 0) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) s[p][tn] = ld_b128(r, 2560 + 16 * j, rec[tn] + wk);
+    }
+  }
+  __device__ __forceinline__ u32x4 b(int u, int p, int tn, int h, int G) const {
+    const uint32_t sc = s[p][tn][u], q = B::codes(u, p, tn, h), hb = qh[u][tn][h];
+    const half2v d = gm::splat(h ? sc >> 16 : sc & 0xFFFFu), off = {(_Float16)1040.0f, (_Float16)1040.0f};
+    const uint32_t lo = (q & 0x0F0F0F0Fu) | (spread4(hb >> (4 * G)) << 4);
+    const uint32_t hi = ((q >> 4) & 0x0F0F0F0Fu) | (spread4(hb >> (16 + 4 * G)) << 4);
+    return B::affine8(lo, hi, off, d);
+  }
+};
+
+// MXFP4: row section at 2048 + 8 j, the eight E8M0 bytes; w = 2^(e - 127)
+// e2m1[code], each the f16 rounding of the scaled value (gfx950's scaled FP4
+// conversion takes a byte's two nibbles, elements 4G + i and 16 + 4G + i).
+template <int TN> struct Rows<MXFP4, TN> : NibRows<MXFP4, TN> {
+  using B = NibRows<MXFP4, TN>;
+  static constexpr int kRec = 16 * 136;
+  static constexpr int loads(int u) { return u == 0 ? 2 : u == 2 ? 1 : 0; }
+  u32x2 s[2][TN];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int lane, int j, const int (&rec)[TN], int wk, int u,
+                                       int p) {
+    B::load_sections(r, lane, rec, wk, u, p);
+    if (u == 0) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) s[p][tn] = ld_b64(r, 2048 + 8 * j, rec[tn] + wk);
+    }
+  }
+  __device__ __forceinline__ u32x4 b(int u, int p, int tn, int h, int) const {
+    const int blk = 2 * u + h;
+    const float sc = e8m0_to_f32((s[p][tn][blk >> 2] >> (8 * (blk & 3))) & 0xFFu);
+    const uint32_t q = B::codes(u, p, tn, h);
+    const uint32_t p0 = gm::bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc, 0));
+    const uint32_t p1 = gm::bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc, 1));
+    const uint32_t p2 = gm::bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc, 2));
+    const uint32_t p3 = gm::bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc, 3));
+    return u32x4{perm(p1, p0, 0x05040100u), perm(p3, p2, 0x05040100u), perm(p1, p0, 0x07060302u),
+                 perm(p3, p2, 0x07060302u)};
   }
 };
 
@@ -115,12 +253,11 @@ template <int KIND, typename AT, int TM, int TN, int KQ, int NH>
 __global__ __launch_bounds__(64 * KQ * NH, 1) void gemm_pk_kernel(const uint8_t *__restrict__ P,
                                                                   const AT *__restrict__ A, float *__restrict__ C,
                                                                   int M, int N, int K, int tiles_m) {
-  using D = Pk<KIND>;
+  using R = Rows<KIND, TN>;
   using AS = AStage<AT, TM>;
   constexpr bool kF32 = sizeof(AT) == 4;
   constexpr int KW = KQ * NH;
   static_assert(AS::NLD % NH == 0, "staging loads split evenly");
-  static_assert(D::kSections == kRing && D::kSteps == 2, "one ring turn per k-block");
   // One LDS array per ring position (the k parts' buffers side by side),
   // so that the compiler, which orders LDS reads after direct-to-LDS loads
   // into the same array only, lets a stage's fragment reads run while the
@@ -150,36 +287,41 @@ __global__ __launch_bounds__(64 * KQ * NH, 1) void gemm_pk_kernel(const uint8_t 
   // offset.  Record of row tile tn at k-block kb: (tile * nkb + kb) * kRec;
   // tiles past the last read the last one (never stored).
   const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(P), 0, (int)(((uint32_t)(N + 15) / 16) * (uint32_t)nkb * (uint32_t)D::kRec), kRsrcWord3);
+      const_cast<uint8_t *>(P), 0, (int)(((uint32_t)(N + 15) / 16) * (uint32_t)nkb * (uint32_t)R::kRec), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<AT *>(A), 0, (int)((uint32_t)M * (uint32_t)K * (uint32_t)sizeof(AT)), kRsrcWord3);
   const int last_tile = (N + 15) / 16 - 1;
   int rec0[TN];
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) rec0[tn] = min(n0 / 16 + tn, last_tile) * nkb * D::kRec;
-  const int woff = 16 * lane, soff = D::scale_row(j);
+  for (int tn = 0; tn < TN; ++tn) rec0[tn] = min(n0 / 16 + tn, last_tile) * nkb * R::kRec;
   // Activation staging loads: load q of a stage brings tokens m0 + TPL q ..
   // + TPL - 1 (clamped to M - 1, never stored), lane l the chunk that goes
   // to position l mod CPT of token TPL q + l / CPT.
   const int at = lane / AS::CPT, ap = lane % AS::CPT;
   const int acol = 16 * (ap ^ (at % AS::KEYP));
   // Fragment reads (bytes within a stage buffer): lane (i, G) of token tile
-  // tm, step h reads the chunk(s) holding elements 32 h + 8 G .. + 7.
-  constexpr int NA = kF32 ? 2 : 1;
-  int frd[D::kSteps][NA];
+  // tm, step h reads part e of its eight elements, kPartElems elements at
+  // a_part(0, h, G, e), as one or two 16-byte pieces or one 8-byte piece.
+  constexpr int PB = R::kPartElems * (int)sizeof(AT);  // bytes per part
+  constexpr int NP = PB >= 16 ? PB / 16 : 1;           // pieces per part
+  int frd[2][R::kParts][NP];
 #pragma unroll
-  for (int h = 0; h < D::kSteps; ++h)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int e = 0; e < NA; ++e) {
-      const int c = (32 * h + 8 * G) * (int)sizeof(AT) / 16 + e;
-      frd[h][e] = j * AS::CPT * 16 + 16 * (c ^ (j % AS::KEYP));
-    }
+    for (int e = 0; e < R::kParts; ++e)
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        const int b0 = R::a_part(0, h, G, e) * (int)sizeof(AT) + 16 * q;
+        frd[h][e][q] = j * AS::CPT * 16 + 16 * ((b0 >> 4) ^ (j % AS::KEYP)) + (b0 & 15);
+      }
   const int grp = wq * AS::BYTES;  // this part's buffer in each ring array
 
-  // Vector-memory operations a stage issues per wave: its activation share,
-  // its sections, and (section 0 only) the scale rows.
-  constexpr int kBase = AS::NLD / NH + TN;
-  u32x4 wreg[kRing][TN], srow[2][TN];
+  R rows;
+  // Vector-memory operations a wave issues for the stage at ring position u
+  // (its activation share and its weight rows), and those of the two stages
+  // after ring position u.
+  constexpr auto count = [](int u) { return AS::NLD / NH + R::loads(u) * TN; };
+  constexpr auto more = [count](int u) { return count((u + 1) % kRing) + count((u + 2) % kRing); };
 
   // Loads of stage t (clamped to the last stage: a re-read never used) into
   // ring position u = t mod kRing and scale buffer p.
@@ -193,15 +335,7 @@ __global__ __launch_bounds__(64 * KQ * NH, 1) void gemm_pk_kernel(const uint8_t 
       const int q = wh * (AS::NLD / NH) + i;
       dma16(ars, dst + 1024 * q, min(m0 + AS::TPL * q + at, M - 1) * K * (int)sizeof(AT) + acol, ak);
     }
-    const int wk = kb * D::kRec;  // wave-uniform
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-      wreg[u][tn] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, woff, rec0[tn] + wk + 1024 * u, 0));
-    if (u == 0) {
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        srow[p][tn] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, soff, rec0[tn] + wk, 0));
-    }
+    rows.load(prs, lane, j, rec0, kb * R::kRec, u, p);
   };
 
   floatx4 acc[TM][TN];
@@ -217,24 +351,34 @@ __global__ __launch_bounds__(64 * KQ * NH, 1) void gemm_pk_kernel(const uint8_t 
     for (int tm = 0; tm < TM; ++tm) {
       const uint8_t *row = src + 16 * tm * AS::CPT * 16;
       if constexpr (kF32) {
-        const f32x4 a0 = __builtin_bit_cast(f32x4, *reinterpret_cast<const u32x4 *>(row + frd[h][0]));
-        const f32x4 a1 = __builtin_bit_cast(f32x4, *reinterpret_cast<const u32x4 *>(row + frd[h][1]));
-        const float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < R::kParts; ++e)
+#pragma unroll
+          for (int q = 0; q < NP; ++q) {
+            const f32x4 v = __builtin_bit_cast(f32x4, *reinterpret_cast<const u32x4 *>(row + frd[h][e][q]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[e * R::kPartElems + 4 * q + i] = v[i];
+          }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const _Float16 hv = (_Float16)a[e];
           ahi[tm][e] = hv;
           alo[tm][e] = (_Float16)(a[e] - (float)hv);
         }
+      } else if constexpr (PB == 16) {
+        ahi[tm] = as_h8(*reinterpret_cast<const u32x4 *>(row + frd[h][0][0]));
       } else {
-        ahi[tm] = as_h8(*reinterpret_cast<const u32x4 *>(row + frd[h][0]));
+        const u32x2 x0 = *reinterpret_cast<const u32x2 *>(row + frd[h][0][0]);
+        const u32x2 x1 = *reinterpret_cast<const u32x2 *>(row + frd[h][1][0]);
+        ahi[tm] = as_h8(u32x4{x0[0], x0[1], x1[0], x1[1]});
       }
     }
   };
   auto products = [&](int u, int p, int h, const half8 (&ahi)[TM], const half8 (&alo)[TM]) {
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
-      const half8 bf = as_h8(D::b(wreg[u][tn], srow[p][tn][u], h));
+      const half8 bf = as_h8(rows.b(u, p, tn, h, G));
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[tm], bf, acc[tm][tn], 0, 0, 0);
@@ -250,7 +394,7 @@ __global__ __launch_bounds__(64 * KQ * NH, 1) void gemm_pk_kernel(const uint8_t 
   // the compiler wait for all of them, the later stages' too).
   auto arrive = [&](int u) {
     __builtin_amdgcn_sched_barrier(0);
-    constexpr int kMore[kRing] = {2 * kBase, 2 * kBase, 2 * kBase + TN, 2 * kBase + TN};
+    constexpr int kMore[kRing] = {more(0), more(1), more(2), more(3)};
     switch (u) {
       case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMore[0])); break;
       case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMore[1])); break;
@@ -265,8 +409,10 @@ __global__ __launch_bounds__(64 * KQ * NH, 1) void gemm_pk_kernel(const uint8_t 
   // Stage t at ring position u, scale buffer p (its k-block's parity); the
   // loads it issues are for stage t + kRing - 1.
   auto stage = [&](int t, int u, int p) {
+    // Stage t + kRing - 1 lies in the next k-block unless this stage opens
+    // one (ring position 0).
     const int un = (u + kRing - 1) % kRing;
-    load(t + kRing - 1, un, un == 0 ? p ^ 1 : p);
+    load(t + kRing - 1, un, u == 0 ? p : p ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     products(u, p, 0, a0hi, a0lo);
     frags(u, 1, a1hi, a1lo);
@@ -372,12 +518,18 @@ static hipError_t run_kind(const uint8_t *P, const void *A, int a_f16, float *C,
 
 }  // namespace pk
 
-bool gemm_packed_supported(int kind) { return kind == Q8_0; }
+bool gemm_packed_supported(int kind) {
+  return kind == Q8_0 || kind == Q4_0 || kind == Q5_0 || kind == IQ4_NL || kind == MXFP4;
+}
 
 hipError_t launch_gemm_packed(int kind, const uint8_t *P, const void *A, int a_f16, float *C, int64_t M, int64_t N,
                               int64_t K, hipStream_t s) {
   switch (kind) {
     case Q8_0: return pk::run_kind<Q8_0>(P, A, a_f16, C, M, N, K, s);
+    case Q4_0: return pk::run_kind<Q4_0>(P, A, a_f16, C, M, N, K, s);
+    case Q5_0: return pk::run_kind<Q5_0>(P, A, a_f16, C, M, N, K, s);
+    case IQ4_NL: return pk::run_kind<IQ4_NL>(P, A, a_f16, C, M, N, K, s);
+    case MXFP4: return pk::run_kind<MXFP4>(P, A, a_f16, C, M, N, K, s);
     default: break;
   }
   return hipErrorNotSupported;

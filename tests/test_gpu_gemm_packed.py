@@ -23,7 +23,7 @@ import gguf_block_quantized_kind_amd as qmm  # noqa: E402
 
 from test_gpu_parity import SENTINEL, assert_within_bound, dev, filled, host, _sample_rows  # noqa: E402
 
-KINDS = ["Q8_0"]
+KINDS = ["Q8_0", "Q4_0", "Q5_0", "IQ4_NL", "MXFP4"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -64,7 +64,11 @@ def test_matmul_packed_parity(oracle_mod, kind, xdt, N, K):
 @pytest.mark.parametrize("kind", KINDS)
 def test_matmul_packed_unit_vectors_return_f16_weights(oracle_mod, kind):
     N, K = 150, 1024
-    W = wl.random_weights(kind, N, K, wl.rng("gpu_gemm_packed_unit", kind), scales="stress")
+    # Stress scales, kept within the f16 range the GEMM's weights live in
+    # (MXFP4: E8M0 exponents 100 .. 140, i.e. |w| <= 6 * 2^13).
+    g = wl.rng("gpu_gemm_packed_unit", kind)
+    W = (wl.random_weights(kind, N, K, g, e8m0_range=(100, 140)) if kind == "MXFP4"
+         else wl.random_weights(kind, N, K, g, scales="stress"))
     want = oracle_mod.dequant(kind, W).reshape(N, K).astype(np.float16).astype(np.float32)
     ks = [0, 1, 7, 8, 31, 32, 255, 256, 511, 600, K - 1] + list(range(100, 121))
     X = np.zeros((len(ks), K), dtype=np.float16)

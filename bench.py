@@ -28,8 +28,10 @@ Also printed in the same JSON line:
                 (libqmm_probe.so) timed over the same bytes with the same
                 copy rotation (ceiling_GBps, frac_of_ceiling);
   roofline_gemm the same for the prefill GEMM half of the metric: the slower
-                of the two 512 x 4096 x 4096 GEMMs (Q8_0, Q5_0), TFLOP/s
-                against the 2.5 PFLOP/s dense f16 matrix-core peak;
+                of the two 512 x 4096 x 4096 GEMMs (Q8_0, Q5_0) in the step's
+                weight layout (repacked records by default), TFLOP/s against
+                the 2.5 PFLOP/s dense f16 matrix-core peak, with both layouts
+                of both kinds under "all";
   cpu_baseline  the oracle (binary64 CPU reference) timed on the host cores
                 on full steps of the same workload, and on one core over a
                 sample of rows (single_core);
@@ -237,7 +239,7 @@ def secondary_cases(torch, qmm, wl, layout: str = "packed"):
             qmm.qmm_gemv_i8(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K, ws)
 
         cases.append(Case(w.name + "_i8", w.kind, launch, copies, w.weight_bytes, w.flops))
-    for w in wl.C1 + wl.C3 + wl.C4:
+    for w in wl.C1 + wl.C4:
         copies = make_copies(torch, w.weights())
         x = torch.from_numpy(w.x()).cuda()
         y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
@@ -246,6 +248,17 @@ def secondary_cases(torch, qmm, wl, layout: str = "packed"):
             qmm.qmm_matmul(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
 
         cases.append(Case(w.name, w.kind, launch, copies, w.weight_bytes, w.flops))
+    # The codebook prefill workloads over repacked records (the 32-element
+    # kinds the packed GEMM takes).
+    for w in [w for w in wl.C4 if w.M > 8 and w.kind in ("IQ4_NL", "MXFP4")]:
+        copies = packed_copies(torch, qmm, w)
+        x = torch.from_numpy(w.x()).cuda()
+        y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+
+        def launch(i, w=w, x=x, y=y, copies=copies):
+            qmm.qmm_matmul_packed(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
+
+        cases.append(Case(w.name + "_packed", w.kind, launch, copies, w.weight_bytes, w.flops))
     # The MXFP4 prefill workload again on the scaled FP8 x FP4 matrix cores
     # (its own, looser tolerance; activations quantized to MX FP8 in the call).
     for w in [w for w in wl.C4 if w.kind == "MXFP4" and w.M > 8]:
@@ -559,31 +572,39 @@ def main():
                 "ceiling_GBps": ceiling["GBps"], "frac_of_ceiling": round(achieved / ceiling["GBps"], 4),
                 "ceiling": ceiling}
 
-    # The prefill GEMM half of the metric: 512 x 4096 x 4096, Q8_0 and Q5_0.
+    # The prefill GEMM half of the metric: 512 x 4096 x 4096, Q8_0 and Q5_0,
+    # on native GGUF rows (qmm_matmul) and on the load-time repacked records
+    # (qmm_matmul_packed, the layout the decode step reads).  The roofline
+    # block reports the slower kind in the step's layout.
     gemm = {}
     for w in wl.C3:
-        copies = make_copies(torch, w.weights())
-        x = torch.from_numpy(w.x()).cuda()
-        y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        for lay in ("native", "packed"):
+            copies = packed_copies(torch, qmm, w) if lay == "packed" else make_copies(torch, w.weights())
+            x = torch.from_numpy(w.x()).cuda()
+            y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
 
-        def launch(i, w=w, x=x, y=y, copies=copies):
-            qmm.qmm_matmul(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
+            def launch(i, w=w, x=x, y=y, copies=copies, lay=lay):
+                if lay == "packed":
+                    qmm.qmm_matmul_packed(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
+                else:
+                    qmm.qmm_matmul(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
 
-        c = Case(w.name, w.kind, launch, copies, w.weight_bytes, w.flops)
-        c.launch(0)
-        torch.cuda.synchronize()
-        gemm[w.name] = (c, describe(c, time_launches(torch, c, 32)))
-        copies.clear()
-        torch.cuda.empty_cache()
-    gname = max(gemm, key=lambda k: gemm[k][1]["us_per_launch"])
-    gcase, gd = gemm[gname]
+            name = w.name + ("_packed" if lay == "packed" else "")
+            c = Case(name, w.kind, launch, copies, w.weight_bytes, w.flops)
+            c.launch(0)
+            torch.cuda.synchronize()
+            gemm[name] = (c, describe(c, time_launches(torch, c, 32)), lay)
+            copies.clear()
+            torch.cuda.empty_cache()
+    in_layout = {k: v for k, v in gemm.items() if v[2] == ("packed" if args.layout == "packed" else "native")}
+    gname = max(in_layout, key=lambda k: in_layout[k][1]["us_per_launch"])
+    gcase, gd, _ = gemm[gname]
     gach = gcase.flops / (gd["us_per_launch"] * 1e-6) / 1e12
     roofline_gemm = {"bound": "mfma", "achieved": round(gach, 2), "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gach / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": f"qmm GEMM {gname}", "algorithmic_flops_per_launch": gcase.flops,
                      "us_per_launch": gd["us_per_launch"], "us_median": gd["us_median"],
                      "all": {k: v[1] for k, v in gemm.items()}}
-
     secondary = {}
     if not args.no_secondary:
         sec = secondary_cases(torch, qmm, wl, args.layout)

@@ -53,6 +53,11 @@ __device__ __forceinline__ u32x2 ld8(const uint8_t *p) {
   return v;
 }
 
+// Four consecutive activations as loaded (one 16- or 8-byte load).
+template <typename XT> struct XVec;
+template <> struct XVec<float> { typedef float type __attribute__((ext_vector_type(4))); };
+template <> struct XVec<_Float16> { typedef _Float16 type __attribute__((ext_vector_type(4))); };
+
 __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 __device__ __forceinline__ uint32_t as_u(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 

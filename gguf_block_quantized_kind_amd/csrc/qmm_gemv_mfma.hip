@@ -53,10 +53,6 @@ using Held = typename std::conditional<
     PACKED, typename Rec<KIND>::Packed,
     typename std::conditional<Dd::CHUNKED, typename Chunks<Dd>::Held, typename Dd::Raw>::type>::type;
 
-template <typename XT> struct XVec;
-template <> struct XVec<float> { typedef float type __attribute__((ext_vector_type(4))); };
-template <> struct XVec<_Float16> { typedef _Float16 type __attribute__((ext_vector_type(4))); };
-
 // PACKED: W is the repacked layout (the records above Rec in
 // qmm_gemv_mfma.h) instead of native rows; row_bytes is then unused.
 template <int KIND, typename XT, int MT, int S, int R, int PD, int OCC, bool ROUTED, bool PACKED>
@@ -70,7 +66,9 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   extern __shared__ u32x4 lds[];  // S rings of PD+1 k-blocks, one zero fragment, S weight stagings;
                                   // later the reduction
   using CK = Chunks<Dd>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // The wave index is uniform: in a scalar register the k-block loop below
+  // runs on scalar branches.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, G = lane >> 4;
   // Routed experts: this workgroup serves one work item, up to MT pairs
   // order[c0 ..] of expert e, whose rows start at expert e's weights.
@@ -147,12 +145,16 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   const int kb0 = (int)((int64_t)wave * nkb / S), kb1 = (int)((int64_t)(wave + 1) * nkb / S);
   Held<KIND, PACKED> raw[NS][R];
   X4 xv[NS][XS::kPerLane];
+  // Every lane issues every load (dead lanes read token 0's slice and drop
+  // it; past the wave's last k-block the last one is read again), so the
+  // loads of one call are never under a branch and the wait for k-block kb
+  // can leave the PD later k-blocks in flight.
+  const int kb_last = max(kb1 - 1, 0);
   auto issue = [&](int kb, int slot) {
+    kb = min(kb, kb_last);
 #pragma unroll
     for (int i = 0; i < XS::kPerLane; ++i) {
-      X4 v = {};
-      if (xlive[i]) __builtin_memcpy(&v, X + xoff[i] + (int64_t)kb * Dd::KB, sizeof(X4));
-      xv[slot][i] = v;
+      __builtin_memcpy(&xv[slot][i], X + xoff[i] + (int64_t)kb * Dd::KB, sizeof(X4));
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -171,100 +173,109 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   // j * RS, each chunk at its byte offset in the k-block.
   uint8_t *stage = reinterpret_cast<uint8_t *>(lds + S * (PD + 1) * kFrag + 1) + wave * 16 * CK::RS;
 #pragma unroll
-  for (int d = 0; d < PD; ++d)
-    if (kb0 + d < kb1) issue(kb0 + d, d);
+  for (int d = 0; d < PD; ++d) issue(kb0 + d, d);
 
-  for (int kb = kb0; kb < kb1; kb += NS) {
+  // Decode and multiply the k-block held in ring slot d.
+  auto consume = [&](int d) {
+    // Its activations into LDS ring slot d (pair order per half).
+    u32x4 *xk = ring + d * kFrag;
 #pragma unroll
-    for (int d = 0; d < NS; ++d) {
-      if (kb + d >= kb1) break;
-      if (kb + d + PD < kb1) issue(kb + d + PD, (d + PD) % NS);
-      // Activations of k-block kb+d into ring slot d (pair order per half).
-      u32x4 *xk = ring + d * kFrag;
+    for (int i = 0; i < XS::kPerLane; ++i) {
+      if (xdst[i] < 0) continue;
+      const X4 v = xlive[i] ? xv[d][i] : X4{};
+      const half2v p0 = {(_Float16)v[0], (_Float16)v[2]}, p1 = {(_Float16)v[1], (_Float16)v[3]};
+      u32x2 *dst = reinterpret_cast<u32x2 *>(xk) + xdst[i];
+      *dst = u32x2{as_u(p0), as_u(p1)};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const u32x4 *xr = j < MT ? xk + j * 4 + G : zero;
+    const int xstep = j < MT ? MT * 4 : 0;
+    half8 a[Dd::NSTEP];
+    floatx4 xsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < XS::kPerLane; ++i) {
-        if (xdst[i] < 0) continue;
-        const X4 v = xv[d][i];
-        const half2v p0 = {(_Float16)v[0], (_Float16)v[2]}, p1 = {(_Float16)v[1], (_Float16)v[3]};
-        u32x2 *dst = reinterpret_cast<u32x2 *>(xk) + xdst[i];
-        *dst = u32x2{as_u(p0), as_u(p1)};
+    for (int st = 0; st < Dd::NSTEP; ++st) {
+      a[st] = __builtin_bit_cast(half8, xr[st * xstep]);
+      if constexpr (Dd::HAS_MIN) {
+        const _Float16 v = Dd::ind(st, G, j) ? (_Float16)1.0f : (_Float16)0.0f;
+        xsum = mfma16(half8{v, v, v, v, v, v, v, v}, a[st], xsum);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const u32x4 *xr = j < MT ? xk + j * 4 + G : zero;
-      const int xstep = j < MT ? MT * 4 : 0;
-      half8 a[Dd::NSTEP];
-      floatx4 xsum = {0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int st = 0; st < Dd::NSTEP; ++st) {
-        a[st] = __builtin_bit_cast(half8, xr[st * xstep]);
-        if constexpr (Dd::HAS_MIN) {
-          const _Float16 v = Dd::ind(st, G, j) ? (_Float16)1.0f : (_Float16)0.0f;
-          xsum = mfma16(half8{v, v, v, v, v, v, v, v}, a[st], xsum);
-        }
-      }
+    for (int r = 0; r < R; ++r) {
+      typename Dd::Raw fr;  // the decoder's fields for this tile and k-block
+      if constexpr (PACKED) {
+        fr = Rec<KIND>::unpack(raw[d][r], G);
+      } else if constexpr (Dd::CHUNKED) {
+        // Stage the tile's k-block in LDS, then read the decoder's fields.
+        uint8_t *row = stage + j * CK::RS;
+        constexpr int rem = Dd::BYTES - 16 * (CK::C - 1);  // new bytes in the last chunk
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        typename Dd::Raw fr;  // the decoder's fields for this tile and k-block
-        if constexpr (PACKED) {
-          fr = Rec<KIND>::unpack(raw[d][r], G);
-        } else if constexpr (Dd::CHUNKED) {
-          // Stage the tile's k-block in LDS, then read the decoder's fields.
-          uint8_t *row = stage + j * CK::RS;
-          constexpr int rem = Dd::BYTES - 16 * (CK::C - 1);  // new bytes in the last chunk
-#pragma unroll
-          for (int i = 0; i < CK::L; ++i) {
-            const int c = 4 * i + G;
-            if (c >= CK::C) continue;
-            const u32x4 v = raw[d][r].c[i];
-            if constexpr (rem == 16) {
+        for (int i = 0; i < CK::L; ++i) {
+          const int c = 4 * i + G;
+          if (c >= CK::C) continue;
+          const u32x4 v = raw[d][r].c[i];
+          if constexpr (rem == 16) {
+            *reinterpret_cast<u32x4 *>(row + 16 * c) = v;
+          } else {
+            if (c < CK::C - 1) {
               *reinterpret_cast<u32x4 *>(row + 16 * c) = v;
+            } else if constexpr (rem == 8) {  // the last chunk overlaps: store its new bytes
+              *reinterpret_cast<u32x2 *>(row + 16 * c) = u32x2{v[2], v[3]};
             } else {
-              if (c < CK::C - 1) {
-                *reinterpret_cast<u32x4 *>(row + 16 * c) = v;
-              } else if constexpr (rem == 8) {  // the last chunk overlaps: store its new bytes
-                *reinterpret_cast<u32x2 *>(row + 16 * c) = u32x2{v[2], v[3]};
-              } else {
-                static_assert(rem == 2, "last chunk layout");
-                *reinterpret_cast<uint16_t *>(row + 16 * c) = (uint16_t)(v[3] >> 16);
-              }
+              static_assert(rem == 2, "last chunk layout");
+              *reinterpret_cast<uint16_t *>(row + 16 * c) = (uint16_t)(v[3] >> 16);
             }
           }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          Dd::load(row, G, fr);
-        } else {
-          fr = raw[d][r];
         }
-        const typename Dd::Sc sc = Dd::prep(fr, G);
-        if constexpr (Dd::STEP_SCALE) {
-#pragma unroll
-          for (int st = 0; st < Dd::NSTEP; ++st) {
-            const floatx4 D = mfma16(a[st], Dd::bop(fr, sc, st, 0), floatx4{0.f, 0.f, 0.f, 0.f});
-            acc[r] = Dd::post_step(acc[r], D, fr, st);
-          }
-        } else {
-          floatx4 D[Dd::NPART];
-#pragma unroll
-          for (int p = 0; p < Dd::NPART; ++p) D[p] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int st = 0; st < Dd::NSTEP; ++st)
-#pragma unroll
-            for (int p = 0; p < Dd::NPART; ++p) D[p] = mfma16(a[st], Dd::bop(fr, sc, st, p), D[p]);
-          acc[r] = Dd::post(acc[r], D, xsum, sc);
-        }
-        if constexpr (Dd::CHUNKED && !PACKED) {
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();  // the staging is rewritten by the next tile
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        Dd::load(row, G, fr);
+      } else {
+        fr = raw[d][r];
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();  // slot d is rewritten NS k-blocks later
+      const typename Dd::Sc sc = Dd::prep(fr, G);
+      if constexpr (Dd::STEP_SCALE) {
+#pragma unroll
+        for (int st = 0; st < Dd::NSTEP; ++st) {
+          const floatx4 D = mfma16(a[st], Dd::bop(fr, sc, st, 0), floatx4{0.f, 0.f, 0.f, 0.f});
+          acc[r] = Dd::post_step(acc[r], D, fr, st);
+        }
+      } else {
+        floatx4 D[Dd::NPART];
+#pragma unroll
+        for (int p = 0; p < Dd::NPART; ++p) D[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < Dd::NSTEP; ++st)
+#pragma unroll
+          for (int p = 0; p < Dd::NPART; ++p) D[p] = mfma16(a[st], Dd::bop(fr, sc, st, p), D[p]);
+        acc[r] = Dd::post(acc[r], D, xsum, sc);
+      }
+      if constexpr (Dd::CHUNKED && !PACKED) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();  // the staging is rewritten by the next tile
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // slot d is rewritten NS k-blocks later
+  };
+  // Whole rounds of NS k-blocks: every round issues NS refills, never under a
+  // branch, so each wait leaves the PD newer k-blocks in flight.  The last
+  // cnt % NS k-blocks (already issued) follow.
+  const int cnt = max(kb1 - kb0, 0), full = cnt - cnt % NS;
+  for (int i = 0; i < full; i += NS) {
+#pragma unroll
+    for (int d = 0; d < NS; ++d) {
+      issue(kb0 + i + d + PD, (d + PD) % NS);
+      consume(d);
     }
   }
+#pragma unroll
+  for (int d = 0; d < NS - 1; ++d)
+    if (d < cnt - full) consume(d);
 
   if constexpr (S > 1) {
     __syncthreads();  // every wave is done with its ring
@@ -397,6 +408,28 @@ static hipError_t run_packed(const uint8_t *P, const void *x, int x_f16, float *
     case 42: if (M <= 1) return run<KIND, 1, 2, 1, 2, 4, false, true>(P, x, x_f16, y, M, N, K, s); break;
     case 43: if (M <= 1) return run<KIND, 1, 8, 1, 1, 4, false, true>(P, x, x_f16, y, M, N, K, s); break;
     case 44: if (M <= 1) return run<KIND, 1, 2, 1, 2, 3, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 45: if (M > 4) return run<KIND, 8, 4, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 46: if (M > 4) return run<KIND, 8, 2, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 47: if (M > 4) return run<KIND, 8, 8, 2, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 48: if (M > 4) return run<KIND, 8, 2, 4, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 49: if (M > 4) return run<KIND, 8, 4, 4, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 50: if (M > 4) return run<KIND, 8, 8, 1, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 51: if (M > 4) return run<KIND, 8, 4, 1, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 52: if (M > 4) return run<KIND, 8, 4, 1, 3, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 53: if (M <= 1) return run<KIND, 1, 4, 2, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 54: if (M <= 1) return run<KIND, 1, 2, 1, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 55: if (M <= 1) return run<KIND, 1, 2, 2, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 56: if (M <= 1) return run<KIND, 1, 4, 1, 3, 4, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 57: if (M > 4) return run<KIND, 8, 2, 2, 1, 2, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 58: if (M > 4) return run<KIND, 8, 2, 2, 1, 3, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 59: if (M > 4) return run<KIND, 8, 4, 2, 1, 2, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 60: if (M > 4) return run<KIND, 8, 4, 2, 1, 3, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 61: if (M > 4) return run<KIND, 8, 2, 1, 1, 3, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 62: if (M > 4) return run<KIND, 8, 4, 1, 1, 4, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 63: if (M <= 1) return run<KIND, 1, 2, 1, 2, 2, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 64: if (M <= 1) return run<KIND, 1, 4, 1, 1, 3, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 65: if (M <= 1) return run<KIND, 1, 4, 1, 2, 3, false, true>(P, x, x_f16, y, M, N, K, s); break;
+    case 66: if (M <= 1) return run<KIND, 1, 8, 1, 1, 3, false, true>(P, x, x_f16, y, M, N, K, s); break;
     default: break;
   }
 #else
@@ -444,6 +477,9 @@ hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f
 #else
   constexpr int cfg = 0;
 #endif
+  // Two to eight tokens: the kernel that stages activations per workgroup
+  // (tuning shapes below 100 select this file's kernel instead).
+  if (M > 1 && (cfg == 0 || cfg >= 100)) return launch_gemv_xs(kind, P, x, x_f16, y, M, N, K, s, cfg);
   switch (kind) {
     case Q4_K: return gv::run_packed<Q4_K>(P, x, x_f16, y, M, N, K, s, cfg);
     case Q6_K: return gv::run_packed<Q6_K>(P, x, x_f16, y, M, N, K, s, cfg);

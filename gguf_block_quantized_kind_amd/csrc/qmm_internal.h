@@ -28,6 +28,11 @@ bool packed_supported(int kind);
 hipError_t launch_repack(int kind, const uint8_t *W, void *P, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
                               int64_t K, hipStream_t s);
+// The 2-to-8-token form of that GEMV (qmm_gemv_xs.hip): activations staged
+// once per workgroup; cfg picks a tuning shape in -DQMM_TUNING builds (0: the
+// default shape).
+hipError_t launch_gemv_xs(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
+                          int64_t K, hipStream_t s, int cfg = 0);
 
 // The prefill GEMM over repacked weights (any M; qmm_gemm_pk.hip), for the
 // kinds gemm_packed_supported names; P offsets must fit in 32 bits.

@@ -75,6 +75,24 @@ def test_gemv_packed_parity(oracle_mod, kind, xdt):
 
 
 @pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("N,K", [(300, 2816), (40, 4096), (17, 512), (4500, 512)])
+def test_gemv_packed_two_to_eight_tokens(oracle_mod, kind, N, K):
+    """The 2-to-8-token kernel: K split over k-parts unevenly (11
+    k-blocks: a k-part idles a round; 2 k-blocks), whole and remainder
+    rounds of the weight pipeline, ragged tiles (N = 17, 300), and
+    more tiles than compute units (N = 4500: workgroups of one and two
+    tiles, waves without a tile)."""
+    g = wl.rng("gpu_gemv_packed_xs", f"{kind}_{N}_{K}")
+    W = wl.random_weights(kind, N, K, g)
+    P = packed(kind, dev(W), N, K)
+    for M, dt in ((2, np.float32), (4, np.float16), (6, np.float32), (8, np.float16), (8, np.float32)):
+        X = wl.activations((M, K), dt, g)
+        got = gemv(kind, P, X, N)
+        Y, B = oracle_mod.matmul(kind, W, K, X)
+        assert_within_bound(got, Y, B, f"{kind} M={M} N={N} K={K} {dt.__name__}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
 def test_gemv_packed_unit_vectors_return_the_weights(oracle_mod, kind):
     N, K = 40, 512
     W = wl.random_weights(kind, N, K, wl.rng("gpu_packed_unit", kind))

@@ -478,8 +478,12 @@ hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f
   constexpr int cfg = 0;
 #endif
   // Two to eight tokens: the kernel that stages activations per workgroup
-  // (tuning shapes below 100 select this file's kernel instead).
+  // (tuning shapes below 100 select this file's kernels instead).
   if (M > 1 && (cfg == 0 || cfg >= 100)) return launch_gemv_xs(kind, P, x, x_f16, y, M, N, K, s, cfg);
+  // One token, Q4_K or Q6_K: the kernel that applies sub-block scales after
+  // the products (tuning shapes from 200 up).
+  if (M == 1 && gemv_t1_supported(kind) && (cfg == 0 || cfg >= 200))
+    return launch_gemv_t1(kind, P, x, x_f16, y, N, K, s, cfg);
   switch (kind) {
     case Q4_K: return gv::run_packed<Q4_K>(P, x, x_f16, y, M, N, K, s, cfg);
     case Q6_K: return gv::run_packed<Q6_K>(P, x, x_f16, y, M, N, K, s, cfg);

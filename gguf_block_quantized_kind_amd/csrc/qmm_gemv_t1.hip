@@ -1,0 +1,288 @@
+// qmm_gemv_t1.hip -- the single-token decode GEMV over repacked Q4_K and
+// Q6_K weights.
+//
+// Rows of A as sub-block selectors.  With one token, 15 of the 16 A rows of
+// v_mfma_f32_16x16x32_f16 would hold zeros.  Here, at each MFMA step, lane
+// group G's 8 activations go into the A row of the sub-block that group's
+// weights belong to at that step (every other row of that group's columns
+// is zero), so row r of D collects one sub-block's partial dot product and
+// nothing else.  The sub-block scales and minimums are then applied to D in
+// f32 once per k-block, instead of being folded into every B element:
+//
+//   Q4_K  B holds each raw 4-bit code as an f16 subnormal: the nibble masked
+//         into the low mantissa bits is q * 2^-24 (a high nibble left in
+//         place, 16q * 2^-24), one AND per two codes.  D rows 4G and 4G + 1
+//         are sub-blocks 2G and 2G + 1 of lane group G (low and high
+//         nibbles), later scaled by d * sc * 2^24 (2^20).  The sums of the
+//         activations per sub-block, for the minimum term, come from the
+//         same A against a B of ones.
+//   Q6_K  B holds q - 32 exactly (the 6-bit code under the f16 1024 offset,
+//         removed by one packed add or fma).  D row 8h + 2g + a is sub-block
+//         8h + 2g + a (half h, quarter g, byte lane a of the decoder in
+//         qmm_gemv_mfma.h), later scaled by d * sc.
+//
+// Every product is exact in f32 (an f16 activation times a small integer, or
+// times a small integer times 2^-24) and the MFMA accumulates in f32, so the
+// error bound of the folded decoders holds unchanged: the activations rounded
+// once to f16, then f32 sums.
+//
+// Work split and pipeline as the single-token shapes of qmm_gemv_mfma.hip: a
+// workgroup of S waves owns one 16-row tile and wave w takes k-blocks
+// [w * n / S, (w + 1) * n / S) with PD k-blocks in flight; every load is
+// issued on every path (clamped past the wave's last k-block), so no wait is
+// widened by a branch.
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "qmm_gemv_mfma.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace gv {
+
+template <int KIND> struct T1;
+
+template <> struct T1<Q4_K> {
+  using Dd = DecQ4K;
+  using Raw = DecQ4K::Raw;
+  static constexpr bool HAS_MIN = true;
+  static constexpr int NSEL = 2;  // A-row groups: steps 0-3 and 4-7
+  __device__ static int sel_of_step(int s) { return s >> 2; }
+  // The A row lane group G fills in selector group c: sub-block 2G + c.
+  __device__ static int arow(int c, int G) { return 4 * G + c; }
+  struct Sc { float f0, f1, g0, g1; };
+  __device__ static Sc prep(const Raw &r, int G) {
+    // Scales and mins of sub-blocks 2G, 2G + 1 (the 12-byte pack; Vulkore
+    // quant_test.cpp, ref::q4k_scale_min), two 8-bit lanes at once.
+    const int c = 16 * (G & 1);
+    const uint32_t a = r.hdr.y >> c, b = r.hdr.z >> c, e = r.hdr.w >> c;
+    uint32_t sc2, mn2;
+    if (G < 2) {
+      sc2 = a & 0x3F3Fu;
+      mn2 = b & 0x3F3Fu;
+    } else {
+      sc2 = (e & 0x0F0Fu) | ((a >> 2) & 0x3030u);
+      mn2 = ((e >> 4) & 0x0F0Fu) | ((b >> 2) & 0x3030u);
+    }
+    const float d = lo_f16(r.hdr.x), dmin = hi_f16(r.hdr.x);
+    Sc s;
+    s.f0 = (d * 16777216.0f) * (float)(sc2 & 0xFFu);        // codes arrive as q * 2^-24
+    s.f1 = (d * 1048576.0f) * (float)((sc2 >> 8) & 0xFFu);  // and as 16q * 2^-24
+    s.g0 = -dmin * (float)(mn2 & 0xFFu);
+    s.g1 = -dmin * (float)((mn2 >> 8) & 0xFFu);
+    return s;
+  }
+  __device__ static half8 bop(const Raw &r, int st) {
+    const int w = st & 3;
+    const uint32_t v0 = w < 2 ? (w == 0 ? r.q0.x : r.q0.z) : (w == 2 ? r.q1.x : r.q1.z);
+    const uint32_t v1 = w < 2 ? (w == 0 ? r.q0.y : r.q0.w) : (w == 2 ? r.q1.y : r.q1.w);
+    const uint32_t m = st < 4 ? 0x000F000Fu : 0x00F000F0u;
+    return pack8(v0 & m, (v0 >> 8) & m, v1 & m, (v1 >> 8) & m);
+  }
+  // Lane (j, G) holds D rows 4G .. 4G + 3: sub-blocks 2G, 2G + 1, then zeros.
+  __device__ static float post(float acc, floatx4 D, floatx4 X, const Sc &s) {
+    return acc + s.f0 * D[0] + s.f1 * D[1] + s.g0 * X[0] + s.g1 * X[1];
+  }
+};
+
+template <> struct T1<Q6_K> {
+  using Dd = DecQ6K;
+  using Raw = DecQ6K::Raw;
+  static constexpr bool HAS_MIN = false;
+  static constexpr int NSEL = 4;  // A-row groups: quarters g = step / 2
+  __device__ static int sel_of_step(int s) { return s >> 1; }
+  // Group G = 2h + a at quarter g: sub-block 8h + 2g + a.
+  __device__ static int arow(int g, int G) { return 8 * (G >> 1) + 2 * g + (G & 1); }
+  struct Sc { float sc[4], d; };
+  __device__ static Sc prep(const Raw &r, int G) {
+    // Lane (j, G) holds D rows 4G .. 4G + 3, sub-blocks 4G + q: bytes
+    // 4(G & 1) + q of the eight scales this lane loaded (8 (G >> 1) ..).
+    const uint32_t w = (G & 1) ? r.sc.y : r.sc.x;
+    Sc s;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s.sc[q] = (float)(int)(int8_t)(uint8_t)((w >> (8 * q)) & 0xFFu);
+    s.d = lo_f16(r.d);
+    return s;
+  }
+  __device__ static half8 bop(const Raw &r, int st) {
+    const int g = st >> 1, w = 2 * (st & 1);
+    const u32x4 &ql = (g & 1) ? r.ql1 : r.ql0;
+    const uint32_t q0 = w == 0 ? ql.x : ql.z, q1 = w == 0 ? ql.y : ql.w;
+    const uint32_t h0 = w == 0 ? r.qh.x : r.qh.z, h1 = w == 0 ? r.qh.y : r.qh.w;
+    // As the folded decoder: low case, nibble at bits 0-3 and the two high
+    // bits moved to 4-5 (e = 1024 + q); high case, nibble left at 4-7 and
+    // the high bits moved to 8-9 (e = 1024 + 16q).
+    const uint32_t qm = g < 2 ? 0x000F000Fu : 0x00F000F0u;
+    const uint32_t hm = g < 2 ? 0x00300030u : 0x03000300u;
+    const int up = (g & 1) ? 2 : 4;
+    const uint32_t e0 = and_or(h0 << up, hm, mag(q0, qm));
+    const uint32_t e1 = and_or(h0 >> (8 - up), hm, mag(q0 >> 8, qm));
+    const uint32_t e2 = and_or(h1 << up, hm, mag(q1, qm));
+    const uint32_t e3 = and_or(h1 >> (8 - up), hm, mag(q1 >> 8, qm));
+    // q - 32: e - 1056, or e / 16 - 96 (both exact).
+    if (g < 2) {
+      const half2v off = {-1056.0f16, -1056.0f16};
+      return pack8(as_u(as_h2(e0) + off), as_u(as_h2(e1) + off), as_u(as_h2(e2) + off), as_u(as_h2(e3) + off));
+    }
+    const uint32_t f = 0x2C002C00u, b = 0xD600D600u;  // (1/16, 1/16), (-96, -96)
+    return pack8(fold(e0, f, b), fold(e1, f, b), fold(e2, f, b), fold(e3, f, b));
+  }
+  __device__ static float post(float acc, floatx4 D, floatx4, const Sc &s) {
+    return acc + s.d * (s.sc[0] * D[0] + s.sc[1] * D[1] + s.sc[2] * D[2] + s.sc[3] * D[3]);
+  }
+};
+
+template <int KIND, typename XT, int S, int PD, int OCC>
+__global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void gemv_t1_kernel(
+    const uint8_t *__restrict__ P, const XT *__restrict__ X, float *__restrict__ Y, int64_t N, int K) {
+  using Tr = T1<KIND>;
+  using Dd = typename Tr::Dd;
+  using Raw = typename Tr::Raw;
+  using X4 = typename XVec<XT>::type;
+  constexpr int kFrag = Dd::NSTEP * 4;  // 16-byte fragments of one k-block (step s, group G at 4s + G)
+  constexpr int NS = PD + 1;
+  constexpr int64_t kRec = 16 * Dd::BYTES;
+  // LDS: kFrag zero fragments (read by lanes whose A row is empty), then S
+  // rings of NS k-blocks; later the reduction.
+  extern __shared__ u32x4 lds[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int j = lane & 15, G = lane >> 4;
+  const int64_t tile = blockIdx.x;
+  const int nkb = K / Dd::KB;
+  const int kb0 = (int)((int64_t)wave * nkb / S), kb1 = (int)((int64_t)(wave + 1) * nkb / S);
+  const int kb_last = max(kb1 - 1, 0);
+  u32x4 *ring = lds + kFrag + wave * NS * kFrag;
+  for (int i = threadIdx.x; i < kFrag; i += 64 * S) lds[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  // Lane h = lane converts elements x_off(s, G', h & 1) + [0, 4) of the
+  // k-block: fragment f = h / 2 = 4s + G', half h & 1.
+  const int xoff = Dd::x_off(lane >> 3, (lane >> 1) & 3, lane & 1);
+  // A fragment base of selector group c in slot d: this lane's fragment run
+  // if its row is that group's A row, else the zero run.
+  const u32x4 *abase[NS][Tr::NSEL];
+#pragma unroll
+  for (int d = 0; d < NS; ++d)
+#pragma unroll
+    for (int c = 0; c < Tr::NSEL; ++c) abase[d][c] = (j == Tr::arow(c, G) ? ring + d * kFrag : lds) + G;
+
+  const uint8_t *wt = P + tile * nkb * kRec;
+  typename Rec<KIND>::Packed raw[NS];
+  X4 xv[NS];
+  auto issue = [&](int kb, int slot) {
+    kb = min(kb, kb_last);
+    __builtin_memcpy(&xv[slot], X + xoff + (int64_t)kb * Dd::KB, sizeof(X4));
+    Rec<KIND>::load(wt + kb * kRec, lane, j, G, raw[slot]);
+  };
+  float acc = 0.0f;
+  const half8 ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
+  auto consume = [&](int d) {
+    {
+      const X4 v = xv[d];
+      const half2v p0 = {(_Float16)v[0], (_Float16)v[2]}, p1 = {(_Float16)v[1], (_Float16)v[3]};
+      reinterpret_cast<u32x2 *>(ring + d * kFrag)[lane] = u32x2{as_u(p0), as_u(p1)};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const Raw fr = Rec<KIND>::unpack(raw[d], G);
+    const typename Tr::Sc sc = Tr::prep(fr, G);
+    floatx4 D = {0.f, 0.f, 0.f, 0.f}, Xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < Dd::NSTEP; ++st) {
+      const half8 a = __builtin_bit_cast(half8, abase[d][Tr::sel_of_step(st)][4 * st]);
+      if constexpr (Tr::HAS_MIN) Xs = mfma16(a, ones, Xs);
+      D = mfma16(a, Tr::bop(fr, st), D);
+    }
+    acc = Tr::post(acc, D, Xs, sc);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // slot d is rewritten NS k-blocks later
+  };
+
+#pragma unroll
+  for (int d = 0; d < PD; ++d) issue(kb0 + d, d);
+  const int cnt = max(kb1 - kb0, 0), full = cnt - cnt % NS;
+  for (int i = 0; i < full; i += NS) {
+#pragma unroll
+    for (int d = 0; d < NS; ++d) {
+      issue(kb0 + i + d + PD, (d + PD) % NS);
+      consume(d);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < NS - 1; ++d)
+    if (d < cnt - full) consume(d);
+
+  // Row j's sum is spread over the four lane groups, then over the S waves.
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  if constexpr (S > 1) {
+    __syncthreads();  // every wave is done with its ring
+    float *red = reinterpret_cast<float *>(lds);
+    if (wave > 0 && lane < 16) red[(wave - 1) * 16 + lane] = acc;
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < S - 1; ++w) acc += red[w * 16 + (lane & 15)];
+  }
+  const int64_t row = tile * 16 + j;
+  if (lane < 16 && row < N) Y[row] = acc;
+}
+
+template <int KIND, int S, int PD, int OCC = 1>
+static hipError_t run_t1(const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K, hipStream_t s) {
+  constexpr int kFrag = T1<KIND>::Dd::NSTEP * 4;
+  const size_t lds = std::max<size_t>((size_t)(1 + S * (PD + 1)) * kFrag * 16, (size_t)(S - 1) * 16 * 4);
+  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * S);
+  if (x_f16)
+    hipLaunchKernelGGL((gemv_t1_kernel<KIND, _Float16, S, PD, OCC>), grid, block, lds, s, P, (const _Float16 *)x, y,
+                       N, (int)K);
+  else
+    hipLaunchKernelGGL((gemv_t1_kernel<KIND, float, S, PD, OCC>), grid, block, lds, s, P, (const float *)x, y, N,
+                       (int)K);
+  return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t run_t1_k(const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K, hipStream_t s,
+                           int cfg) {
+#ifdef QMM_TUNING
+  switch (cfg) {
+    case 201: return run_t1<KIND, 4, 1, 4>(P, x, x_f16, y, N, K, s);
+    case 202: return run_t1<KIND, 4, 1>(P, x, x_f16, y, N, K, s);
+    case 203: return run_t1<KIND, 4, 2>(P, x, x_f16, y, N, K, s);
+    case 204: return run_t1<KIND, 2, 1>(P, x, x_f16, y, N, K, s);
+    case 205: return run_t1<KIND, 2, 2>(P, x, x_f16, y, N, K, s);
+    case 206: return run_t1<KIND, 2, 3>(P, x, x_f16, y, N, K, s);
+    case 207: return run_t1<KIND, 8, 1>(P, x, x_f16, y, N, K, s);
+    case 208: return run_t1<KIND, 8, 2>(P, x, x_f16, y, N, K, s);
+    case 209: return run_t1<KIND, 4, 3>(P, x, x_f16, y, N, K, s);
+    case 210: return run_t1<KIND, 1, 3>(P, x, x_f16, y, N, K, s);
+    case 211: return run_t1<KIND, 4, 2, 3>(P, x, x_f16, y, N, K, s);
+    case 212: return run_t1<KIND, 16, 1>(P, x, x_f16, y, N, K, s);
+    default: break;
+  }
+#else
+  (void)cfg;
+#endif
+  // Two waves per tile, one k-block in flight (measured best for both kinds
+  // at 14336 x 4096 among 1 to 16 waves and 1 to 3 k-blocks in flight).
+  return run_t1<KIND, 2, 1>(P, x, x_f16, y, N, K, s);
+}
+
+}  // namespace gv
+
+bool gemv_t1_supported(int kind) { return kind == Q4_K || kind == Q6_K; }
+
+hipError_t launch_gemv_t1(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K,
+                          hipStream_t s, int cfg) {
+  switch (kind) {
+    case Q4_K: return gv::run_t1_k<Q4_K>(P, x, x_f16, y, N, K, s, cfg);
+    case Q6_K: return gv::run_t1_k<Q6_K>(P, x, x_f16, y, N, K, s, cfg);
+    default: break;
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace qmm

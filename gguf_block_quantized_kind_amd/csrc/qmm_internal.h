@@ -33,6 +33,11 @@ hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f
 // default shape).
 hipError_t launch_gemv_xs(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
                           int64_t K, hipStream_t s, int cfg = 0);
+// Its single-token form for Q4_K and Q6_K (qmm_gemv_t1.hip): sub-blocks
+// kept apart in the rows of the matrix-core product, scales applied after it.
+bool gemv_t1_supported(int kind);
+hipError_t launch_gemv_t1(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K,
+                          hipStream_t s, int cfg = 0);
 
 // The prefill GEMM over repacked weights (any M; qmm_gemm_pk.hip), for the
 // kinds gemm_packed_supported names; P offsets must fit in 32 bits.

@@ -108,6 +108,23 @@ def test_gemv_packed_unit_vectors_return_the_weights(oracle_mod, kind):
             assert np.array_equal(got[i], want[:, k]), f"{kind} column {k}"
 
 
+@pytest.mark.parametrize("kind", KINDS)
+def test_gemv_packed_one_token_unit_vectors_return_the_weights(oracle_mod, kind):
+    """One token (the kernel that scales sub-blocks after the products for
+    Q4_K and Q6_K): x = e_k returns column k of the weights exactly, also
+    with stress scales (signed f16 scales from about 2^-7 to 2^7)."""
+    N, K = 40, 768
+    for scales in (("config",) if kind == "MXFP4" else ("config", "stress")):
+        W = wl.random_weights(kind, N, K, wl.rng("gpu_packed_unit1", f"{kind}_{scales}"), scales=scales)
+        want = oracle_mod.dequant(kind, W).reshape(N, K).astype(np.float32)
+        P = packed(kind, dev(W), N, K)
+        for k in (0, 1, 15, 16, 31, 32, 63, 64, 127, 128, 200, 255, 256, 511, 600, 767):
+            X = np.zeros((1, K), dtype=np.float32)
+            X[0, k] = 1.0
+            got = gemv(kind, P, X, N)
+            assert np.array_equal(got[0], want[:, k]), f"{kind} {scales} column {k}"
+
+
 @pytest.mark.parametrize("kind", ["Q4_K", "Q4_0", "MXFP4"])
 def test_gemv_packed_single_row_and_single_kblock(oracle_mod, kind):
     for N, K in ((1, 256), (3, 256), (16, 256), (33, 256)):

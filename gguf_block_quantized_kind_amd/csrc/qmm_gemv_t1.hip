@@ -143,8 +143,8 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   constexpr int kFrag = Dd::NSTEP * 4;  // 16-byte fragments of one k-block (step s, group G at 4s + G)
   constexpr int NS = PD + 1;
   constexpr int64_t kRec = 16 * Dd::BYTES;
-  // LDS: kFrag zero fragments (read by lanes whose A row is empty), then S
-  // rings of NS k-blocks; later the reduction.
+  // LDS per wave: kFrag zero fragments (read by lanes whose A row is empty)
+  // and a ring of NS k-blocks; later the reduction.
   extern __shared__ u32x4 lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, G = lane >> 4;
@@ -152,9 +152,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   const int nkb = K / Dd::KB;
   const int kb0 = (int)((int64_t)wave * nkb / S), kb1 = (int)((int64_t)(wave + 1) * nkb / S);
   const int kb_last = max(kb1 - 1, 0);
-  u32x4 *ring = lds + kFrag + wave * NS * kFrag;
-  for (int i = threadIdx.x; i < kFrag; i += 64 * S) lds[i] = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
+  u32x4 *zrun = lds + wave * (NS + 1) * kFrag, *ring = zrun + kFrag;
 
   // Lane h = lane converts elements x_off(s, G', h & 1) + [0, 4) of the
   // k-block: fragment f = h / 2 = 4s + G', half h & 1.
@@ -165,7 +163,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
 #pragma unroll
   for (int d = 0; d < NS; ++d)
 #pragma unroll
-    for (int c = 0; c < Tr::NSEL; ++c) abase[d][c] = (j == Tr::arow(c, G) ? ring + d * kFrag : lds) + G;
+    for (int c = 0; c < Tr::NSEL; ++c) abase[d][c] = (j == Tr::arow(c, G) ? ring + d * kFrag : zrun) + G;
 
   const uint8_t *wt = P + tile * nkb * kRec;
   typename Rec<KIND>::Packed raw[NS];
@@ -202,6 +200,9 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
 
 #pragma unroll
   for (int d = 0; d < PD; ++d) issue(kb0 + d, d);
+  // With the first loads in flight: this wave's zero run (the wave barrier
+  // in the first consume orders it before any read).
+  if (lane < kFrag) zrun[lane] = u32x4{0u, 0u, 0u, 0u};
   const int cnt = max(kb1 - kb0, 0), full = cnt - cnt % NS;
   for (int i = 0; i < full; i += NS) {
 #pragma unroll
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
 template <int KIND, int S, int PD, int OCC = 1>
 static hipError_t run_t1(const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K, hipStream_t s) {
   constexpr int kFrag = T1<KIND>::Dd::NSTEP * 4;
-  const size_t lds = std::max<size_t>((size_t)(1 + S * (PD + 1)) * kFrag * 16, (size_t)(S - 1) * 16 * 4);
+  const size_t lds = std::max<size_t>((size_t)S * (PD + 2) * kFrag * 16, (size_t)(S - 1) * 16 * 4);
   const dim3 grid((unsigned)((N + 15) / 16)), block(64 * S);
   if (x_f16)
     hipLaunchKernelGGL((gemv_t1_kernel<KIND, _Float16, S, PD, OCC>), grid, block, lds, s, P, (const _Float16 *)x, y,

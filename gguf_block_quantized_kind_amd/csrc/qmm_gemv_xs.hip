@@ -41,7 +41,7 @@ constexpr int kWaitLds = 0xC07F;
 template <int KIND, typename XT, int MT, int T, int S, int PD, int XD>
 __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__restrict__ P,
                                                              const XT *__restrict__ X, float *__restrict__ Y,
-                                                             int M, int64_t N, int K) {
+                                                             int M, int64_t N, int K, int per_wg, int extra) {
   using Dd = Dec<KIND>;
   using X4 = typename XVec<XT>::type;
   constexpr int kFrag = Dd::NSTEP * MT * 4;  // 16-byte fragments per k-block (layout of qmm_gemv_mfma.hip)
@@ -58,8 +58,10 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, G = lane >> 4;
   const int t = wave % T, kp = wave / T;
-  const int64_t ntiles = (N + 15) / 16;
-  const int64_t t0 = (int64_t)blockIdx.x * ntiles / gridDim.x, t1 = (int64_t)(blockIdx.x + 1) * ntiles / gridDim.x;
+  // Workgroup b owns tiles [t0, t1): per_wg each, one more for the first
+  // `extra` workgroups.
+  const int b = blockIdx.x;
+  const int t0 = b * per_wg + min(b, extra), t1 = t0 + per_wg + (b < extra ? 1 : 0);
   // A wave without a tile (t >= t1 - t0) stages its share of the activations
   // and loads the workgroup's last tile again (cache hits), but decodes and
   // stores nothing.
@@ -86,15 +88,6 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
     xoff[i] = xlive[i] ? tok * K + Dd::x_off(st, g2, h & 1) : 0;
     xdst[i] = in < kShare ? h : -1;
   }
-  // Halves of absent tokens stay zero in both ring slots.
-  if (threadIdx.x == 0) lds[S * 2 * kFrag] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < kPerLane; ++i)
-    if (xdst[i] >= 0 && !xlive[i]) {
-      reinterpret_cast<u32x2 *>(ring)[xdst[i]] = u32x2{0u, 0u};
-      reinterpret_cast<u32x2 *>(ring + kFrag)[xdst[i]] = u32x2{0u, 0u};
-    }
-
   const uint8_t *wt = P + tile * nkb * kRec;
   typename Rec<KIND>::Packed raw[NS];
   X4 xv[XD][kPerLane];  // activation shares of the next XD k-blocks
@@ -167,6 +160,16 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
     if (q + XD >= 0) issue_x(kb0 + q + XD, (q + XD) % XD);
     if (q + PD >= 0) issue_w(kb0 + q + PD, (q + PD) % NS);
   }
+  // With the first loads in flight: halves of absent tokens stay zero in both
+  // ring slots (the first round's barrier orders these writes before any
+  // read).
+  if (threadIdx.x == 0) lds[S * 2 * kFrag] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i)
+    if (xdst[i] >= 0 && !xlive[i]) {
+      reinterpret_cast<u32x2 *>(ring)[xdst[i]] = u32x2{0u, 0u};
+      reinterpret_cast<u32x2 *>(ring + kFrag)[xdst[i]] = u32x2{0u, 0u};
+    }
   const int full = rounds - rounds % U;
   for (int r = 0; r < full; r += U) {
 #pragma unroll
@@ -215,13 +218,14 @@ static hipError_t run_xs(const uint8_t *P, const void *x, int x_f16, float *y, i
   const size_t lds = std::max<size_t>((size_t)S * 2 * kFrag * 16 + 16, (size_t)(S - 1) * T * 64 * 16);
   const int64_t ntiles = (N + 15) / 16;
   const int64_t wgs = std::max<int64_t>((ntiles + T - 1) / T, spread ? std::min<int64_t>(ntiles, device_cus()) : 1);
+  const int per_wg = (int)(ntiles / wgs), extra = (int)(ntiles % wgs);
   const dim3 grid((unsigned)wgs), block(64 * T * S);
   if (x_f16)
     hipLaunchKernelGGL((gemv_xs_kernel<KIND, _Float16, MT, T, S, PD, XD>), grid, block, lds, s, P,
-                       (const _Float16 *)x, y, M, N, (int)K);
+                       (const _Float16 *)x, y, M, N, (int)K, per_wg, extra);
   else
     hipLaunchKernelGGL((gemv_xs_kernel<KIND, float, MT, T, S, PD, XD>), grid, block, lds, s, P, (const float *)x, y, M,
-                       N, (int)K);
+                       N, (int)K, per_wg, extra);
   return hipGetLastError();
 }
 

@@ -88,9 +88,13 @@ size_t moe_workspace_bytes(int64_t E, int64_t M, int64_t topk);
 // packed: W is E experts in the repacked layout (qmm_moe_packed); the
 // matrix-core kernel must then apply (moe_mfma_supported and 32-bit
 // activation offsets), which the caller has checked.
+// routed: the workspace already holds the routing of these ids for the same
+// number of pairs per work item (moe_item_pairs), so it is not recomputed.
 hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids, int64_t topk,
                       const void *X, int x_f16, int x_per_slot, float *Y, int64_t M, int64_t N,
-                      int64_t K, void *ws, hipStream_t s, bool packed = false);
+                      int64_t K, void *ws, hipStream_t s, bool packed = false, bool routed = false);
+// Pairs per work item launch_moe uses for these arguments (N does not enter).
+int moe_item_pairs(int kind, int64_t E, int64_t M, int64_t topk, int64_t K, bool packed);
 
 // Largest expert count the routing prologue handles.
 constexpr int64_t kMoeMaxExperts = 4096;

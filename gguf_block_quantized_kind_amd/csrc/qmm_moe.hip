@@ -162,10 +162,7 @@ static hipError_t run_moe(const uint8_t *W, int64_t E, int64_t topk, const void 
   return hipGetLastError();
 }
 
-hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids, int64_t topk,
-                      const void *X, int x_f16, int x_per_slot, float *Y, int64_t M, int64_t N,
-                      int64_t K, void *ws, hipStream_t s, bool packed) {
-  int32_t *wsi = static_cast<int32_t *>(ws);
+int moe_item_pairs(int kind, int64_t E, int64_t M, int64_t topk, int64_t K, bool packed) {
   const MoeLayout L{E, M * topk};
   // The matrix-core kernel addresses activations with 32-bit element offsets.
   const bool mfma = packed || (moe_mfma_supported(kind, K) && L.P * K < ((int64_t)1 << 31));
@@ -173,17 +170,28 @@ hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids,
   // uniform routing gives experts 16 pairs on average, 8 from 4 pairs on
   // average, else 1 (an 8-pair item that carries one or two pairs costs
   // more than streaming the expert once per pair).
-  const int mt = !mfma ? 1 : (L.P >= 16 * E ? 16 : (L.P >= 4 * E ? 8 : 1));
+  return !mfma ? 1 : (L.P >= 16 * E ? 16 : (L.P >= 4 * E ? 8 : 1));
+}
+
+hipError_t launch_moe(int kind, const uint8_t *W, int64_t E, const int32_t *ids, int64_t topk,
+                      const void *X, int x_f16, int x_per_slot, float *Y, int64_t M, int64_t N,
+                      int64_t K, void *ws, hipStream_t s, bool packed, bool routed) {
+  int32_t *wsi = static_cast<int32_t *>(ws);
+  const MoeLayout L{E, M * topk};
+  const bool mfma = packed || (moe_mfma_supported(kind, K) && L.P * K < ((int64_t)1 << 31));
+  const int mt = moe_item_pairs(kind, E, M, topk, K, packed);
   if (mfma && mt == 1) {
     // One pair per item needs no grouping: each workgroup reads its pair's
     // expert from ids and the routing prologue is skipped.
     const MoeRoute rt{wsi, 0, 0, 0, 0, (int)topk, x_per_slot, ids, (int)E, (int)L.P};
     return launch_moe_mfma(kind, W, X, x_f16, Y, 1, N, K, rt, (int)L.P, s, packed);
   }
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), (size_t)(3 * E + 2048) * sizeof(int32_t), s, ids,
-                     M * topk, (int)E, mt, wsi);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (!routed) {
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(1024), (size_t)(3 * E + 2048) * sizeof(int32_t), s, ids,
+                       M * topk, (int)E, mt, wsi);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   if (mfma) {
     const MoeRoute rt{wsi, (int)L.offsets(), (int)L.order(), (int)L.nwork(), (int)L.work(), (int)topk, x_per_slot,
                       nullptr, (int)E, (int)L.P};

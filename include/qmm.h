@@ -132,15 +132,21 @@ int qmm_matmul(int kind, const void *W, const void *A, int a_dtype, float *C,
  * experts of K rows of N_ff elements; both in the layout of qmm_moe.  For
  * token t and slot s with e = ids[t][s] in [0, E):
  *   h = silu(W_gate[e] . X[t]) * (W_up[e] . X[t]),  silu(v) = v / (1 + e^-v)
- *   Y[t] = sum over such slots, in slot order, of topk_w[t][s] * (W_d[e] . h)
+ *   Y[t] = sum over such slots of topk_w[t][s] * (W_d[e] . h)
  * X is [M][K] f32 or f16; topk_w is [M][topk] f32; Y is [M][K] f32, 16-byte
  * aligned, overwritten.  Slots whose id lies outside [0, E) add nothing.
  * The products run as qmm_moe (each within 1e-3 sum|w||x| + 1e-6), h and
  * the combine in f32; each pair's h is divided by a power of two that
  * brings max|h| to 2^14 or below before the down product (whose matrix-core
- * path takes f16 activations), and the combine multiplies it back, exactly.  workspace: qmm_moe_ffn_workspace_bytes(E, M, topk,
- * N_ff, K) bytes, 256-byte aligned, overwritten; calls sharing it must not
- * overlap.  Errors as qmm_moe, with both matrices' shapes checked (gate/up
+ * path takes f16 activations), and the combine multiplies it back, exactly.
+ * The sum over slots runs in a fixed order (the same call gives the same
+ * bits).  With fewer than four pairs per expert on average (M * topk < 4 E),
+ * whole k-blocks (N_ff, K multiples of 256), topk <= 64 and a kind with a
+ * matrix-core decoder over the layout given (repacked: as qmm_gemv_packed;
+ * native: Q4_K, Q6_K), the FFN runs in two launches: gate/up with the
+ * SiLU-product in its epilogue, then down with the combine in its epilogue.
+ * workspace: qmm_moe_ffn_workspace_bytes(E, M, topk, N_ff, K) bytes,
+ * 256-byte aligned, overwritten; calls sharing it must not overlap.  Errors as qmm_moe, with both matrices' shapes checked (gate/up
  * first) and a NULL topk_w or misaligned Y as QMM_ERR_BAD_ARG. */
 int qmm_moe_ffn(int kind, const void *W_gu, const void *W_d, int64_t E, const int32_t *ids,
                 const float *topk_w, int64_t topk, const void *X, int x_dtype, float *Y,

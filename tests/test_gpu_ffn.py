@@ -72,6 +72,37 @@ def test_ffn_parity(oracle_mod, kind, N_ff, K):
         check(got, y, tol, f"{kind} M={M}")
 
 
+@pytest.mark.parametrize("kind", ["Q4_K", "Q6_K"])
+@pytest.mark.parametrize("packed", [False, True])
+def test_ffn_two_launches(oracle_mod, kind, packed):
+    """The two-launch FFN (fewer than four pairs per expert, whole
+    k-blocks), native and repacked: M = 1, 3, 5, 7 tokens with 16 experts,
+    top 2 (experts with zero, one and several pairs), f16 and f32
+    activations; skipped slots add nothing."""
+    E, topk, N_ff, K = 16, 2, 512, 768
+    g = wl.rng("gpu_ffn_two", f"{kind}_{packed}")
+    W_gu = wl.random_weights(kind, E * 2 * N_ff, K, g)
+    W_d = wl.random_weights(kind, E * K, N_ff, g)
+    if packed:
+        P_gu = qmm.repack_experts(kind, dev(W_gu), E, 2 * N_ff, K)
+        P_d = qmm.repack_experts(kind, dev(W_d), E, K, N_ff)
+    for M in (1, 3, 5, 7):
+        ids = wl.routing(M, E, topk, g)
+        if M > 2:
+            ids[1, 1] = -1
+        w = _weights(g, M, topk)
+        X = wl.activations((M, K), np.float32 if M == 3 else np.float16, g)
+        if packed:
+            Y = torch.full((M, K), SENTINEL, dtype=torch.float32, device="cuda")
+            ws = torch.empty(qmm.qmm_moe_ffn_workspace_bytes(E, M, topk, N_ff, K), dtype=torch.uint8, device="cuda")
+            qmm.qmm_moe_ffn_packed(kind, P_gu, P_d, E, dev(ids), dev(w), topk, dev(X), Y, M, N_ff, K, ws)
+            got = host(Y)
+        else:
+            got = run_ffn(kind, W_gu, W_d, E, ids, w, X, N_ff)
+        y, tol = oracle_mod.moe_ffn(kind, W_gu, W_d, E, N_ff, K, ids, w, X)
+        check(got, y, tol, f"{kind} packed={packed} M={M}")
+
+
 def test_ffn_f32_activations(oracle_mod):
     kind, E, topk, N_ff, K, M = "Q4_K", 4, 2, 256, 256, 7
     g = wl.rng("gpu_ffn_f32", kind)
@@ -85,10 +116,11 @@ def test_ffn_f32_activations(oracle_mod):
     check(got, y, tol, "f32 X")
 
 
-def test_ffn_full_size_sampled(oracle_mod):
+@pytest.mark.parametrize("M", [1, 16])
+def test_ffn_full_size_sampled(oracle_mod, M):
     """128 experts, top 8, gate/up [1536, 2048] and down [2048, 768] Q4_K,
-    16 tokens; the oracle computes 64 sampled output columns."""
-    e = next(x for x in wl.C5 if x.M == 16)
+    1 and 16 tokens; the oracle computes 64 sampled output columns."""
+    e = next(x for x in wl.C5 if x.M == M)
     N_ff, K = e.N_gu // 2, e.K_gu
     ids = e.ids()
     W_gu, W_d = e.w_gu(), e.w_d()

@@ -451,6 +451,163 @@ struct DecIQ4XS : StepBase {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Q5_K (176 B: d, dmin, the Q4_K scale/min pack, qh[32], qs[128]).  As Q4_K,
+// group G decodes code bytes 32G .. 32G + 31 (sub-blocks 2G, 2G + 1); the
+// fifth bit of element 64G + l (+ 32) is bit 2G (2G + 1) of qh[l].  The
+// B value sc * q, q < 32, is an exact f16 integer (sc * q <= 63 * 31).
+// ---------------------------------------------------------------------------
+struct DecQ5K {
+  static constexpr int KB = 256, NSTEP = 8, NPART = 1, BYTES = 176;
+  static constexpr bool HAS_MIN = true, CHUNKED = false, STEP_SCALE = false;
+  struct Raw { u32x4 hdr, q0, q1, h0, h1; };
+  struct Sc : DecQ4K::Sc { int sh; };  // sh = 2G: this group's fifth-bit position
+  __device__ static int x_off(int s, int G, int h) { return DecQ4K::x_off(s, G, h); }
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+    r.hdr = ld16(blk);
+    r.h0 = ld16(blk + 16);
+    r.h1 = ld16(blk + 32);
+    r.q0 = ld16(blk + 48 + 32 * G);
+    r.q1 = ld16(blk + 64 + 32 * G);
+  }
+  __device__ static Sc prep(const Raw &r, int G) {
+    Sc s;
+    static_cast<DecQ4K::Sc &>(s) = DecQ4K::prep(DecQ4K::Raw{r.hdr, r.q0, r.q1}, G);
+    s.sh = 2 * G;
+    return s;
+  }
+  __device__ static half8 bop(const Raw &r, const Sc &s, int st, int) {
+    const int w = st & 3;
+    const uint32_t v0 = w < 2 ? (w == 0 ? r.q0.x : r.q0.z) : (w == 2 ? r.q1.x : r.q1.z);
+    const uint32_t v1 = w < 2 ? (w == 0 ? r.q0.y : r.q0.w) : (w == 2 ? r.q1.y : r.q1.w);
+    // qh bytes 8w .. 8w + 7 hold the fifth bits of these eight elements.
+    const uint32_t g0 = w < 2 ? (w == 0 ? r.h0.x : r.h0.z) : (w == 2 ? r.h1.x : r.h1.z);
+    const uint32_t g1 = w < 2 ? (w == 0 ? r.h0.y : r.h0.w) : (w == 2 ? r.h1.y : r.h1.w);
+    const uint32_t a0 = g0 >> s.sh, a1 = g1 >> s.sh;
+    // Low case: the nibble at bits 0-3, the fifth bit (bit 0 of a) to bit 4:
+    // e = 1024 + q.  High case: the nibble left at bits 4-7, the fifth bit
+    // (bit 1 of a) to bit 8: e = 1024 + 16 q.
+    const bool lo = st < 4;
+    const uint32_t qm = lo ? 0x000F000Fu : 0x00F000F0u, hm = lo ? 0x00100010u : 0x01000100u;
+    const uint32_t e0 = and_or(lo ? a0 << 4 : a0 << 7, hm, mag(v0, qm));
+    const uint32_t e1 = and_or(lo ? a0 >> 4 : a0 >> 1, hm, mag(v0 >> 8, qm));
+    const uint32_t e2 = and_or(lo ? a1 << 4 : a1 << 7, hm, mag(v1, qm));
+    const uint32_t e3 = and_or(lo ? a1 >> 4 : a1 >> 1, hm, mag(v1 >> 8, qm));
+    const uint32_t f = lo ? s.f_lo : s.f_hi, b = lo ? s.b_lo : s.b_hi;
+    return pack8(fold(e0, f, b), fold(e1, f, b), fold(e2, f, b), fold(e3, f, b));
+  }
+  __device__ static bool ind(int s, int G, int i) { return DecQ4K::ind(s, G, i); }
+  __device__ static floatx4 post(floatx4 acc, const floatx4 *D, floatx4 X, const Sc &s) {
+    return DecQ4K::post(acc, D, X, s);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Q2_K (84 B: scales[16] (low nibble scale, high nibble min), qs[64], d,
+// dmin) and Q3_K (110 B: hmask[32], qs[64], twelve bytes of 6-bit scales,
+// d).  Element 128n + 32j + l holds bits 2j, 2j + 1 of qs[32n + l]
+// (Q3_K: plus the high-mask bit 4n + j of hmask[l]); sixteen sub-blocks of
+// 16 elements.  Group G = 2n + a decodes qs bytes 32n + 16a .. + 15, so
+// step s = 2j + b (bytes 8b .. 8b + 7, shift 2j) lies in sub-block
+// 8n + 2j + a, and group G's four sub-blocks (j = 0 .. 3) take A rows
+// 4G + j for their activation sums.
+// ---------------------------------------------------------------------------
+struct DecQ2K {
+  static constexpr int KB = 256, NSTEP = 8, NPART = 1, BYTES = 84;
+  static constexpr bool HAS_MIN = true, CHUNKED = false, STEP_SCALE = false;
+  struct Raw { u32x4 sc, q; uint32_t dd; };
+  struct Sc { uint32_t f[4], b[4]; float d, mn[4]; };
+  __device__ static int x_off(int s, int G, int h) { return DecQ6K::x_off(s, G, h); }
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+    r.sc = ld16(blk);
+    r.q = ld16(blk + 16 + 16 * G);
+    r.dd = rd32(blk + 80);
+  }
+  __device__ static Sc prep(const Raw &r, int G) {
+    Sc s;
+    const float d = lo_f16(r.dd), dmin = hi_f16(r.dd);
+    s.d = d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 8 * (G >> 1) + 2 * j + (G & 1);  // the step's sub-block
+      const uint32_t byte = (r.sc[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      const _Float16 c = (_Float16)(float)(byte & 15u);
+      s.f[j] = as_u(half2v{c, c});
+      s.b[j] = as_u(half2v{-1024.0f16 * c, -1024.0f16 * c});  // c <= 15: exact
+      s.mn[j] = -dmin * (float)(byte >> 4);
+    }
+    return s;
+  }
+  __device__ static half8 bop(const Raw &r, const Sc &s, int st, int) {
+    const int j = st >> 1, b = st & 1;
+    const uint32_t v0 = (b ? r.q.z : r.q.x) >> (2 * j), v1 = (b ? r.q.w : r.q.y) >> (2 * j);
+    const uint32_t m = 0x00030003u, f = s.f[j], c = s.b[j];
+    return pack8(fold(mag(v0, m), f, c), fold(mag(v0 >> 8, m), f, c), fold(mag(v1, m), f, c),
+                 fold(mag(v1 >> 8, m), f, c));
+  }
+  __device__ static bool ind(int s, int G, int i) { return i == 4 * G + (s >> 1); }
+  __device__ static floatx4 post(floatx4 acc, const floatx4 *D, floatx4 X, const Sc &s) {
+    acc = acc + s.d * D[0];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = mfma4f32(X[q], s.mn[q], acc);
+    return acc;
+  }
+};
+
+struct DecQ3K {
+  static constexpr int KB = 256, NSTEP = 8, NPART = 1, BYTES = 110;
+  static constexpr bool HAS_MIN = false, CHUNKED = false, STEP_SCALE = false;
+  struct Raw { u32x4 hm, q; u32x2 lo; uint32_t hi, d; };
+  struct Sc { uint32_t f[4], b[4]; float d; int hb; };  // hb = 4n: this group's high-mask bits
+  __device__ static int x_off(int s, int G, int h) { return DecQ6K::x_off(s, G, h); }
+  __device__ static void load(const uint8_t *blk, int G, Raw &r) {
+    r.hm = ld16(blk + 16 * (G & 1));
+    r.q = ld16(blk + 32 + 16 * G);
+    r.lo = ld8(blk + 96);
+    r.hi = rd32(blk + 104);
+    r.d = rd16(blk + 108);
+  }
+  __device__ static Sc prep(const Raw &r, int G) {
+    // Scale i = 8n + 2j + a: low four bits in byte i (n = 0, low nibble) or
+    // byte i - 8 (n = 1, high nibble), top two at bits 2 (i / 4) of byte
+    // 8 + i % 4; used as sc - 32.  The code v = q2 + 4 h (0 .. 7) arrives
+    // at mantissa bits 3-5 (e = 1024 + 8 v), so (sc - 32)(v - 4) =
+    // e (sc - 32) / 8 - 132 (sc - 32), both factors exact f16 values.
+    const int n = G >> 1, a = G & 1;
+    Sc s;
+    s.d = lo_f16(r.d);
+    s.hb = 4 * n;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = 2 * j + a;  // i - 8n
+      const uint32_t lb = (r.lo[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      const int low4 = (int)(n ? lb >> 4 : lb & 15u);
+      const int high2 = (int)((r.hi >> (8 * (k & 3) + 2 * (2 * n + (j >> 1)))) & 3u);
+      const float v = (float)((low4 | (high2 << 4)) - 32);
+      const _Float16 f = (_Float16)(v * 0.125f), c = (_Float16)(v * -132.0f);
+      s.f[j] = as_u(half2v{f, f});
+      s.b[j] = as_u(half2v{c, c});
+    }
+    return s;
+  }
+  __device__ static half8 bop(const Raw &r, const Sc &s, int st, int) {
+    const int j = st >> 1, b = st & 1;
+    const uint32_t v0 = (b ? r.q.z : r.q.x) >> (2 * j), v1 = (b ? r.q.w : r.q.y) >> (2 * j);
+    // The high-mask bits 4n + j of the same eight bytes of hmask.
+    const int hs = s.hb + j;
+    const uint32_t h0 = (b ? r.hm.z : r.hm.x) >> hs, h1 = (b ? r.hm.w : r.hm.y) >> hs;
+    const uint32_t cm = 0x00180018u, hm = 0x00200020u;
+    const uint32_t e0 = and_or(h0 << 5, hm, and_or(v0 << 3, cm, kMagic));
+    const uint32_t e1 = and_or(h0 >> 3, hm, and_or(v0 >> 5, cm, kMagic));
+    const uint32_t e2 = and_or(h1 << 5, hm, and_or(v1 << 3, cm, kMagic));
+    const uint32_t e3 = and_or(h1 >> 3, hm, and_or(v1 >> 5, cm, kMagic));
+    const uint32_t f = s.f[j], c = s.b[j];
+    return pack8(fold(e0, f, c), fold(e1, f, c), fold(e2, f, c), fold(e3, f, c));
+  }
+  __device__ static bool ind(int, int, int) { return false; }
+  __device__ static floatx4 post(floatx4 acc, const floatx4 *D, floatx4, const Sc &s) { return acc + s.d * D[0]; }
+};
+
 template <int KIND> struct Dec;
 template <> struct Dec<Q4_K> : DecQ4K {};
 template <> struct Dec<Q6_K> : DecQ6K {};
@@ -460,6 +617,9 @@ template <> struct Dec<Q8_0> : DecQ8_0 {};
 template <> struct Dec<IQ4_NL> : DecIQ4NL {};
 template <> struct Dec<MXFP4> : DecMXFP4 {};
 template <> struct Dec<IQ4_XS> : DecIQ4XS {};
+template <> struct Dec<Q5_K> : DecQ5K {};
+template <> struct Dec<Q2_K> : DecQ2K {};
+template <> struct Dec<Q3_K> : DecQ3K {};
 
 // ---------------------------------------------------------------------------
 // The repacked layout written by qmm_repack.  Tile t (rows 16t .. 16t+15) and

@@ -48,10 +48,16 @@ struct Chunks {
   struct Held { u32x4 c[L]; };
   __device__ static int offset(int c) { return c < C - 1 ? 16 * c : Dd::BYTES - 16; }
 };
+template <int KIND, bool PACKED, typename Dd>
+struct HeldOf {  // native rows (kinds without repacked records stop here)
+  using type = typename std::conditional<Dd::CHUNKED, typename Chunks<Dd>::Held, typename Dd::Raw>::type;
+};
+template <int KIND, typename Dd>
+struct HeldOf<KIND, true, Dd> {
+  using type = typename Rec<KIND>::Packed;
+};
 template <int KIND, bool PACKED, typename Dd = Dec<KIND>>
-using Held = typename std::conditional<
-    PACKED, typename Rec<KIND>::Packed,
-    typename std::conditional<Dd::CHUNKED, typename Chunks<Dd>::Held, typename Dd::Raw>::type>::type;
+using Held = typename HeldOf<KIND, PACKED, Dd>::type;
 
 // PACKED: W is the repacked layout (the records above Rec in
 // qmm_gemv_mfma.h) instead of native rows; row_bytes is then unused.
@@ -501,6 +507,7 @@ hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f
 bool moe_mfma_supported(int kind, int64_t K) {
   switch (kind) {
     case Q4_K: case Q6_K: case IQ4_XS: case Q4_0: case Q5_0: case Q8_0: case IQ4_NL: case MXFP4:
+    case Q2_K: case Q3_K: case Q5_K:
       return K % 256 == 0;
     default:
       return false;
@@ -526,6 +533,9 @@ hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16,
     case Q4_K: return gv::run_routed<Q4_K, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
     case Q6_K: return gv::run_routed<Q6_K, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
     case IQ4_XS: return gv::run_routed<IQ4_XS, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q2_K: return gv::run_routed<Q2_K, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q3_K: return gv::run_routed<Q3_K, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+    case Q5_K: return gv::run_routed<Q5_K, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
     case Q4_0: return gv::run_routed<Q4_0, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
     case Q5_0: return gv::run_routed<Q5_0, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
     case Q8_0: return gv::run_routed<Q8_0, false>(W, X, x_f16, Y, mt, N, K, s, rt, items);
@@ -556,6 +566,9 @@ hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16
     case Q4_K: return gv::run_m<Q4_K>(W, x, x_f16, y, M, N, K, s, cfg);
     case Q6_K: return gv::run_m<Q6_K>(W, x, x_f16, y, M, N, K, s, cfg);
     case IQ4_XS: return gv::run_m<IQ4_XS>(W, x, x_f16, y, M, N, K, s, cfg);
+    case Q2_K: return gv::run_m<Q2_K>(W, x, x_f16, y, M, N, K, s, cfg);
+    case Q3_K: return gv::run_m<Q3_K>(W, x, x_f16, y, M, N, K, s, cfg);
+    case Q5_K: return gv::run_m<Q5_K>(W, x, x_f16, y, M, N, K, s, cfg);
     default: break;
   }
   // The 32-element kinds walk K in k-blocks of eight blocks.

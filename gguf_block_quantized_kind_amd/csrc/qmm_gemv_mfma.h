@@ -777,6 +777,46 @@ template <> struct Rec<Q6_K> {
   __device__ static Packed unpack(const Packed &p, int) { return p; }
 };
 
+// Q5_K: the Q4_K code sections, then the row's 32 qh bytes and its 16-byte
+// header as row sections.
+template <> struct Rec<Q5_K> {
+  using Packed = DecQ5K::Raw;
+  __device__ static void load(const uint8_t *rec, int lane, int j, int, Packed &p) {
+    p.q0 = lda16(rec + 16 * lane);
+    p.q1 = lda16(rec + 1024 + 16 * lane);
+    p.h0 = lda16(rec + 2048 + 32 * j);
+    p.h1 = lda16(rec + 2048 + 32 * j + 16);
+    p.hdr = lda16(rec + 2560 + 16 * j);
+  }
+  __device__ static Packed unpack(const Packed &p, int) { return p; }
+};
+
+// Q2_K: group G's sixteen code bytes (one lane section), then the row's
+// sixteen scale bytes and its f16 d, dmin.
+template <> struct Rec<Q2_K> {
+  using Packed = DecQ2K::Raw;
+  __device__ static void load(const uint8_t *rec, int lane, int j, int, Packed &p) {
+    p.q = lda16(rec + 16 * lane);
+    p.sc = lda16(rec + 1024 + 16 * j);
+    p.dd = *reinterpret_cast<const uint32_t *>(__builtin_assume_aligned(rec + 1280 + 4 * j, 4));
+  }
+  __device__ static Packed unpack(const Packed &p, int) { return p; }
+};
+
+// Q3_K: group G's sixteen code bytes, then the row's hmask (group G reads
+// the half 16 (G & 1) ..), scale bytes 0-7 and 8-11, and f16 d.
+template <> struct Rec<Q3_K> {
+  using Packed = DecQ3K::Raw;
+  __device__ static void load(const uint8_t *rec, int lane, int j, int G, Packed &p) {
+    p.q = lda16(rec + 16 * lane);
+    p.hm = lda16(rec + 1024 + 32 * j + 16 * (G & 1));
+    p.lo = lda8(rec + 1536 + 8 * j);
+    p.hi = *reinterpret_cast<const uint32_t *>(__builtin_assume_aligned(rec + 1664 + 4 * j, 4));
+    p.d = *reinterpret_cast<const uint16_t *>(__builtin_assume_aligned(rec + 1728 + 2 * j, 2));
+  }
+  __device__ static Packed unpack(const Packed &p, int) { return p; }
+};
+
 
 }  // namespace gv
 }  // namespace qmm

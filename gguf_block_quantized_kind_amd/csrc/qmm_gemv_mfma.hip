@@ -467,6 +467,7 @@ static hipError_t run_packed(const uint8_t *P, const void *x, int x_f16, float *
 bool packed_supported(int kind) {
   switch (kind) {
     case Q4_K: case Q6_K: case IQ4_XS: case Q4_0: case Q5_0: case Q8_0: case IQ4_NL: case MXFP4:
+    case Q2_K: case Q3_K: case Q5_K:
       return true;
     default:
       return false;
@@ -499,6 +500,9 @@ hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f
     case Q8_0: return gv::run_packed<Q8_0>(P, x, x_f16, y, M, N, K, s, cfg);
     case IQ4_NL: return gv::run_packed<IQ4_NL>(P, x, x_f16, y, M, N, K, s, cfg);
     case MXFP4: return gv::run_packed<MXFP4>(P, x, x_f16, y, M, N, K, s, cfg);
+    case Q2_K: return gv::run_packed<Q2_K>(P, x, x_f16, y, M, N, K, s, cfg);
+    case Q3_K: return gv::run_packed<Q3_K>(P, x, x_f16, y, M, N, K, s, cfg);
+    case Q5_K: return gv::run_packed<Q5_K>(P, x, x_f16, y, M, N, K, s, cfg);
     default: break;
   }
   return hipErrorNotSupported;
@@ -526,6 +530,9 @@ hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16,
       case Q8_0: return gv::run_routed<Q8_0, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
       case IQ4_NL: return gv::run_routed<IQ4_NL, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
       case MXFP4: return gv::run_routed<MXFP4, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      case Q2_K: return gv::run_routed<Q2_K, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      case Q3_K: return gv::run_routed<Q3_K, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
+      case Q5_K: return gv::run_routed<Q5_K, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
       default: return hipErrorNotSupported;
     }
   }

@@ -277,6 +277,9 @@ hipError_t launch_gemv_xs(int kind, const uint8_t *P, const void *x, int x_f16, 
     case Q8_0: return gv::run_xs_m<Q8_0>(P, x, x_f16, y, M, N, K, s, cfg);
     case IQ4_NL: return gv::run_xs_m<IQ4_NL>(P, x, x_f16, y, M, N, K, s, cfg);
     case MXFP4: return gv::run_xs_m<MXFP4>(P, x, x_f16, y, M, N, K, s, cfg);
+    case Q2_K: return gv::run_xs_m<Q2_K>(P, x, x_f16, y, M, N, K, s, cfg);
+    case Q3_K: return gv::run_xs_m<Q3_K>(P, x, x_f16, y, M, N, K, s, cfg);
+    case Q5_K: return gv::run_xs_m<Q5_K>(P, x, x_f16, y, M, N, K, s, cfg);
     default: break;
   }
   return hipErrorNotSupported;

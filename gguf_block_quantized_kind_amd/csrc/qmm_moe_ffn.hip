@@ -139,7 +139,15 @@ using Fx4 = gv::floatx4;
 // One tile's k-block as loaded: the repacked record's fields, or the
 // decoder's fields of a native row.
 template <int KIND, bool PACKED>
-using Held = typename std::conditional<PACKED, typename gv::Rec<KIND>::Packed, typename Dec<KIND>::Raw>::type;
+struct HeldOf {
+  using type = typename Dec<KIND>::Raw;
+};
+template <int KIND>
+struct HeldOf<KIND, true> {
+  using type = typename gv::Rec<KIND>::Packed;
+};
+template <int KIND, bool PACKED>
+using Held = typename HeldOf<KIND, PACKED>::type;
 
 // Where a tile's k-block lives: expert base W, tile (16 rows) `tile` of an
 // expert with `rows` rows, k-block kb; lane (j, G).
@@ -516,6 +524,9 @@ hipError_t launch_moe_ffn(int kind, const uint8_t *W_gu, const uint8_t *W_d, int
         return fz::run_fused<IQ4_XS, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
       case MXFP4:
         return fz::run_fused<MXFP4, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
+      case Q2_K: return fz::run_fused<Q2_K, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
+      case Q3_K: return fz::run_fused<Q3_K, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
+      case Q5_K: return fz::run_fused<Q5_K, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
       default: break;
     }
   }

@@ -20,7 +20,7 @@ struct Shape {
   int B;            // bytes of one row's k-block
   int n_lane;       // lane sections
   int n_row;        // row sections
-  int width[2];     // bytes per row of each row section
+  int width[4];     // bytes per row of each row section
 };
 
 template <int KIND> struct Map;
@@ -73,6 +73,27 @@ template <> struct Map<Q6_K> {
   __device__ static int row(int sec, int i) { return sec == 0 ? 192 + i : 208 + i; }  // scales, d
 };
 
+// Q5_K: the Q4_K code sections, then qh[32] and the 16-byte header as row
+// sections (every group of a row reads all 32 fifth-bit bytes).
+template <> struct Map<Q5_K> {
+  static constexpr Shape shape{176, 2, 2, {32, 16}};
+  __device__ static int lane(int c, int G, int i) { return 48 + 32 * G + 16 * c + i; }
+  __device__ static int row(int sec, int i) { return sec == 0 ? 16 + i : i; }  // qh, then d, dmin, scales
+};
+// Q2_K and Q3_K: group G = 2n + a takes code bytes 32n + 16a .. + 15.
+template <> struct Map<Q2_K> {
+  static constexpr Shape shape{84, 1, 2, {16, 4}};
+  __device__ static int lane(int, int G, int i) { return 16 + 16 * G + i; }
+  __device__ static int row(int sec, int i) { return sec == 0 ? i : 80 + i; }  // scales, then d, dmin
+};
+template <> struct Map<Q3_K> {
+  static constexpr Shape shape{110, 1, 4, {32, 8, 4, 2}};
+  __device__ static int lane(int, int G, int i) { return 32 + 16 * G + i; }
+  __device__ static int row(int sec, int i) {  // hmask, scale bytes 0-7, scale bytes 8-11, d
+    return sec == 0 ? i : sec == 1 ? 96 + i : sec == 2 ? 104 + i : 108 + i;
+  }
+};
+
 // Row j (in the tile) and offset in its k-block of record byte o.
 template <int KIND>
 __device__ void source(int o, int &j, int &off) {
@@ -85,14 +106,15 @@ __device__ void source(int o, int &j, int &off) {
     return;
   }
   o -= 1024 * sh.n_lane;
-  if (o < 16 * sh.width[0] || sh.n_row == 1) {
-    j = o / sh.width[0];
-    off = Mp::row(0, o % sh.width[0]);
-    return;
+#pragma unroll
+  for (int sec = 0; sec < sh.n_row; ++sec) {
+    if (o < 16 * sh.width[sec] || sec == sh.n_row - 1) {
+      j = o / sh.width[sec];
+      off = Mp::row(sec, o % sh.width[sec]);
+      return;
+    }
+    o -= 16 * sh.width[sec];
   }
-  o -= 16 * sh.width[0];
-  j = o / sh.width[1];
-  off = Mp::row(1, o % sh.width[1]);
 }
 
 // One thread per 4 bytes of the repacked tensor (records are multiples of
@@ -140,6 +162,9 @@ int64_t packed_bytes_of(int kind, int64_t N, int64_t K) {
     case Q5_0: B = 176; break;
     case Q8_0: B = 272; break;
     case Q6_K: B = 210; break;
+    case Q5_K: B = 176; break;
+    case Q2_K: B = 84; break;
+    case Q3_K: B = 110; break;
     default: return -1;
   }
   if (K <= 0 || K % 256 != 0 || N <= 0) return -1;
@@ -156,6 +181,9 @@ hipError_t launch_repack(int kind, const uint8_t *W, void *P, int64_t N, int64_t
     case IQ4_XS: return rp::run<IQ4_XS>(W, P, N, K, s);
     case Q4_K: return rp::run<Q4_K>(W, P, N, K, s);
     case Q6_K: return rp::run<Q6_K>(W, P, N, K, s);
+    case Q5_K: return rp::run<Q5_K>(W, P, N, K, s);
+    case Q2_K: return rp::run<Q2_K>(W, P, N, K, s);
+    case Q3_K: return rp::run<Q3_K>(W, P, N, K, s);
     default: break;
   }
   return hipErrorNotSupported;

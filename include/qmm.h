@@ -232,14 +232,15 @@ size_t qmm_moe_workspace_bytes(int64_t E, int64_t M, int64_t topk);
  * in tiles of 16 (the last padded with zero rows), K in k-blocks of 256
  * elements; tile t and k-block b form one record of 16 * B bytes at
  * (t * K/256 + b) * 16 * B, B being one row's k-block in native bytes (144
- * for Q4_0, IQ4_NL, Q4_K; 136 for MXFP4, IQ4_XS; 176 Q5_0; 272 Q8_0; 210
- * Q6_K).  A record holds exactly the bytes of its sixteen native row pieces,
+ * for Q4_0, IQ4_NL, Q4_K; 136 for MXFP4, IQ4_XS; 176 Q5_0, Q5_K; 272 Q8_0;
+ * 210 Q6_K; 84 Q2_K; 110 Q3_K).  A record holds exactly the bytes of its sixteen native row pieces,
  * permuted: first lane sections of 1024 bytes (16-byte slot 16 G + j holds
  * the code bytes that lane j + 16 G of a wave decodes for row j), then row
  * sections (per row: its scales and headers).  The per-kind byte tables are
  * in qmm_repack.hip.
  *
- * Kinds: Q4_0, Q5_0, Q8_0, IQ4_NL, MXFP4, IQ4_XS, Q4_K, Q6_K.  Size in bytes of
+ * Kinds: all eleven (Q4_0, Q5_0, Q8_0, IQ4_NL, MXFP4, IQ4_XS, Q2_K, Q3_K,
+ * Q4_K, Q5_K, Q6_K).  Size in bytes of
  * the repacked tensor of N rows of K elements: qmm_packed_bytes (-1 for any
  * other kind, K not a multiple of 256, or N <= 0). */
 int64_t qmm_packed_bytes(int kind, int64_t N, int64_t K);

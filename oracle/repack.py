@@ -14,8 +14,8 @@ page's plane format), and its definition is this module:
 * Rows are taken in groups of 16 (a "tile"); a last, partial group is padded
   with zero rows.  K is taken in k-blocks of 256 elements, so one row's
   k-block is ``B`` consecutive bytes of its GGUF row (B = 144 for Q4_0,
-  Q4_K and IQ4_NL's eight blocks, 136 for MXFP4 and IQ4_XS, 176 for Q5_0,
-  272 for Q8_0, 210 for Q6_K).
+  Q4_K and IQ4_NL's eight blocks, 136 for MXFP4 and IQ4_XS, 176 for Q5_0
+  and Q5_K, 272 for Q8_0, 210 for Q6_K, 84 for Q2_K, 110 for Q3_K).
 * Tile t, k-block b becomes one record of 16 B bytes at offset
   ``(t * n_kblocks + b) * 16 * B``: the same bytes, permuted, so the repacked
   tensor is exactly as large as the native one plus the padding rows.
@@ -41,8 +41,10 @@ TILE_ROWS = 16
 _GEOMETRY = {  # kind: (block bytes, block elements), the GGUF block sizes
     "Q4_0": (18, 32), "Q5_0": (22, 32), "Q8_0": (34, 32), "IQ4_NL": (18, 32),
     "MXFP4": (17, 32), "IQ4_XS": (136, 256), "Q4_K": (144, 256), "Q6_K": (210, 256),
+    "Q2_K": (84, 256), "Q3_K": (110, 256), "Q5_K": (176, 256),
 }
-_IDS = {2: "Q4_0", 6: "Q5_0", 8: "Q8_0", 20: "IQ4_NL", 39: "MXFP4", 23: "IQ4_XS", 12: "Q4_K", 14: "Q6_K"}
+_IDS = {2: "Q4_0", 6: "Q5_0", 8: "Q8_0", 20: "IQ4_NL", 39: "MXFP4", 23: "IQ4_XS", 12: "Q4_K", 14: "Q6_K",
+        10: "Q2_K", 11: "Q3_K", 13: "Q5_K"}
 
 KINDS = tuple(_GEOMETRY)
 
@@ -109,6 +111,23 @@ def _layout(kind):
             return (64 * h + 16 * a + i, 64 * h + 32 + 16 * a + i, 128 + 32 * h + 16 * a + i)[c]
         return 3, lane, [(16, lambda i: 192 + i),                      # the sixteen int8 scales
                          (2, lambda i: 208 + i)]                       # f16 d
+    if k == "Q5_K":
+        def lane(c, G, i):  # code bytes 32G + 16c .. +15 (sub-blocks 2G, 2G+1), after the 16-byte header and qh
+            return 48 + 32 * G + 16 * c + i
+        return 2, lane, [(32, lambda i: 16 + i),                       # qh[32]: every row's fifth bits
+                         (16, lambda i: i)]                            # d, dmin, 12 scale bytes
+    if k == "Q2_K":
+        def lane(c, G, i):  # G = 2n + a: code bytes 32n + 16a .. +15
+            return 16 + 16 * G + i
+        return 1, lane, [(16, lambda i: i),                            # scales[16] (scale, min nibbles)
+                         (4, lambda i: 80 + i)]                        # f16 d, dmin
+    if k == "Q3_K":
+        def lane(c, G, i):  # G = 2n + a: code bytes 32n + 16a .. +15
+            return 32 + 16 * G + i
+        return 1, lane, [(32, lambda i: i),                            # hmask[32]
+                         (8, lambda i: 96 + i),                        # scale bytes 0..7 (low four bits)
+                         (4, lambda i: 104 + i),                       # scale bytes 8..11 (top two bits)
+                         (2, lambda i: 108 + i)]                       # f16 d
     raise KeyError(k)
 
 

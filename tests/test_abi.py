@@ -170,14 +170,13 @@ def test_repack_sizes_and_refusals_in_order(lib, oracle_mod):
             assert lib.qmm_packed_bytes(kid, N, K) == rp.packed_bytes(name, N, K)
         # Whole tiles: the native size exactly.
         assert lib.qmm_packed_bytes(kid, 32, 4096) == 32 * qmm.qmm_row_bytes(kid, 4096)
-    for kid in (10, 11, 13):   # Q2_K, Q3_K, Q5_K have no repacked layout
-        assert lib.qmm_packed_bytes(kid, 16, 256) == -1
+    assert len(rp.KINDS) == 11                     # every kind has a repacked layout
+    assert lib.qmm_packed_bytes(99, 16, 256) == -1   # not a kind
     assert lib.qmm_packed_bytes(2, 16, 288) == -1
     assert lib.qmm_packed_bytes(2, 0, 256) == -1
     r = lib.qmm_repack
     assert r(2, FAKE, FAKE, 0, 256, None) == EMPTY
-    assert r(13, FAKE, FAKE, 16, 256, None) == KIND
-    assert "repacked" in qmm.qmm_last_error()
+    assert r(99, FAKE, FAKE, 16, 256, None) == KIND
     assert r(2, FAKE, FAKE, 16, 48, None) == KALIGN     # not whole Q4_0 blocks
     assert r(2, FAKE, FAKE, 16, 288, None) == KALIGN    # whole blocks, not whole k-blocks
     assert "256" in qmm.qmm_last_error()
@@ -185,7 +184,7 @@ def test_repack_sizes_and_refusals_in_order(lib, oracle_mod):
     assert r(2, FAKE, FAKE + 8, 16, 256, None) == ARG   # P not 16-byte aligned
     g = lib.qmm_gemv_packed
     assert g(12, FAKE, FAKE, 0, FAKE, 0, 16, 256, None) == EMPTY
-    assert g(11, FAKE, FAKE, 0, FAKE, 1, 16, 256, None) == KIND
+    assert g(99, FAKE, FAKE, 0, FAKE, 1, 16, 256, None) == KIND
     assert g(2, FAKE, FAKE, 0, FAKE, 1, 16, 256 + 32, None) == KALIGN
     assert g(12, FAKE, FAKE, 2, FAKE, 1, 16, 256, None) == DTYPE
     assert g(12, None, FAKE, 0, FAKE, 1, 16, 256, None) == ARG
@@ -203,7 +202,7 @@ def test_gemv_i8_refusals_in_order(lib):
     assert lib.qmm_gemv_i8_workspace_bytes(8, 4096) == 32768 + 2 * 4096
     assert lib.qmm_gemv_i8_workspace_bytes(0, 512) == 0 and lib.qmm_gemv_i8_workspace_bytes(3, 48) == 0
     assert g(8, FAKE, FAKE, 0, FAKE, 0, 16, 512, FAKE, need, None) == EMPTY
-    assert g(10, FAKE, FAKE, 0, FAKE, 3, 16, 512, FAKE, need, None) == KIND    # Q2_K: no repacked layout
+    assert g(10, FAKE, FAKE, 0, FAKE, 3, 16, 512, FAKE, need, None) == KIND    # Q2_K: not an integer-code kind
     assert g(12, FAKE, FAKE, 0, FAKE, 3, 16, 512, FAKE, need, None) == KIND    # Q4_K: not an integer-code kind
     assert "IQ4_NL or MXFP4" in qmm.qmm_last_error()
     assert g(8, FAKE, FAKE, 0, FAKE, 3, 16, 288, FAKE, need, None) == KALIGN
@@ -226,7 +225,7 @@ def test_moe_packed_refusals_in_order(lib):
                         k.get("N", 16), k.get("K", 256), k.get("ws", FAKE), k.get("wsb", need), None]
     assert f(*args(E=0)) == EMPTY
     assert f(*args(M=0)) == EMPTY
-    assert f(*args(kind=13)) == KIND                      # Q5_K: no repacked layout
+    assert f(*args(kind=99)) == KIND                      # not a kind
     assert f(*args(kind=2, K=288)) == KALIGN
     assert f(*args(dt=5)) == DTYPE
     assert f(*args(P=None)) == ARG
@@ -246,7 +245,7 @@ def test_moe_ffn_packed_refusals(lib):
     args = lambda **k: [k.get("kind", 12), k.get("Pg", FAKE), k.get("Pd", FAKE), 4, FAKE, FAKE, 2,
                         FAKE, 1, FAKE, k.get("M", 2), k.get("Nff", 256), k.get("K", 512), FAKE, need, None]
     assert f(*args(Nff=0)) == EMPTY
-    assert f(*args(kind=10)) == KIND                  # Q2_K has no repacked layout
+    assert f(*args(kind=99)) == KIND                  # not a kind
     assert f(*args(kind=2, K=288)) == KALIGN          # K not whole k-blocks
     assert f(*args(kind=2, Nff=288)) == KALIGN        # N_ff (the down matrix's K) not whole k-blocks
     assert f(*args(Pg=FAKE + 8)) == ARG

@@ -248,6 +248,26 @@ def secondary_cases(torch, qmm, wl, layout: str = "packed"):
             qmm.qmm_matmul(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
 
         cases.append(Case(w.name, w.kind, launch, copies, w.weight_bytes, w.flops))
+    # The other super-block kinds at the decode step's shape (N=14336,
+    # K=4096, f32 x, M = 1 and 8; weights drawn as the step's): repacked,
+    # then native rows.
+    for kind in ("Q2_K", "Q3_K", "Q5_K"):
+        for M in (1, 8):
+            w = wl.Matmul(f"c2_{kind.lower()}_m{M}", kind, M, 14336, 4096, "f32")
+            x = torch.from_numpy(w.x()).cuda()
+            y = torch.empty((M, w.N), dtype=torch.float32, device="cuda")
+            for layout in ("packed", "native"):
+                copies = packed_copies(torch, qmm, w) if layout == "packed" else make_copies(torch, w.weights())
+
+                def launch(i, w=w, x=x, y=y, copies=copies, layout=layout):
+                    c = copies[i % len(copies)]
+                    if layout == "packed":
+                        qmm.qmm_gemv_packed(w.kind, c, x, y, w.M, w.N, w.K)
+                    else:
+                        qmm.qmm_gemv_ex(w.kind, c, x, y, w.M, w.N, w.K)
+
+                cases.append(Case(w.name + ("_packed" if layout == "packed" else ""), w.kind, launch, copies,
+                                  w.weight_bytes, w.flops))
     # The codebook prefill workloads over repacked records (the 32-element
     # kinds the packed GEMM takes).
     for w in [w for w in wl.C4 if w.M > 8 and w.kind in ("IQ4_NL", "MXFP4")]:

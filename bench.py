@@ -424,8 +424,9 @@ def write_traffic(case, case_fetch, case_write, copy_fetch, copy_write, copy_byt
     out = {"source_digest": source_digest(), "copy_bytes": copy_bytes,
            "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale": fetch_scale, "write_scale": write_scale, "cases": {}}
-    f, nf = _pmc_average(case_fetch, "FETCH_SIZE", "gemv_mfma_kernel")
-    w, nw = _pmc_average(case_write, "WRITE_SIZE", "gemv_mfma_kernel")
+    # The decode GEMV kernels (gemv_t1_kernel, gemv_xs_kernel, gemv_mfma_kernel).
+    f, nf = _pmc_average(case_fetch, "FETCH_SIZE", "qmm::gv::gemv_")
+    w, nw = _pmc_average(case_write, "WRITE_SIZE", "qmm::gv::gemv_")
     out["cases"][case] = {"fetch_kib": f, "write_kib": w, "dispatches": [nf, nw],
                           "hbm_bytes_per_launch": round(f * 1024.0 * fetch_scale + w * 1024.0 * write_scale)}
     os.makedirs(PROFILES, exist_ok=True)

@@ -151,16 +151,17 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   const int kb0 = (int)((int64_t)wave * nkb / S), kb1 = (int)((int64_t)(wave + 1) * nkb / S);
   Held<KIND, PACKED> raw[NS][R];
   X4 xv[NS][XS::kPerLane];
-  // Every lane issues every load (dead lanes read token 0's slice and drop
-  // it; past the wave's last k-block the last one is read again), so the
-  // loads of one call are never under a branch and the wait for k-block kb
-  // can leave the PD later k-blocks in flight.
-  const int kb_last = max(kb1 - 1, 0);
+  // Dead lanes skip their activation loads (zeros); no k-block past the
+  // wave's last is issued.  (A form that issues every load unconditionally,
+  // in whole rounds of NS k-blocks so that no wait drains the later ones,
+  // holds more registers here and measured 5-100% slower on this kernel's
+  // shapes.)
   auto issue = [&](int kb, int slot) {
-    kb = min(kb, kb_last);
 #pragma unroll
     for (int i = 0; i < XS::kPerLane; ++i) {
-      __builtin_memcpy(&xv[slot][i], X + xoff[i] + (int64_t)kb * Dd::KB, sizeof(X4));
+      X4 v = {};
+      if (xlive[i]) __builtin_memcpy(&v, X + xoff[i] + (int64_t)kb * Dd::KB, sizeof(X4));
+      xv[slot][i] = v;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -179,7 +180,8 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   // j * RS, each chunk at its byte offset in the k-block.
   uint8_t *stage = reinterpret_cast<uint8_t *>(lds + S * (PD + 1) * kFrag + 1) + wave * 16 * CK::RS;
 #pragma unroll
-  for (int d = 0; d < PD; ++d) issue(kb0 + d, d);
+  for (int d = 0; d < PD; ++d)
+    if (kb0 + d < kb1) issue(kb0 + d, d);
 
   // Decode and multiply the k-block held in ring slot d.
   auto consume = [&](int d) {
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
 #pragma unroll
     for (int i = 0; i < XS::kPerLane; ++i) {
       if (xdst[i] < 0) continue;
-      const X4 v = xlive[i] ? xv[d][i] : X4{};
+      const X4 v = xv[d][i];
       const half2v p0 = {(_Float16)v[0], (_Float16)v[2]}, p1 = {(_Float16)v[1], (_Float16)v[3]};
       u32x2 *dst = reinterpret_cast<u32x2 *>(xk) + xdst[i];
       *dst = u32x2{as_u(p0), as_u(p1)};
@@ -271,17 +273,14 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   // Whole rounds of NS k-blocks: every round issues NS refills, never under a
   // branch, so each wait leaves the PD newer k-blocks in flight.  The last
   // cnt % NS k-blocks (already issued) follow.
-  const int cnt = max(kb1 - kb0, 0), full = cnt - cnt % NS;
-  for (int i = 0; i < full; i += NS) {
+  for (int kb = kb0; kb < kb1; kb += NS) {
 #pragma unroll
     for (int d = 0; d < NS; ++d) {
-      issue(kb0 + i + d + PD, (d + PD) % NS);
+      if (kb + d >= kb1) break;
+      if (kb + d + PD < kb1) issue(kb + d + PD, (d + PD) % NS);
       consume(d);
     }
   }
-#pragma unroll
-  for (int d = 0; d < NS - 1; ++d)
-    if (d < cnt - full) consume(d);
 
   if constexpr (S > 1) {
     __syncthreads();  // every wave is done with its ring

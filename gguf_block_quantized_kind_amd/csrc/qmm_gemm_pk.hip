@@ -507,12 +507,26 @@ static hipError_t run_kind(const uint8_t *P, const void *A, int a_f16, float *C,
     const char *e = getenv("QMM_GEMM_PK_CFG");
     return e ? atoi(e) : 0;
   }();
+  const int64_t nkb = K / 256;
   switch (cfg) {
     case 1: return run_any<KIND, 4, 8, 1>(P, A, a_f16, C, M, N, K, s);
     case 2: return run_any<KIND, 2, 4, 2>(P, A, a_f16, C, M, N, K, s);
+    case 3: if (a_f16 && nkb % 2 == 0) return run<KIND, _Float16, 4, 3, 2, 4>(P, A, C, M, N, K, s); break;
+    case 5: if (a_f16 && nkb % 4 == 0) return run<KIND, _Float16, 4, 3, 4, 2>(P, A, C, M, N, K, s); break;
+    case 6: if (a_f16 && nkb % 2 == 0) return run<KIND, _Float16, 4, 2, 2, 4>(P, A, C, M, N, K, s); break;
+    case 7: if (a_f16 && nkb % 2 == 0) return run<KIND, _Float16, 4, 4, 2, 4>(P, A, C, M, N, K, s); break;
     default: break;
   }
 #endif
+  // 64 x 128 tiles, or 64 x 192 (two k parts of four waves over three row
+  // tiles each) when the 64 x 128 grid would take more than one round of
+  // the compute units and the 64 x 192 grid takes one: 256 x 11008 x 4096,
+  // IQ4_NL 61.9 -> 48.4 us, MXFP4 53.9 -> 41.7 us (the 64 x 192 grid is
+  // slower where 64 x 128 already fits one round: 512 x 4096 x 4096 Q8_0
+  // 29.4 -> 34.0 us).
+  const int64_t cus = device_cus(), tm = (M + 63) / 64;
+  if (a_f16 && (K / 256) % 2 == 0 && tm * ((N + 127) / 128) > cus && tm * ((N + 191) / 192) <= cus)
+    return run<KIND, _Float16, 4, 3, 2, 4>(P, A, C, M, N, K, s);
   return run_any<KIND, 4, 4, 2>(P, A, a_f16, C, M, N, K, s);
 }
 

@@ -199,8 +199,10 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
   }
 }
 
+}  // namespace gv
+
 // Compute units of the current device (looked up once per device).
-static int device_cus() {
+int device_cus() {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
@@ -210,6 +212,8 @@ static int device_cus() {
   cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
+
+namespace gv {
 
 template <int KIND, int MT, int T, int S, int PD, int XD = 2>
 static hipError_t run_xs(const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,

@@ -41,6 +41,9 @@ hipError_t launch_gemv_t1(int kind, const uint8_t *P, const void *x, int x_f16, 
 
 // The prefill GEMM over repacked weights (any M; qmm_gemm_pk.hip), for the
 // kinds gemm_packed_supported names; P offsets must fit in 32 bits.
+// Compute units of the current device (looked up once per device).
+int device_cus();
+
 bool gemm_packed_supported(int kind);
 hipError_t launch_gemm_packed(int kind, const uint8_t *P, const void *A, int a_f16, float *C, int64_t M, int64_t N,
                               int64_t K, hipStream_t s);

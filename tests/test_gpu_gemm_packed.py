@@ -9,7 +9,11 @@ prefill GEMM for M > 8, the packed GEMV below.
   (5 k-blocks) or leave waves without work (1 k-block);
 * one-hot rows: each output is the weight rounded once to f16, exactly;
 * the same call twice gives the same bits (fixed summation order);
-* the 512 x 4096 x 4096 prefill workload on sampled rows.
+* the 512 x 4096 x 4096 prefill workload on sampled rows;
+* grids whose 64 x 128 tiles would take more than one round of the compute
+  units (64 x 192 tiles then): a ragged 200 x 9990 x 512 case on every row,
+  twice for identical bits, and the 256 x 11008 x 4096 workload on sampled
+  rows.
 """
 import numpy as np
 import pytest
@@ -91,6 +95,41 @@ def test_matmul_packed_is_deterministic(kind):
 
 @pytest.mark.parametrize("w", [w for w in wl.C3 if w.kind in KINDS], ids=lambda w: w.name)
 def test_matmul_packed_full_size_sampled(oracle_mod, w):
+    W = w.weights()
+    P = packed(w.kind, W, w.N, w.K)
+    X = w.x()
+    got = matmul(w.kind, P, X, w.N)
+    assert not np.any(got == SENTINEL)
+    rows = _sample_rows(w.N, wl.rng(w.name, "sample_packed"))
+    Y, B = oracle_mod.matmul(w.kind, W, w.K, X, rows=rows)
+    assert_within_bound(got[:, rows], Y, B, w.name)
+
+
+def _wide_grid(M, N):
+    """True when the call takes the 64 x 192 tiles (the 64 x 128 grid would
+    need more than one round of the compute units, the 64 x 192 grid one)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tm = (M + 63) // 64
+    return tm * ((N + 127) // 128) > cus and tm * ((N + 191) // 192) <= cus
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_matmul_packed_wide_grid_ragged(oracle_mod, kind):
+    M, N, K = 200, 9990, 512
+    assert _wide_grid(M, N)
+    g = wl.rng("gpu_gemm_packed_wide", kind)
+    W = wl.random_weights(kind, N, K, g)
+    P = packed(kind, W, N, K)
+    X = dev(wl.activations((M, K), np.float16, g))
+    a, b = matmul(kind, P, X, N), matmul(kind, P, X, N)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    Y, B = oracle_mod.matmul(kind, W, K, host(X))
+    assert_within_bound(a, Y, B, f"{kind} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("w", [w for w in wl.C4 if w.M > 8 and w.kind in KINDS], ids=lambda w: w.name)
+def test_matmul_packed_wide_grid_workload_sampled(oracle_mod, w):
+    assert _wide_grid(w.M, w.N)
     W = w.weights()
     P = packed(w.kind, W, w.N, w.K)
     X = w.x()

@@ -200,6 +200,26 @@ def gemv_cases(torch, qmm, wl, layout: str = "packed"):
     return cases
 
 
+def gemm_cases(torch, qmm, wl):
+    """(case, layout) for the 512 x 4096 x 4096 prefill GEMMs, Q8_0 and Q5_0,
+    on native GGUF rows (qmm_matmul) and on repacked records
+    (qmm_matmul_packed).  Weight copies are made as each case is built."""
+    for w in wl.C3:
+        for lay in ("native", "packed"):
+            copies = packed_copies(torch, qmm, w) if lay == "packed" else make_copies(torch, w.weights())
+            x = torch.from_numpy(w.x()).cuda()
+            y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+
+            def launch(i, w=w, x=x, y=y, copies=copies, lay=lay):
+                if lay == "packed":
+                    qmm.qmm_matmul_packed(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
+                else:
+                    qmm.qmm_matmul(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
+
+            yield Case(w.name + ("_packed" if lay == "packed" else ""), w.kind, launch, copies, w.weight_bytes,
+                       w.flops), lay
+
+
 def secondary_cases(torch, qmm, wl, layout: str = "packed"):
     cases = []
     # The decode step in the other weight layout.
@@ -494,7 +514,8 @@ def main():
                          "native GGUF rows")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing budget (0: skip)")
     ap.add_argument("--profile-case", metavar="NAME",
-                    help="counter-collection mode: launch only this decode GEMV case, eagerly, --steps times")
+                    help="counter-collection mode: launch only this case (a decode GEMV, prefill GEMM or "
+                         "secondary workload), eagerly, --steps times")
     ap.add_argument("--copy-probe", type=int, metavar="MIB",
                     help="counter-calibration mode: --steps device copies of MIB MiB each")
     ap.add_argument("--write-traffic", nargs=5, metavar=("CASE", "CASE_FETCH", "CASE_WRITE", "COPY_FETCH",
@@ -534,7 +555,16 @@ def main():
 
     cases = gemv_cases(torch, qmm, wl, args.layout)
     if args.profile_case:
-        case = next(c for c in cases if c.name == args.profile_case)
+        case = next((c for c in cases if c.name == args.profile_case), None)
+        if case is None:  # a prefill GEMM or a secondary workload
+            cases.clear()
+            torch.cuda.empty_cache()
+            case = next((c for c, _ in gemm_cases(torch, qmm, wl) if c.name == args.profile_case), None)
+        if case is None:
+            case = next((c for c in secondary_cases(torch, qmm, wl, args.layout) if c.name == args.profile_case),
+                        None)
+        if case is None:
+            sys.exit(f"no case named {args.profile_case}")
         for i in range(args.steps):
             case.launch(i)
         torch.cuda.synchronize()
@@ -598,25 +628,12 @@ def main():
     # (qmm_matmul_packed, the layout the decode step reads).  The roofline
     # block reports the slower kind in the step's layout.
     gemm = {}
-    for w in wl.C3:
-        for lay in ("native", "packed"):
-            copies = packed_copies(torch, qmm, w) if lay == "packed" else make_copies(torch, w.weights())
-            x = torch.from_numpy(w.x()).cuda()
-            y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
-
-            def launch(i, w=w, x=x, y=y, copies=copies, lay=lay):
-                if lay == "packed":
-                    qmm.qmm_matmul_packed(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
-                else:
-                    qmm.qmm_matmul(w.kind, copies[i % len(copies)], x, y, w.M, w.N, w.K)
-
-            name = w.name + ("_packed" if lay == "packed" else "")
-            c = Case(name, w.kind, launch, copies, w.weight_bytes, w.flops)
-            c.launch(0)
-            torch.cuda.synchronize()
-            gemm[name] = (c, describe(c, time_launches(torch, c, 32)), lay)
-            copies.clear()
-            torch.cuda.empty_cache()
+    for c, lay in gemm_cases(torch, qmm, wl):
+        c.launch(0)
+        torch.cuda.synchronize()
+        gemm[c.name] = (c, describe(c, time_launches(torch, c, 32)), lay)
+        c.copies.clear()
+        torch.cuda.empty_cache()
     in_layout = {k: v for k, v in gemm.items() if v[2] == ("packed" if args.layout == "packed" else "native")}
     gname = max(in_layout, key=lambda k: in_layout[k][1]["us_per_launch"])
     gcase, gd, _ = gemm[gname]

@@ -36,102 +36,11 @@
 #include <algorithm>
 
 #include "qmm_gemv_mfma.h"
+#include "qmm_gemv_t1.h"
 #include "qmm_internal.h"
 
 namespace qmm {
 namespace gv {
-
-template <int KIND> struct T1;
-
-template <> struct T1<Q4_K> {
-  using Dd = DecQ4K;
-  using Raw = DecQ4K::Raw;
-  static constexpr bool HAS_MIN = true;
-  static constexpr int NSEL = 2;  // A-row groups: steps 0-3 and 4-7
-  __device__ static int sel_of_step(int s) { return s >> 2; }
-  // The A row lane group G fills in selector group c: sub-block 2G + c.
-  __device__ static int arow(int c, int G) { return 4 * G + c; }
-  struct Sc { float f0, f1, g0, g1; };
-  __device__ static Sc prep(const Raw &r, int G) {
-    // Scales and mins of sub-blocks 2G, 2G + 1 (the 12-byte pack; Vulkore
-    // quant_test.cpp, ref::q4k_scale_min), two 8-bit lanes at once.
-    const int c = 16 * (G & 1);
-    const uint32_t a = r.hdr.y >> c, b = r.hdr.z >> c, e = r.hdr.w >> c;
-    uint32_t sc2, mn2;
-    if (G < 2) {
-      sc2 = a & 0x3F3Fu;
-      mn2 = b & 0x3F3Fu;
-    } else {
-      sc2 = (e & 0x0F0Fu) | ((a >> 2) & 0x3030u);
-      mn2 = ((e >> 4) & 0x0F0Fu) | ((b >> 2) & 0x3030u);
-    }
-    const float d = lo_f16(r.hdr.x), dmin = hi_f16(r.hdr.x);
-    Sc s;
-    s.f0 = (d * 16777216.0f) * (float)(sc2 & 0xFFu);        // codes arrive as q * 2^-24
-    s.f1 = (d * 1048576.0f) * (float)((sc2 >> 8) & 0xFFu);  // and as 16q * 2^-24
-    s.g0 = -dmin * (float)(mn2 & 0xFFu);
-    s.g1 = -dmin * (float)((mn2 >> 8) & 0xFFu);
-    return s;
-  }
-  __device__ static half8 bop(const Raw &r, int st) {
-    const int w = st & 3;
-    const uint32_t v0 = w < 2 ? (w == 0 ? r.q0.x : r.q0.z) : (w == 2 ? r.q1.x : r.q1.z);
-    const uint32_t v1 = w < 2 ? (w == 0 ? r.q0.y : r.q0.w) : (w == 2 ? r.q1.y : r.q1.w);
-    const uint32_t m = st < 4 ? 0x000F000Fu : 0x00F000F0u;
-    return pack8(v0 & m, (v0 >> 8) & m, v1 & m, (v1 >> 8) & m);
-  }
-  // Lane (j, G) holds D rows 4G .. 4G + 3: sub-blocks 2G, 2G + 1, then zeros.
-  __device__ static float post(float acc, floatx4 D, floatx4 X, const Sc &s) {
-    return acc + s.f0 * D[0] + s.f1 * D[1] + s.g0 * X[0] + s.g1 * X[1];
-  }
-};
-
-template <> struct T1<Q6_K> {
-  using Dd = DecQ6K;
-  using Raw = DecQ6K::Raw;
-  static constexpr bool HAS_MIN = false;
-  static constexpr int NSEL = 4;  // A-row groups: quarters g = step / 2
-  __device__ static int sel_of_step(int s) { return s >> 1; }
-  // Group G = 2h + a at quarter g: sub-block 8h + 2g + a.
-  __device__ static int arow(int g, int G) { return 8 * (G >> 1) + 2 * g + (G & 1); }
-  struct Sc { float sc[4], d; };
-  __device__ static Sc prep(const Raw &r, int G) {
-    // Lane (j, G) holds D rows 4G .. 4G + 3, sub-blocks 4G + q: bytes
-    // 4(G & 1) + q of the eight scales this lane loaded (8 (G >> 1) ..).
-    const uint32_t w = (G & 1) ? r.sc.y : r.sc.x;
-    Sc s;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) s.sc[q] = (float)(int)(int8_t)(uint8_t)((w >> (8 * q)) & 0xFFu);
-    s.d = lo_f16(r.d);
-    return s;
-  }
-  __device__ static half8 bop(const Raw &r, int st) {
-    const int g = st >> 1, w = 2 * (st & 1);
-    const u32x4 &ql = (g & 1) ? r.ql1 : r.ql0;
-    const uint32_t q0 = w == 0 ? ql.x : ql.z, q1 = w == 0 ? ql.y : ql.w;
-    const uint32_t h0 = w == 0 ? r.qh.x : r.qh.z, h1 = w == 0 ? r.qh.y : r.qh.w;
-    // As the folded decoder: low case, nibble at bits 0-3 and the two high
-    // bits moved to 4-5 (e = 1024 + q); high case, nibble left at 4-7 and
-    // the high bits moved to 8-9 (e = 1024 + 16q).
-    const uint32_t qm = g < 2 ? 0x000F000Fu : 0x00F000F0u;
-    const uint32_t hm = g < 2 ? 0x00300030u : 0x03000300u;
-    const int up = (g & 1) ? 2 : 4;
-    const uint32_t e0 = and_or(h0 << up, hm, mag(q0, qm));
-    const uint32_t e1 = and_or(h0 >> (8 - up), hm, mag(q0 >> 8, qm));
-    const uint32_t e2 = and_or(h1 << up, hm, mag(q1, qm));
-    const uint32_t e3 = and_or(h1 >> (8 - up), hm, mag(q1 >> 8, qm));
-    // q - 32: e - 1056, or e / 16 - 96 (both exact).
-    if (g < 2) {
-      const half2v off = {-1056.0f16, -1056.0f16};
-      return pack8(as_u(as_h2(e0) + off), as_u(as_h2(e1) + off), as_u(as_h2(e2) + off), as_u(as_h2(e3) + off));
-    }
-    const uint32_t f = 0x2C002C00u, b = 0xD600D600u;  // (1/16, 1/16), (-96, -96)
-    return pack8(fold(e0, f, b), fold(e1, f, b), fold(e2, f, b), fold(e3, f, b));
-  }
-  __device__ static float post(float acc, floatx4 D, floatx4, const Sc &s) {
-    return acc + s.d * (s.sc[0] * D[0] + s.sc[1] * D[1] + s.sc[2] * D[2] + s.sc[3] * D[3]);
-  }
-};
 
 template <int KIND, typename XT, int S, int PD, int OCC>
 __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void gemv_t1_kernel(

@@ -37,6 +37,7 @@
 
 #include "qmm_device.h"
 #include "qmm_gemv_mfma.h"
+#include "qmm_gemv_t1.h"
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -223,6 +224,46 @@ __device__ __forceinline__ void kblock(const typename Dec<KIND>::Raw (&fr)[R], c
   }
 }
 
+// Q4_K and Q6_K take the single-token decoders of qmm_gemv_t1.h: the A rows
+// select sub-blocks, the B operands carry no scales, and the scales are
+// applied to D once per k-block.
+template <int KIND>
+constexpr bool kT1 = KIND == Q4_K || KIND == Q6_K;
+// Selector groups of those decoders (1 for the other kinds: unused).
+template <int KIND, bool = kT1<KIND>>
+struct Nsel {
+  static constexpr int value = 1;
+};
+template <int KIND>
+struct Nsel<KIND, true> {
+  static constexpr int value = gv::T1<KIND>::NSEL;
+};
+
+// One k-block of tile raws r[0 .. R) with those decoders.  abase[c] is this
+// lane's fragment run for selector group c (its own run where its row is that
+// group's A row, the zero run elsewhere); acc[r] gathers this lane's share of
+// row j's dot product (the four lane groups' shares add up to it).
+template <int KIND, int R>
+__device__ __forceinline__ void kblock_t1(const typename Dec<KIND>::Raw (&fr)[R],
+                                          const u32x4 *const (&abase)[gv::T1<KIND>::NSEL], int G, float (&acc)[R],
+                                          float weight) {
+  using Tr = gv::T1<KIND>;
+  using Dd = Dec<KIND>;
+  const half8 ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
+  Fx4 xs = {0.f, 0.f, 0.f, 0.f}, D[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) D[r] = Fx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < Dd::NSTEP; ++st) {
+    const half8 a = __builtin_bit_cast(half8, abase[Tr::sel_of_step(st)][4 * st]);
+    if constexpr (Tr::HAS_MIN) xs = gv::mfma16(a, ones, xs);
+#pragma unroll
+    for (int r = 0; r < R; ++r) D[r] = gv::mfma16(a, Tr::bop(fr[r], st), D[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] += weight * Tr::post(0.f, D[r], xs, Tr::prep(fr[r], G));
+}
+
 // Launch 1.  Workgroup (t, p): pair p's gate tile t and up tile t + n_ff/16
 // of expert ids[p], against token p / topk; S waves split the k-blocks.
 template <int KIND, typename XT, int S, int PD, bool PACKED>
@@ -253,16 +294,26 @@ __global__ __launch_bounds__(64 * S) void gu_kernel(Tiles<KIND, PACKED> W, int E
     for (int r = 0; r < 2; ++r) W.load(e, tiles[r], kb, lane, j, G, raw[slot][r]);
   };
   Fx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float acc1[2] = {0.f, 0.f};  // the single-token decoders' per-lane shares
   const u32x4 *xbase[NS];
 #pragma unroll
   for (int d = 0; d < NS; ++d) xbase[d] = (j == 0 ? ring + d * kFrag : zrun) + G;
   const int xstep = j == 0 ? 4 : 0;
+  constexpr int NSEL = Nsel<KIND>::value;
+  const u32x4 *abase[NS][NSEL];
+  if constexpr (kT1<KIND>) {
+#pragma unroll
+    for (int d = 0; d < NS; ++d)
+#pragma unroll
+      for (int c = 0; c < NSEL; ++c) abase[d][c] = (j == gv::T1<KIND>::arow(c, G) ? ring + d * kFrag : zrun) + G;
+  }
   auto consume = [&](int d) {
     stage_x(ring + d * kFrag, lane, xv[d], 1.0f);
     typename Dd::Raw fr[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) fr[r] = Tiles<KIND, PACKED>::raw(raw[d][r], G);
-    kblock<KIND, 2>(fr, xbase[d], xstep, G, j, acc, 1.0f);
+    if constexpr (kT1<KIND>) kblock_t1<KIND, 2>(fr, abase[d], G, acc1, 1.0f);
+    else kblock<KIND, 2>(fr, xbase[d], xstep, G, j, acc, 1.0f);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();  // slot d is rewritten NS k-blocks later
   };
@@ -281,23 +332,34 @@ __global__ __launch_bounds__(64 * S) void gu_kernel(Tiles<KIND, PACKED> W, int E
   for (int d = 0; d < NS - 1; ++d)
     if (d < cnt - full) consume(d);
 
+  // Row j of the gate and up tiles in lanes 0 .. 15 (token row 0 of D, or
+  // the sum of the four lane groups' shares).
+  float v[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if constexpr (kT1<KIND>) {
+      v[r] = acc1[r] + __shfl_xor(acc1[r], 16);
+      v[r] += __shfl_xor(v[r], 32);
+    } else {
+      v[r] = acc[r][0];
+    }
+  }
   if constexpr (S > 1) {
     __syncthreads();
     float *red = reinterpret_cast<float *>(lds);
     if (wave > 0 && lane < 16) {
-      red[((wave - 1) * 2 + 0) * 16 + lane] = acc[0][0];
-      red[((wave - 1) * 2 + 1) * 16 + lane] = acc[1][0];
+      red[((wave - 1) * 2 + 0) * 16 + lane] = v[0];
+      red[((wave - 1) * 2 + 1) * 16 + lane] = v[1];
     }
     __syncthreads();
     if (wave > 0) return;
 #pragma unroll
     for (int w = 0; w < S - 1; ++w) {
-      acc[0][0] += red[(w * 2 + 0) * 16 + (lane & 15)];
-      acc[1][0] += red[(w * 2 + 1) * 16 + (lane & 15)];
+      v[0] += red[(w * 2 + 0) * 16 + (lane & 15)];
+      v[1] += red[(w * 2 + 1) * 16 + (lane & 15)];
     }
   }
-  // Lanes 0 .. 15 hold row j of the gate and up tiles (token row 0 of D).
-  const float g = acc[0][0], u = acc[1][0];
+  const float g = v[0], u = v[1];
   const float h = g / (1.0f + expf(-g)) * u;
   float m = lane < 16 ? fabsf(h) : 0.f;
 #pragma unroll
@@ -370,17 +432,29 @@ __global__ __launch_bounds__(64 * S) void down_kernel(Tiles<KIND, PACKED> W, int
     }
   }
   Fx4 acc[1] = {{0.f, 0.f, 0.f, 0.f}};
+  float acc1[1] = {0.f};  // the single-token decoders' per-lane share
   const u32x4 *xbase[NS];
 #pragma unroll
   for (int d = 0; d < NS; ++d) xbase[d] = (j == 0 ? ring + d * kFrag : zrun) + G;
   const int xstep = j == 0 ? 4 : 0;
+  constexpr int NSEL = Nsel<KIND>::value;
+  const u32x4 *abase[NS][NSEL];
+  if constexpr (kT1<KIND>) {
+#pragma unroll
+    for (int d = 0; d < NS; ++d)
+#pragma unroll
+      for (int c = 0; c < NSEL; ++c) abase[d][c] = (j == gv::T1<KIND>::arow(c, G) ? ring + d * kFrag : zrun) + G;
+  }
   auto consume = [&](int u, int d) {
     const int s = u / nkb;
     stage_x(ring + d * kFrag, lane, xv[d],
             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xs), s)));
     const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ws), s));
     typename Dd::Raw fr[1] = {Tiles<KIND, PACKED>::raw(raw[d][0], G)};
-    if (__builtin_amdgcn_readlane(es, s) >= 0) kblock<KIND, 1>(fr, xbase[d], xstep, G, j, acc, w);
+    if (__builtin_amdgcn_readlane(es, s) >= 0) {
+      if constexpr (kT1<KIND>) kblock_t1<KIND, 1>(fr, abase[d], G, acc1, w);
+      else kblock<KIND, 1>(fr, xbase[d], xstep, G, j, acc, w);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
   };
@@ -396,16 +470,23 @@ __global__ __launch_bounds__(64 * S) void down_kernel(Tiles<KIND, PACKED> W, int
   for (int d = 0; d < NS - 1; ++d)
     if (d < cnt - full) consume(u0 + full + d, d);
 
+  float v;
+  if constexpr (kT1<KIND>) {
+    v = acc1[0] + __shfl_xor(acc1[0], 16);
+    v += __shfl_xor(v, 32);
+  } else {
+    v = acc[0][0];
+  }
   if constexpr (S > 1) {
     __syncthreads();
     float *red = reinterpret_cast<float *>(lds);
-    if (wave > 0 && lane < 16) red[(wave - 1) * 16 + lane] = acc[0][0];
+    if (wave > 0 && lane < 16) red[(wave - 1) * 16 + lane] = v;
     __syncthreads();
     if (wave > 0) return;
 #pragma unroll
-    for (int w = 0; w < S - 1; ++w) acc[0][0] += red[w * 16 + (lane & 15)];
+    for (int w = 0; w < S - 1; ++w) v += red[w * 16 + (lane & 15)];
   }
-  if (lane < 16) Y[(int64_t)t * K + 16 * c + j] = acc[0][0];
+  if (lane < 16) Y[(int64_t)t * K + 16 * c + j] = v;
 }
 
 template <int KIND, bool PACKED, int S1, int PD1, int S2, int PD2>

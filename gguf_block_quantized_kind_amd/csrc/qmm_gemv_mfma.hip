@@ -519,6 +519,9 @@ bool moe_mfma_supported(int kind, int64_t K) {
 
 hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int mt, int64_t N,
                            int64_t K, const MoeRoute &rt, int items, hipStream_t s, bool packed) {
+  // One pair per item, Q4_K or Q6_K: the single-token decoders.
+  if (mt == 1 && rt.ids != nullptr && items <= 65535 && gemv_t1_supported(kind))
+    return launch_moe_t1(kind, W, X, x_f16, Y, N, K, rt, items, s, packed);
   if (packed) {
     switch (kind) {
       case Q4_K: return gv::run_routed<Q4_K, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
@@ -568,6 +571,9 @@ hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16
 #else
   constexpr int cfg = 0;
 #endif
+  // One token, Q4_K or Q6_K: the single-token decoders.
+  if (M == 1 && gemv_t1_supported(kind) && (cfg == 0 || cfg >= 200))
+    return launch_gemv_t1(kind, W, x, x_f16, y, N, K, s, cfg, false);
   switch (kind) {
     case Q4_K: return gv::run_m<Q4_K>(W, x, x_f16, y, M, N, K, s, cfg);
     case Q6_K: return gv::run_m<Q6_K>(W, x, x_f16, y, M, N, K, s, cfg);

@@ -1,5 +1,6 @@
-// qmm_gemv_t1.hip -- the single-token decode GEMV over repacked Q4_K and
-// Q6_K weights.
+// qmm_gemv_t1.hip -- the single-token decode GEMV for Q4_K and Q6_K, over
+// repacked records or native GGUF rows, and its routed form for expert
+// products of one pair per workgroup.
 //
 // Rows of A as sub-block selectors.  With one token, 15 of the 16 A rows of
 // v_mfma_f32_16x16x32_f16 would hold zeros.  Here, at each MFMA step, lane
@@ -26,14 +27,16 @@
 // error bound of the folded decoders holds unchanged: the activations rounded
 // once to f16, then f32 sums.
 //
-// Work split and pipeline as the single-token shapes of qmm_gemv_mfma.hip: a
-// workgroup of S waves owns one 16-row tile and wave w takes k-blocks
+// (The decoders themselves are in qmm_gemv_t1.h.)  Work split and pipeline
+// as the single-token shapes of qmm_gemv_mfma.hip: a workgroup of S waves
+// owns one 16-row tile and wave w takes k-blocks
 // [w * n / S, (w + 1) * n / S) with PD k-blocks in flight; every load is
 // issued on every path (clamped past the wave's last k-block), so no wait is
 // widened by a branch.
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "qmm_gemv_mfma.h"
 #include "qmm_gemv_t1.h"
@@ -42,13 +45,19 @@
 namespace qmm {
 namespace gv {
 
-template <int KIND, typename XT, int S, int PD, int OCC>
+// PACKED: W holds repacked records (otherwise native GGUF rows of row_bytes
+// bytes).  ROUTED: workgroup (tile, i) serves pair i of an expert product
+// (one pair per workgroup): expert ids[i] (pairs with an id outside [0, E)
+// are skipped), activations row x_per_slot ? i : i / topk, output row i.
+template <int KIND, typename XT, int S, int PD, int OCC, bool PACKED, bool ROUTED>
 __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))) void gemv_t1_kernel(
-    const uint8_t *__restrict__ P, const XT *__restrict__ X, float *__restrict__ Y, int64_t N, int K) {
+    const uint8_t *__restrict__ W, int64_t row_bytes, const XT *__restrict__ X, float *__restrict__ Y, int64_t N,
+    int K, MoeRoute rt) {
   using Tr = T1<KIND>;
   using Dd = typename Tr::Dd;
   using Raw = typename Tr::Raw;
   using X4 = typename XVec<XT>::type;
+  using Held = typename std::conditional<PACKED, typename Rec<KIND>::Packed, Raw>::type;
   constexpr int kFrag = Dd::NSTEP * 4;  // 16-byte fragments of one k-block (step s, group G at 4s + G)
   constexpr int NS = PD + 1;
   constexpr int64_t kRec = 16 * Dd::BYTES;
@@ -59,6 +68,14 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   const int j = lane & 15, G = lane >> 4;
   const int64_t tile = blockIdx.x;
   const int nkb = K / Dd::KB;
+  if constexpr (ROUTED) {
+    const int pair = blockIdx.y;
+    const int e = pair < rt.pairs ? rt.ids[pair] : -1;
+    if (e < 0 || e >= rt.E) return;  // the whole workgroup, before any barrier
+    W += (int64_t)e * (PACKED ? (N + 15) / 16 * nkb * kRec : N * row_bytes);
+    X += (int64_t)(rt.x_per_slot ? pair : pair / rt.topk) * K;
+    Y += (int64_t)pair * N;
+  }
   const int kb0 = (int)((int64_t)wave * nkb / S), kb1 = (int)((int64_t)(wave + 1) * nkb / S);
   const int kb_last = max(kb1 - 1, 0);
   u32x4 *zrun = lds + wave * (NS + 1) * kFrag, *ring = zrun + kFrag;
@@ -74,13 +91,16 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
 #pragma unroll
     for (int c = 0; c < Tr::NSEL; ++c) abase[d][c] = (j == Tr::arow(c, G) ? ring + d * kFrag : zrun) + G;
 
-  const uint8_t *wt = P + tile * nkb * kRec;
-  typename Rec<KIND>::Packed raw[NS];
+  // Records of this tile, or row j of it (rows past N decode the last row;
+  // their outputs are not stored).
+  const uint8_t *wt = PACKED ? W + tile * nkb * kRec : W + min(tile * 16 + j, N - 1) * row_bytes;
+  Held raw[NS];
   X4 xv[NS];
   auto issue = [&](int kb, int slot) {
     kb = min(kb, kb_last);
     __builtin_memcpy(&xv[slot], X + xoff + (int64_t)kb * Dd::KB, sizeof(X4));
-    Rec<KIND>::load(wt + kb * kRec, lane, j, G, raw[slot]);
+    if constexpr (PACKED) Rec<KIND>::load(wt + kb * kRec, lane, j, G, raw[slot]);
+    else Dd::load(wt + (int64_t)kb * Dd::BYTES, G, raw[slot]);
   };
   float acc = 0.0f;
   const half8 ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
@@ -93,7 +113,9 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const Raw fr = Rec<KIND>::unpack(raw[d], G);
+    Raw fr;
+    if constexpr (PACKED) fr = Rec<KIND>::unpack(raw[d], G);
+    else fr = raw[d];
     const typename Tr::Sc sc = Tr::prep(fr, G);
     floatx4 D = {0.f, 0.f, 0.f, 0.f}, Xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -140,56 +162,90 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   if (lane < 16 && row < N) Y[row] = acc;
 }
 
-template <int KIND, int S, int PD, int OCC = 1>
-static hipError_t run_t1(const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K, hipStream_t s) {
+template <int KIND, int S, int PD, int OCC = 1, bool PACKED = true, bool ROUTED = false>
+static hipError_t run_t1(const uint8_t *W, const void *x, int x_f16, float *y, int64_t N, int64_t K, hipStream_t s,
+                         const MoeRoute &rt = MoeRoute{}, int items = 1) {
   constexpr int kFrag = T1<KIND>::Dd::NSTEP * 4;
   const size_t lds = std::max<size_t>((size_t)S * (PD + 2) * kFrag * 16, (size_t)(S - 1) * 16 * 4);
-  const dim3 grid((unsigned)((N + 15) / 16)), block(64 * S);
+  const int64_t row_bytes = (K / Geometry<KIND>::elems) * Geometry<KIND>::bytes;
+  // Tile-major grid: workgroup i runs on XCD i mod 8, and the pairs of one
+  // tile (a multiple of 8 apart when the tile count is) share its L2.
+  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)items), block(64 * S);
   if (x_f16)
-    hipLaunchKernelGGL((gemv_t1_kernel<KIND, _Float16, S, PD, OCC>), grid, block, lds, s, P, (const _Float16 *)x, y,
-                       N, (int)K);
+    hipLaunchKernelGGL((gemv_t1_kernel<KIND, _Float16, S, PD, OCC, PACKED, ROUTED>), grid, block, lds, s, W,
+                       row_bytes, (const _Float16 *)x, y, N, (int)K, rt);
   else
-    hipLaunchKernelGGL((gemv_t1_kernel<KIND, float, S, PD, OCC>), grid, block, lds, s, P, (const float *)x, y, N,
-                       (int)K);
+    hipLaunchKernelGGL((gemv_t1_kernel<KIND, float, S, PD, OCC, PACKED, ROUTED>), grid, block, lds, s, W, row_bytes,
+                       (const float *)x, y, N, (int)K, rt);
   return hipGetLastError();
 }
 
-template <int KIND>
+template <int KIND, bool PACKED>
 static hipError_t run_t1_k(const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K, hipStream_t s,
                            int cfg) {
 #ifdef QMM_TUNING
   switch (cfg) {
-    case 201: return run_t1<KIND, 4, 1, 4>(P, x, x_f16, y, N, K, s);
-    case 202: return run_t1<KIND, 4, 1>(P, x, x_f16, y, N, K, s);
-    case 203: return run_t1<KIND, 4, 2>(P, x, x_f16, y, N, K, s);
-    case 204: return run_t1<KIND, 2, 1>(P, x, x_f16, y, N, K, s);
-    case 205: return run_t1<KIND, 2, 2>(P, x, x_f16, y, N, K, s);
-    case 206: return run_t1<KIND, 2, 3>(P, x, x_f16, y, N, K, s);
-    case 207: return run_t1<KIND, 8, 1>(P, x, x_f16, y, N, K, s);
-    case 208: return run_t1<KIND, 8, 2>(P, x, x_f16, y, N, K, s);
-    case 209: return run_t1<KIND, 4, 3>(P, x, x_f16, y, N, K, s);
-    case 210: return run_t1<KIND, 1, 3>(P, x, x_f16, y, N, K, s);
-    case 211: return run_t1<KIND, 4, 2, 3>(P, x, x_f16, y, N, K, s);
-    case 212: return run_t1<KIND, 16, 1>(P, x, x_f16, y, N, K, s);
+    case 201: return run_t1<KIND, 4, 1, 4, PACKED>(P, x, x_f16, y, N, K, s);
+    case 202: return run_t1<KIND, 4, 1, 1, PACKED>(P, x, x_f16, y, N, K, s);
+    case 203: return run_t1<KIND, 4, 2, 1, PACKED>(P, x, x_f16, y, N, K, s);
+    case 204: return run_t1<KIND, 2, 1, 1, PACKED>(P, x, x_f16, y, N, K, s);
+    case 205: return run_t1<KIND, 2, 2, 1, PACKED>(P, x, x_f16, y, N, K, s);
+    case 206: return run_t1<KIND, 2, 3, 1, PACKED>(P, x, x_f16, y, N, K, s);
+    case 207: return run_t1<KIND, 8, 1, 1, PACKED>(P, x, x_f16, y, N, K, s);
+    case 208: return run_t1<KIND, 8, 2, 1, PACKED>(P, x, x_f16, y, N, K, s);
+    case 209: return run_t1<KIND, 4, 3, 1, PACKED>(P, x, x_f16, y, N, K, s);
+    case 210: return run_t1<KIND, 1, 3, 1, PACKED>(P, x, x_f16, y, N, K, s);
+    case 211: return run_t1<KIND, 4, 2, 3, PACKED>(P, x, x_f16, y, N, K, s);
+    case 212: return run_t1<KIND, 16, 1, 1, PACKED>(P, x, x_f16, y, N, K, s);
     default: break;
   }
 #else
   (void)cfg;
 #endif
-  // Two waves per tile, one k-block in flight (measured best for both kinds
-  // at 14336 x 4096 among 1 to 16 waves and 1 to 3 k-blocks in flight).
-  return run_t1<KIND, 2, 1>(P, x, x_f16, y, N, K, s);
+  // Two waves per tile (measured best for both kinds at 14336 x 4096 among 1
+  // to 16 waves and 1 to 3 k-blocks in flight): one k-block in flight over
+  // records, two over native rows (whose per-lane field loads are slower to
+  // land; Q4_K 12.0 -> 11.0 us, Q6_K 20.2 -> 18.0 us).
+  if constexpr (!PACKED) return run_t1<KIND, 2, 2, 1, false>(P, x, x_f16, y, N, K, s);
+  return run_t1<KIND, 2, 1, 1, true>(P, x, x_f16, y, N, K, s);
+}
+
+// Routed pairs: K of three k-blocks (an expert down matrix of 768 columns)
+// takes three waves of one k-block each, else the shapes above.
+template <int KIND, bool PACKED>
+static hipError_t run_t1_routed(const uint8_t *W, const void *x, int x_f16, float *y, int64_t N, int64_t K,
+                                hipStream_t s, const MoeRoute &rt, int items) {
+  if (K == 3 * T1<KIND>::Dd::KB) return run_t1<KIND, 3, 1, 1, PACKED, true>(W, x, x_f16, y, N, K, s, rt, items);
+  return run_t1<KIND, 2, PACKED ? 1 : 2, 1, PACKED, true>(W, x, x_f16, y, N, K, s, rt, items);
 }
 
 }  // namespace gv
 
 bool gemv_t1_supported(int kind) { return kind == Q4_K || kind == Q6_K; }
 
-hipError_t launch_gemv_t1(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K,
-                          hipStream_t s, int cfg) {
+hipError_t launch_gemv_t1(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int64_t N, int64_t K,
+                          hipStream_t s, int cfg, bool packed) {
   switch (kind) {
-    case Q4_K: return gv::run_t1_k<Q4_K>(P, x, x_f16, y, N, K, s, cfg);
-    case Q6_K: return gv::run_t1_k<Q6_K>(P, x, x_f16, y, N, K, s, cfg);
+    case Q4_K:
+      return packed ? gv::run_t1_k<Q4_K, true>(W, x, x_f16, y, N, K, s, cfg)
+                    : gv::run_t1_k<Q4_K, false>(W, x, x_f16, y, N, K, s, cfg);
+    case Q6_K:
+      return packed ? gv::run_t1_k<Q6_K, true>(W, x, x_f16, y, N, K, s, cfg)
+                    : gv::run_t1_k<Q6_K, false>(W, x, x_f16, y, N, K, s, cfg);
+    default: break;
+  }
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_moe_t1(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int64_t N, int64_t K,
+                         const MoeRoute &rt, int items, hipStream_t s, bool packed) {
+  switch (kind) {
+    case Q4_K:
+      return packed ? gv::run_t1_routed<Q4_K, true>(W, X, x_f16, Y, N, K, s, rt, items)
+                    : gv::run_t1_routed<Q4_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
+    case Q6_K:
+      return packed ? gv::run_t1_routed<Q6_K, true>(W, X, x_f16, Y, N, K, s, rt, items)
+                    : gv::run_t1_routed<Q6_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
     default: break;
   }
   return hipErrorNotSupported;

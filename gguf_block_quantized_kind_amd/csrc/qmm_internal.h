@@ -34,10 +34,11 @@ hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f
 hipError_t launch_gemv_xs(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
                           int64_t K, hipStream_t s, int cfg = 0);
 // Its single-token form for Q4_K and Q6_K (qmm_gemv_t1.hip): sub-blocks
-// kept apart in the rows of the matrix-core product, scales applied after it.
+// kept apart in the rows of the matrix-core product, scales applied after it;
+// W repacked (packed) or native rows.
 bool gemv_t1_supported(int kind);
-hipError_t launch_gemv_t1(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K,
-                          hipStream_t s, int cfg = 0);
+hipError_t launch_gemv_t1(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int64_t N, int64_t K,
+                          hipStream_t s, int cfg = 0, bool packed = true);
 
 // The prefill GEMM over repacked weights (any M; qmm_gemm_pk.hip), for the
 // kinds gemm_packed_supported names; P offsets must fit in 32 bits.
@@ -118,6 +119,10 @@ struct MoeRoute {
 // The matrix-core expert kernel: one workgroup per (work item, 16-row
 // tile); a work item is up to `mt` (1, 8 or 16) pairs of one expert.
 bool moe_mfma_supported(int kind, int64_t K);
+// The routed single-token form of launch_gemv_t1: one pair per workgroup,
+// the pair's expert read from rt.ids (MoeRoute below).
+hipError_t launch_moe_t1(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int64_t N, int64_t K,
+                         const MoeRoute &rt, int items, hipStream_t s, bool packed);
 // packed: W holds the experts' repacked records (expert e at
 // e * packed_bytes_of(kind, N, K)).
 hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int mt, int64_t N,

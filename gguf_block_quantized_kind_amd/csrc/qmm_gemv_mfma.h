@@ -106,9 +106,10 @@ __device__ __forceinline__ floatx4 mfma4f32(float a, float b, floatx4 c) {
 //   x_off(s, G, h)       first of the 4 consecutive elements of half h (0, 1)
 //                        of the 8 elements step s gives G; inside a half the
 //                        pairs are ordered (0,2), (1,3)
-//   STEP_SCALE           every step has its own f32 scale: post_step(acc, D,
-//                        raw, s) adds scale(s) * D after each step's MFMA
-//                        (which starts from zero); otherwise post() below
+//   STEP_SCALE           every step has its own f32 scale, scale(raw, s):
+//                        post_step(acc, D, raw, s) adds it times D after
+//                        each step's MFMA (which starts from zero); otherwise
+//                        post() below
 //   Raw / load           the lane's bytes of one k-block
 //   Sc / prep            the lane's scales for that k-block
 //   bop(raw, sc, s, p)   B operand p of step s
@@ -325,9 +326,8 @@ struct DecQ4_0 : StepBase {
   __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {
     return bytes_b(r.q[s] & 0x0F0F0F0Fu, (r.q[s] >> 4) & 0x0F0F0F0Fu, kNeg1032);
   }
-  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
-    return acc + lo_f16(r.d[s]) * D;
-  }
+  __device__ static float scale(const Raw &r, int s) { return lo_f16(r.d[s]); }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) { return acc + scale(r, s) * D; }
 };
 
 // Q5_0 (22 B): f16 d, u32 qh (bit e: fifth bit of element e), 16 code
@@ -349,9 +349,8 @@ struct DecQ5_0 : StepBase {
     const uint32_t hi = ((r.q[s] >> 4) & 0x0F0F0F0Fu) | (spread4(r.qh[s] >> 16) << 4);
     return bytes_b(lo, hi, kNeg1040);
   }
-  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
-    return acc + lo_f16(r.d[s]) * D;
-  }
+  __device__ static float scale(const Raw &r, int s) { return lo_f16(r.d[s]); }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) { return acc + scale(r, s) * D; }
 };
 
 // Q8_0 (34 B): f16 d, 32 int8 codes; w = d * q.  Code XOR 0x80 = q + 128.
@@ -370,9 +369,8 @@ struct DecQ8_0 : StepBase {
   __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {
     return bytes_b(r.q[s].x ^ 0x80808080u, r.q[s].y ^ 0x80808080u, kNeg1152);
   }
-  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
-    return acc + lo_f16(r.d[s]) * D;
-  }
+  __device__ static float scale(const Raw &r, int s) { return lo_f16(r.d[s]); }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) { return acc + scale(r, s) * D; }
 };
 
 // IQ4_NL (18 B): f16 d, 16 code bytes packed as Q4_0; w = d * table[code];
@@ -391,9 +389,8 @@ struct DecIQ4NL : StepBase {
   __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {
     return bytes_b(iq4_lookup(r.q[s] & 0x0F0F0F0Fu), iq4_lookup((r.q[s] >> 4) & 0x0F0F0F0Fu), kNeg1152);
   }
-  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
-    return acc + lo_f16(r.d[s]) * D;
-  }
+  __device__ static float scale(const Raw &r, int s) { return lo_f16(r.d[s]); }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) { return acc + scale(r, s) * D; }
 };
 
 // MXFP4 (17 B): E8M0 byte, 16 E2M1 code bytes packed as Q4_0;
@@ -421,9 +418,8 @@ struct DecMXFP4 : StepBase {
     return pack8(perm(p2, p0, 0x05040100u), perm(p3, p1, 0x05040100u), perm(p2, p0, 0x07060302u),
                  perm(p3, p1, 0x07060302u));
   }
-  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
-    return acc + (e8m0_to_f32(r.e[s]) * 0.5f) * D;
-  }
+  __device__ static float scale(const Raw &r, int s) { return e8m0_to_f32(r.e[s]) * 0.5f; }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) { return acc + scale(r, s) * D; }
 };
 
 // IQ4_XS (136 B / 256): f16 d, u16 scales_h, scales_l[4], then eight
@@ -442,13 +438,14 @@ struct DecIQ4XS : StepBase {
   __device__ static half8 bop(const Raw &r, const Sc &, int s, int) {
     return bytes_b(iq4_lookup(r.q[s] & 0x0F0F0F0Fu), iq4_lookup((r.q[s] >> 4) & 0x0F0F0F0Fu), kNeg1152);
   }
-  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) {
+  __device__ static float scale(const Raw &r, int s) {
     const float d = lo_f16(r.h.x);
     const uint32_t sh = r.h.x >> 16;
     const uint32_t sl = (r.h.y >> (4 * s)) & 15u;  // nibble s of scales_l
     const int ls = (int)(sl | (((sh >> (2 * s)) & 3u) << 4));
-    return acc + (d * (float)(ls - 32)) * D;
+    return d * (float)(ls - 32);
   }
+  __device__ static floatx4 post_step(floatx4 acc, floatx4 D, const Raw &r, int s) { return acc + scale(r, s) * D; }
 };
 
 // ---------------------------------------------------------------------------

@@ -380,11 +380,10 @@ static hipError_t run_routed(const uint8_t *W, const void *x, int x_f16, float *
   return run<KIND, 16, 1, 4, 1, 1, true, PACKED>(W, x, x_f16, y, 16, N, K, s, rt, items);
 }
 
-// Launch shapes over the repacked layout (no staging).  One token: the
-// folded decoders keep the native shape; the step-scaled ones split K over
-// more waves (8, or 16 with one k-block in flight when there are at most 256
-// tiles), as measured best at 4096 and 11008 rows.  Fewer waves per tile
-// (two tiles per wave) measured 40-70% slower at one token.
+// Launch shapes over the repacked layout (no staging), for what the kernels
+// of qmm_gemv_t1.hip and qmm_gemv_xs.hip do not take (in default builds:
+// Q2_K, Q3_K and Q5_K at one token).  Fewer waves per tile (two tiles per
+// wave) measured 40-70% slower at one token.
 template <int KIND>
 static hipError_t run_packed(const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,
                              hipStream_t s, int cfg) {
@@ -440,19 +439,6 @@ static hipError_t run_packed(const uint8_t *P, const void *x, int x_f16, float *
 #else
   (void)cfg;
 #endif
-  if constexpr (Dec<KIND>::STEP_SCALE) {
-    if (M <= 1) {
-      if (N <= 4096) return run<KIND, 1, 16, 1, 1, 1, false, true>(P, x, x_f16, y, M, N, K, s);
-      return run<KIND, 1, 8, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
-    }
-  }
-  if constexpr (KIND == Q4_K) {
-    // Four waves per tile with one k-block in flight each, held to 128
-    // registers so that all 3584 waves of a 14336-row matrix are resident
-    // at once (measured about 4% faster than the shape below; Q6_K's
-    // decoder spills under the same cap).
-    if (M <= 1) return run<KIND, 1, 4, 1, 1, 4, false, true>(P, x, x_f16, y, M, N, K, s);
-  }
   if (M <= 1) return run<KIND, 1, 2, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
   if (M <= 2) return run<KIND, 2, 2, 1, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
   if (M <= 4) return run<KIND, 4, 2, 2, 2, 1, false, true>(P, x, x_f16, y, M, N, K, s);
@@ -486,9 +472,9 @@ hipError_t launch_gemv_packed(int kind, const uint8_t *P, const void *x, int x_f
   // Two to eight tokens: the kernel that stages activations per workgroup
   // (tuning shapes below 100 select this file's kernels instead).
   if (M > 1 && (cfg == 0 || cfg >= 100)) return launch_gemv_xs(kind, P, x, x_f16, y, M, N, K, s, cfg);
-  // One token, Q4_K or Q6_K: the kernel that applies sub-block scales after
+  // One token: the kernel that applies the sub-block or block scales after
   // the products (tuning shapes from 200 up).
-  if (M == 1 && gemv_t1_supported(kind) && (cfg == 0 || cfg >= 200))
+  if (M == 1 && gemv_t1_supported(kind, true) && (cfg == 0 || cfg >= 200))
     return launch_gemv_t1(kind, P, x, x_f16, y, N, K, s, cfg);
   switch (kind) {
     case Q4_K: return gv::run_packed<Q4_K>(P, x, x_f16, y, M, N, K, s, cfg);
@@ -519,8 +505,9 @@ bool moe_mfma_supported(int kind, int64_t K) {
 
 hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int mt, int64_t N,
                            int64_t K, const MoeRoute &rt, int items, hipStream_t s, bool packed) {
-  // One pair per item, Q4_K or Q6_K: the single-token decoders.
-  if (mt == 1 && rt.ids != nullptr && items <= 65535 && gemv_t1_supported(kind))
+  // One pair per item, Q4_K or Q6_K: the single-token decoders (the
+  // step-scaled kinds keep this file's kernel for routed pairs).
+  if (mt == 1 && rt.ids != nullptr && items <= 65535 && (kind == Q4_K || kind == Q6_K))
     return launch_moe_t1(kind, W, X, x_f16, Y, N, K, rt, items, s, packed);
   if (packed) {
     switch (kind) {
@@ -572,7 +559,7 @@ hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16
   constexpr int cfg = 0;
 #endif
   // One token, Q4_K or Q6_K: the single-token decoders.
-  if (M == 1 && gemv_t1_supported(kind) && (cfg == 0 || cfg >= 200))
+  if (M == 1 && gemv_t1_supported(kind, false) && (cfg == 0 || cfg >= 200))
     return launch_gemv_t1(kind, W, x, x_f16, y, N, K, s, cfg, false);
   switch (kind) {
     case Q4_K: return gv::run_m<Q4_K>(W, x, x_f16, y, M, N, K, s, cfg);

@@ -10,6 +10,10 @@
 //         16q * 2^-24 for a high nibble left in place); D rows 4G, 4G + 1
 //         are sub-blocks 2G, 2G + 1 of lane group G.
 //   Q6_K  B holds q - 32 exactly; D row 8h + 2g + a is sub-block 8h + 2g + a.
+//   the 32-element kinds and IQ4_XS (one block or group per step, its own
+//         scale): B is the step-scaled decoder's exact code value, A row s
+//         holds step s's activations, so D row s is block s's dot product;
+//         lane group G = 0, 1 holds rows 4G .. 4G + 3 and scales them.
 //
 // Every product is exact in f32 and the matrix cores accumulate in f32, so
 // the folded decoders' error bound holds: activations rounded once to f16,
@@ -112,6 +116,40 @@ template <> struct T1<Q6_K> {
     return acc + s.d * (s.sc[0] * D[0] + s.sc[1] * D[1] + s.sc[2] * D[2] + s.sc[3] * D[3]);
   }
 };
+
+// Step-scaled kinds: eight steps, eight A rows (row s for step s, whatever
+// the lane group), no minimum term.
+template <int KIND>
+struct T1Step {
+  using Dd = Dec<KIND>;
+  using Raw = typename Dd::Raw;
+  static constexpr bool HAS_MIN = false;
+  static constexpr int NSEL = 8;
+  __device__ static int sel_of_step(int s) { return s; }
+  __device__ static int arow(int c, int) { return c; }
+  struct Sc { float s[4]; };
+  // Lane (j, G) holds D rows 4G .. 4G + 3: blocks 4G + q for G = 0, 1, and
+  // zero rows for G = 2, 3 (whatever scale they take).
+  __device__ static Sc prep(const Raw &r, int G) {
+    Sc o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float lo = Dd::scale(r, q), hi = Dd::scale(r, 4 + q);
+      o.s[q] = (G & 1) ? hi : lo;
+    }
+    return o;
+  }
+  __device__ static half8 bop(const Raw &r, int st) { return Dd::bop(r, typename Dd::Sc{}, st, 0); }
+  __device__ static float post(float acc, floatx4 D, floatx4, const Sc &s) {
+    return acc + s.s[0] * D[0] + s.s[1] * D[1] + s.s[2] * D[2] + s.s[3] * D[3];
+  }
+};
+template <> struct T1<Q4_0> : T1Step<Q4_0> {};
+template <> struct T1<Q5_0> : T1Step<Q5_0> {};
+template <> struct T1<Q8_0> : T1Step<Q8_0> {};
+template <> struct T1<IQ4_NL> : T1Step<IQ4_NL> {};
+template <> struct T1<MXFP4> : T1Step<MXFP4> {};
+template <> struct T1<IQ4_XS> : T1Step<IQ4_XS> {};
 
 }  // namespace gv
 }  // namespace qmm

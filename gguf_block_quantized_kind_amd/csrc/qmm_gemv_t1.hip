@@ -202,12 +202,22 @@ static hipError_t run_t1_k(const uint8_t *P, const void *x, int x_f16, float *y,
 #else
   (void)cfg;
 #endif
-  // Two waves per tile (measured best for both kinds at 14336 x 4096 among 1
-  // to 16 waves and 1 to 3 k-blocks in flight): one k-block in flight over
-  // records, two over native rows (whose per-lane field loads are slower to
-  // land; Q4_K 12.0 -> 11.0 us, Q6_K 20.2 -> 18.0 us).
-  if constexpr (!PACKED) return run_t1<KIND, 2, 2, 1, false>(P, x, x_f16, y, N, K, s);
-  return run_t1<KIND, 2, 1, 1, true>(P, x, x_f16, y, N, K, s);
+  if constexpr (Dec<KIND>::STEP_SCALE) {
+    // The step-scaled kinds (records only) decode with more VALU per byte:
+    // more waves per tile, one k-block in flight each; MXFP4 at four waves
+    // held to 128 registers (measured over 1 to 16 waves and 1 to 2 k-blocks
+    // in flight at 4096 x 4096 and 11008 x 4096).
+    if (N <= 4096) return run_t1<KIND, 16, 1, 1, true>(P, x, x_f16, y, N, K, s);
+    if constexpr (KIND == MXFP4) return run_t1<KIND, 4, 1, 4, true>(P, x, x_f16, y, N, K, s);
+    return run_t1<KIND, 8, 1, 1, true>(P, x, x_f16, y, N, K, s);
+  } else {
+    // Two waves per tile (measured best for Q4_K and Q6_K at 14336 x 4096
+    // among 1 to 16 waves and 1 to 3 k-blocks in flight): one k-block in
+    // flight over records, two over native rows (whose per-lane field loads
+    // are slower to land; Q4_K 12.0 -> 11.0 us, Q6_K 20.2 -> 18.0 us).
+    if constexpr (!PACKED) return run_t1<KIND, 2, 2, 1, false>(P, x, x_f16, y, N, K, s);
+    return run_t1<KIND, 2, 1, 1, true>(P, x, x_f16, y, N, K, s);
+  }
 }
 
 // Routed pairs: K of three k-blocks (an expert down matrix of 768 columns)
@@ -221,17 +231,28 @@ static hipError_t run_t1_routed(const uint8_t *W, const void *x, int x_f16, floa
 
 }  // namespace gv
 
-bool gemv_t1_supported(int kind) { return kind == Q4_K || kind == Q6_K; }
+// Over native rows only the folded kinds: the step-scaled kinds read native
+// rows through the LDS staging of qmm_gemv_mfma.hip.
+bool gemv_t1_supported(int kind, bool packed) {
+  switch (kind) {
+    case Q4_K: case Q6_K: return true;
+    case Q4_0: case Q5_0: case Q8_0: case IQ4_NL: case MXFP4: case IQ4_XS: return packed;
+    default: return false;
+  }
+}
 
 hipError_t launch_gemv_t1(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int64_t N, int64_t K,
                           hipStream_t s, int cfg, bool packed) {
+  if (!gemv_t1_supported(kind, packed)) return hipErrorNotSupported;
   switch (kind) {
-    case Q4_K:
-      return packed ? gv::run_t1_k<Q4_K, true>(W, x, x_f16, y, N, K, s, cfg)
-                    : gv::run_t1_k<Q4_K, false>(W, x, x_f16, y, N, K, s, cfg);
-    case Q6_K:
-      return packed ? gv::run_t1_k<Q6_K, true>(W, x, x_f16, y, N, K, s, cfg)
-                    : gv::run_t1_k<Q6_K, false>(W, x, x_f16, y, N, K, s, cfg);
+    case Q4_K: return packed ? gv::run_t1_k<Q4_K, true>(W, x, x_f16, y, N, K, s, cfg)
+                             : gv::run_t1_k<Q4_K, false>(W, x, x_f16, y, N, K, s, cfg);
+    case Q6_K: return packed ? gv::run_t1_k<Q6_K, true>(W, x, x_f16, y, N, K, s, cfg)
+                             : gv::run_t1_k<Q6_K, false>(W, x, x_f16, y, N, K, s, cfg);
+#define QMM_CASE(K_) \
+  case K_: return gv::run_t1_k<K_, true>(W, x, x_f16, y, N, K, s, cfg);
+    QMM_CASE(Q4_0) QMM_CASE(Q5_0) QMM_CASE(Q8_0) QMM_CASE(IQ4_NL) QMM_CASE(MXFP4) QMM_CASE(IQ4_XS)
+#undef QMM_CASE
     default: break;
   }
   return hipErrorNotSupported;
@@ -239,13 +260,16 @@ hipError_t launch_gemv_t1(int kind, const uint8_t *W, const void *x, int x_f16, 
 
 hipError_t launch_moe_t1(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int64_t N, int64_t K,
                          const MoeRoute &rt, int items, hipStream_t s, bool packed) {
+  if (!gemv_t1_supported(kind, packed)) return hipErrorNotSupported;
   switch (kind) {
-    case Q4_K:
-      return packed ? gv::run_t1_routed<Q4_K, true>(W, X, x_f16, Y, N, K, s, rt, items)
-                    : gv::run_t1_routed<Q4_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
-    case Q6_K:
-      return packed ? gv::run_t1_routed<Q6_K, true>(W, X, x_f16, Y, N, K, s, rt, items)
-                    : gv::run_t1_routed<Q6_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
+    case Q4_K: return packed ? gv::run_t1_routed<Q4_K, true>(W, X, x_f16, Y, N, K, s, rt, items)
+                             : gv::run_t1_routed<Q4_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
+    case Q6_K: return packed ? gv::run_t1_routed<Q6_K, true>(W, X, x_f16, Y, N, K, s, rt, items)
+                             : gv::run_t1_routed<Q6_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
+#define QMM_CASE(K_) \
+  case K_: return gv::run_t1_routed<K_, true>(W, X, x_f16, Y, N, K, s, rt, items);
+    QMM_CASE(Q4_0) QMM_CASE(Q5_0) QMM_CASE(Q8_0) QMM_CASE(IQ4_NL) QMM_CASE(MXFP4) QMM_CASE(IQ4_XS)
+#undef QMM_CASE
     default: break;
   }
   return hipErrorNotSupported;

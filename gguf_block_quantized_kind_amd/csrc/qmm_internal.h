@@ -36,7 +36,7 @@ hipError_t launch_gemv_xs(int kind, const uint8_t *P, const void *x, int x_f16, 
 // Its single-token form for Q4_K and Q6_K (qmm_gemv_t1.hip): sub-blocks
 // kept apart in the rows of the matrix-core product, scales applied after it;
 // W repacked (packed) or native rows.
-bool gemv_t1_supported(int kind);
+bool gemv_t1_supported(int kind, bool packed = true);
 hipError_t launch_gemv_t1(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int64_t N, int64_t K,
                           hipStream_t s, int cfg = 0, bool packed = true);
 

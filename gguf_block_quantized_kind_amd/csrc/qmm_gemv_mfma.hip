@@ -505,9 +505,9 @@ bool moe_mfma_supported(int kind, int64_t K) {
 
 hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int mt, int64_t N,
                            int64_t K, const MoeRoute &rt, int items, hipStream_t s, bool packed) {
-  // One pair per item, Q4_K or Q6_K: the single-token decoders (the
+  // One pair per item, a super-block kind: the single-token decoders (the
   // step-scaled kinds keep this file's kernel for routed pairs).
-  if (mt == 1 && rt.ids != nullptr && items <= 65535 && (kind == Q4_K || kind == Q6_K))
+  if (mt == 1 && rt.ids != nullptr && items <= 65535 && gemv_t1_supported(kind, false))
     return launch_moe_t1(kind, W, X, x_f16, Y, N, K, rt, items, s, packed);
   if (packed) {
     switch (kind) {
@@ -558,7 +558,7 @@ hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16
 #else
   constexpr int cfg = 0;
 #endif
-  // One token, Q4_K or Q6_K: the single-token decoders.
+  // One token, a super-block kind: the single-token decoders.
   if (M == 1 && gemv_t1_supported(kind, false) && (cfg == 0 || cfg >= 200))
     return launch_gemv_t1(kind, W, x, x_f16, y, N, K, s, cfg, false);
   switch (kind) {

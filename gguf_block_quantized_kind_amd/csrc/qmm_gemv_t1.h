@@ -10,6 +10,9 @@
 //         16q * 2^-24 for a high nibble left in place); D rows 4G, 4G + 1
 //         are sub-blocks 2G, 2G + 1 of lane group G.
 //   Q6_K  B holds q - 32 exactly; D row 8h + 2g + a is sub-block 8h + 2g + a.
+//   Q5_K, Q2_K, Q3_K  the raw codes (with the fifth or high-mask bit) as
+//         subnormals, as Q4_K; the Q3_K offset -4 enters through the
+//         activation sums.
 //   the 32-element kinds and IQ4_XS (one block or group per step, its own
 //         scale): B is the step-scaled decoder's exact code value, A row s
 //         holds step s's activations, so D row s is block s's dot product;
@@ -57,7 +60,7 @@ template <> struct T1<Q4_K> {
     s.g1 = -dmin * (float)((mn2 >> 8) & 0xFFu);
     return s;
   }
-  __device__ static half8 bop(const Raw &r, int st) {
+  __device__ static half8 bop(const Raw &r, const Sc &, int st) {
     const int w = st & 3;
     const uint32_t v0 = w < 2 ? (w == 0 ? r.q0.x : r.q0.z) : (w == 2 ? r.q1.x : r.q1.z);
     const uint32_t v1 = w < 2 ? (w == 0 ? r.q0.y : r.q0.w) : (w == 2 ? r.q1.y : r.q1.w);
@@ -89,7 +92,7 @@ template <> struct T1<Q6_K> {
     s.d = lo_f16(r.d);
     return s;
   }
-  __device__ static half8 bop(const Raw &r, int st) {
+  __device__ static half8 bop(const Raw &r, const Sc &, int st) {
     const int g = st >> 1, w = 2 * (st & 1);
     const u32x4 &ql = (g & 1) ? r.ql1 : r.ql0;
     const uint32_t q0 = w == 0 ? ql.x : ql.z, q1 = w == 0 ? ql.y : ql.w;
@@ -117,6 +120,120 @@ template <> struct T1<Q6_K> {
   }
 };
 
+// Q5_K: as Q4_K, with the fifth bit just above the nibble (bit 4 for a low
+// nibble, bit 8 for a high nibble left in place): q5 * 2^-24 or
+// 16 q5 * 2^-24, still subnormal.
+template <> struct T1<Q5_K> {
+  using Dd = DecQ5K;
+  using Raw = DecQ5K::Raw;
+  static constexpr bool HAS_MIN = true;
+  static constexpr int NSEL = 2;
+  __device__ static int sel_of_step(int s) { return s >> 2; }
+  __device__ static int arow(int c, int G) { return 4 * G + c; }
+  struct Sc : T1<Q4_K>::Sc { int sh; };  // sh = 2G: this group's fifth-bit position in qh
+  __device__ static Sc prep(const Raw &r, int G) {
+    Sc s;
+    static_cast<T1<Q4_K>::Sc &>(s) = T1<Q4_K>::prep(DecQ4K::Raw{r.hdr, r.q0, r.q1}, G);
+    s.sh = 2 * G;
+    return s;
+  }
+  __device__ static half8 bop(const Raw &r, const Sc &s, int st) {
+    const int w = st & 3;
+    const uint32_t v0 = w < 2 ? (w == 0 ? r.q0.x : r.q0.z) : (w == 2 ? r.q1.x : r.q1.z);
+    const uint32_t v1 = w < 2 ? (w == 0 ? r.q0.y : r.q0.w) : (w == 2 ? r.q1.y : r.q1.w);
+    const uint32_t g0 = w < 2 ? (w == 0 ? r.h0.x : r.h0.z) : (w == 2 ? r.h1.x : r.h1.z);
+    const uint32_t g1 = w < 2 ? (w == 0 ? r.h0.y : r.h0.w) : (w == 2 ? r.h1.y : r.h1.w);
+    const uint32_t a0 = g0 >> s.sh, a1 = g1 >> s.sh;
+    const bool lo = st < 4;
+    const uint32_t qm = lo ? 0x000F000Fu : 0x00F000F0u, hm = lo ? 0x00100010u : 0x01000100u;
+    return pack8(and_or(lo ? a0 << 4 : a0 << 7, hm, v0 & qm), and_or(lo ? a0 >> 4 : a0 >> 1, hm, (v0 >> 8) & qm),
+                 and_or(lo ? a1 << 4 : a1 << 7, hm, v1 & qm), and_or(lo ? a1 >> 4 : a1 >> 1, hm, (v1 >> 8) & qm));
+  }
+  __device__ static float post(float acc, floatx4 D, floatx4 X, const Sc &s) { return T1<Q4_K>::post(acc, D, X, s); }
+};
+
+// Q2_K: step s = 2j + b of group G = 2n + a lies in sub-block 8n + 2j + a;
+// selector j, A row 4G + j.  B holds each 2-bit code left in place, at bits
+// 2j of its byte: q * 4^j * 2^-24.  Scale d * sc * 2^24 / 4^j; minimum
+// -dmin * m times the sub-block's activation sum.
+template <> struct T1<Q2_K> {
+  using Dd = DecQ2K;
+  using Raw = DecQ2K::Raw;
+  static constexpr bool HAS_MIN = true;
+  static constexpr int NSEL = 4;
+  __device__ static int sel_of_step(int s) { return s >> 1; }
+  __device__ static int arow(int c, int G) { return 4 * G + c; }
+  struct Sc { float f[4], g[4]; };
+  __device__ static Sc prep(const Raw &r, int G) {
+    const float d = lo_f16(r.dd), dmin = hi_f16(r.dd);
+    Sc s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 8 * (G >> 1) + 2 * j + (G & 1);
+      const uint32_t byte = (r.sc[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      s.f[j] = (d * (16777216.0f / (float)(1 << (2 * j)))) * (float)(byte & 15u);
+      s.g[j] = -dmin * (float)(byte >> 4);
+    }
+    return s;
+  }
+  __device__ static half8 bop(const Raw &r, const Sc &, int st) {
+    const int j = st >> 1, b = st & 1;
+    const uint32_t v0 = b ? r.q.z : r.q.x, v1 = b ? r.q.w : r.q.y;
+    const uint32_t m = 0x00030003u << (2 * j);
+    return pack8(v0 & m, (v0 >> 8) & m, v1 & m, (v1 >> 8) & m);
+  }
+  __device__ static float post(float acc, floatx4 D, floatx4 X, const Sc &s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc += s.f[q] * D[q] + s.g[q] * X[q];
+    return acc;
+  }
+};
+
+// Q3_K: as Q2_K, with v = q + 4 h (the high-mask bit; 0 .. 7) at bits 0-2 of
+// each half: v * 2^-24.  The weight is (v - 4)(sc - 32) d, so the scale is
+// d (sc - 32) 2^24 and the sub-block's activation sum enters times
+// -4 d (sc - 32).
+template <> struct T1<Q3_K> {
+  using Dd = DecQ3K;
+  using Raw = DecQ3K::Raw;
+  static constexpr bool HAS_MIN = true;
+  static constexpr int NSEL = 4;
+  __device__ static int sel_of_step(int s) { return s >> 1; }
+  __device__ static int arow(int c, int G) { return 4 * G + c; }
+  struct Sc { float f[4], g[4]; int hb; };  // hb = 4n: this group's high-mask bits
+  __device__ static Sc prep(const Raw &r, int G) {
+    const int n = G >> 1, a = G & 1;
+    const float d = lo_f16(r.d);
+    Sc s;
+    s.hb = 4 * n;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = 2 * j + a;  // scale index minus 8n
+      const uint32_t lb = (r.lo[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      const int low4 = (int)(n ? lb >> 4 : lb & 15u);
+      const int high2 = (int)((r.hi >> (8 * (k & 3) + 2 * (2 * n + (j >> 1)))) & 3u);
+      const float ds = d * (float)((low4 | (high2 << 4)) - 32);
+      s.f[j] = ds * 16777216.0f;
+      s.g[j] = -4.0f * ds;
+    }
+    return s;
+  }
+  __device__ static half8 bop(const Raw &r, const Sc &s, int st) {
+    const int j = st >> 1, b = st & 1;
+    const uint32_t v0 = (b ? r.q.z : r.q.x) >> (2 * j), v1 = (b ? r.q.w : r.q.y) >> (2 * j);
+    const int hs = s.hb + j;
+    const uint32_t h0 = (b ? r.hm.z : r.hm.x) >> hs, h1 = (b ? r.hm.w : r.hm.y) >> hs;
+    const uint32_t cm = 0x00030003u, hm = 0x00040004u;
+    return pack8(and_or(h0 << 2, hm, v0 & cm), and_or(h0 >> 6, hm, (v0 >> 8) & cm), and_or(h1 << 2, hm, v1 & cm),
+                 and_or(h1 >> 6, hm, (v1 >> 8) & cm));
+  }
+  __device__ static float post(float acc, floatx4 D, floatx4 X, const Sc &s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc += s.f[q] * D[q] + s.g[q] * X[q];
+    return acc;
+  }
+};
+
 // Step-scaled kinds: eight steps, eight A rows (row s for step s, whatever
 // the lane group), no minimum term.
 template <int KIND>
@@ -139,7 +256,7 @@ struct T1Step {
     }
     return o;
   }
-  __device__ static half8 bop(const Raw &r, int st) { return Dd::bop(r, typename Dd::Sc{}, st, 0); }
+  __device__ static half8 bop(const Raw &r, const Sc &, int st) { return Dd::bop(r, typename Dd::Sc{}, st, 0); }
   __device__ static float post(float acc, floatx4 D, floatx4, const Sc &s) {
     return acc + s.s[0] * D[0] + s.s[1] * D[1] + s.s[2] * D[2] + s.s[3] * D[3];
   }

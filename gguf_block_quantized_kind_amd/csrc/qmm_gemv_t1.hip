@@ -1,6 +1,7 @@
-// qmm_gemv_t1.hip -- the single-token decode GEMV for Q4_K and Q6_K, over
-// repacked records or native GGUF rows, and its routed form for expert
-// products of one pair per workgroup.
+// qmm_gemv_t1.hip -- the single-token decode GEMV: the super-block kinds
+// over repacked records or native GGUF rows, the step-scaled kinds over
+// records, and its routed form for expert products of one pair per
+// workgroup.
 //
 // Rows of A as sub-block selectors.  With one token, 15 of the 16 A rows of
 // v_mfma_f32_16x16x32_f16 would hold zeros.  Here, at each MFMA step, lane
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
     for (int st = 0; st < Dd::NSTEP; ++st) {
       const half8 a = __builtin_bit_cast(half8, abase[d][Tr::sel_of_step(st)][4 * st]);
       if constexpr (Tr::HAS_MIN) Xs = mfma16(a, ones, Xs);
-      D = mfma16(a, Tr::bop(fr, st), D);
+      D = mfma16(a, Tr::bop(fr, sc, st), D);
     }
     acc = Tr::post(acc, D, Xs, sc);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -235,7 +236,7 @@ static hipError_t run_t1_routed(const uint8_t *W, const void *x, int x_f16, floa
 // rows through the LDS staging of qmm_gemv_mfma.hip.
 bool gemv_t1_supported(int kind, bool packed) {
   switch (kind) {
-    case Q4_K: case Q6_K: return true;
+    case Q4_K: case Q6_K: case Q5_K: case Q2_K: case Q3_K: return true;
     case Q4_0: case Q5_0: case Q8_0: case IQ4_NL: case MXFP4: case IQ4_XS: return packed;
     default: return false;
   }
@@ -249,6 +250,12 @@ hipError_t launch_gemv_t1(int kind, const uint8_t *W, const void *x, int x_f16, 
                              : gv::run_t1_k<Q4_K, false>(W, x, x_f16, y, N, K, s, cfg);
     case Q6_K: return packed ? gv::run_t1_k<Q6_K, true>(W, x, x_f16, y, N, K, s, cfg)
                              : gv::run_t1_k<Q6_K, false>(W, x, x_f16, y, N, K, s, cfg);
+    case Q5_K: return packed ? gv::run_t1_k<Q5_K, true>(W, x, x_f16, y, N, K, s, cfg)
+                             : gv::run_t1_k<Q5_K, false>(W, x, x_f16, y, N, K, s, cfg);
+    case Q2_K: return packed ? gv::run_t1_k<Q2_K, true>(W, x, x_f16, y, N, K, s, cfg)
+                             : gv::run_t1_k<Q2_K, false>(W, x, x_f16, y, N, K, s, cfg);
+    case Q3_K: return packed ? gv::run_t1_k<Q3_K, true>(W, x, x_f16, y, N, K, s, cfg)
+                             : gv::run_t1_k<Q3_K, false>(W, x, x_f16, y, N, K, s, cfg);
 #define QMM_CASE(K_) \
   case K_: return gv::run_t1_k<K_, true>(W, x, x_f16, y, N, K, s, cfg);
     QMM_CASE(Q4_0) QMM_CASE(Q5_0) QMM_CASE(Q8_0) QMM_CASE(IQ4_NL) QMM_CASE(MXFP4) QMM_CASE(IQ4_XS)
@@ -266,6 +273,12 @@ hipError_t launch_moe_t1(int kind, const uint8_t *W, const void *X, int x_f16, f
                              : gv::run_t1_routed<Q4_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
     case Q6_K: return packed ? gv::run_t1_routed<Q6_K, true>(W, X, x_f16, Y, N, K, s, rt, items)
                              : gv::run_t1_routed<Q6_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
+    case Q5_K: return packed ? gv::run_t1_routed<Q5_K, true>(W, X, x_f16, Y, N, K, s, rt, items)
+                             : gv::run_t1_routed<Q5_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
+    case Q2_K: return packed ? gv::run_t1_routed<Q2_K, true>(W, X, x_f16, Y, N, K, s, rt, items)
+                             : gv::run_t1_routed<Q2_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
+    case Q3_K: return packed ? gv::run_t1_routed<Q3_K, true>(W, X, x_f16, Y, N, K, s, rt, items)
+                             : gv::run_t1_routed<Q3_K, false>(W, X, x_f16, Y, N, K, s, rt, items);
 #define QMM_CASE(K_) \
   case K_: return gv::run_t1_routed<K_, true>(W, X, x_f16, Y, N, K, s, rt, items);
     QMM_CASE(Q4_0) QMM_CASE(Q5_0) QMM_CASE(Q8_0) QMM_CASE(IQ4_NL) QMM_CASE(MXFP4) QMM_CASE(IQ4_XS)

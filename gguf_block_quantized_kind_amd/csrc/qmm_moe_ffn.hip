@@ -224,11 +224,11 @@ __device__ __forceinline__ void kblock(const typename Dec<KIND>::Raw (&fr)[R], c
   }
 }
 
-// Q4_K and Q6_K take the single-token decoders of qmm_gemv_t1.h: the A rows
-// select sub-blocks, the B operands carry no scales, and the scales are
-// applied to D once per k-block.
+// The super-block kinds take the single-token decoders of qmm_gemv_t1.h: the
+// A rows select sub-blocks, the B operands carry no scales, and the scales
+// are applied to D once per k-block.
 template <int KIND>
-constexpr bool kT1 = KIND == Q4_K || KIND == Q6_K;
+constexpr bool kT1 = KIND == Q4_K || KIND == Q6_K || KIND == Q5_K || KIND == Q2_K || KIND == Q3_K;
 // Selector groups of those decoders (1 for the other kinds: unused).
 template <int KIND, bool = kT1<KIND>>
 struct Nsel {
@@ -251,17 +251,21 @@ __device__ __forceinline__ void kblock_t1(const typename Dec<KIND>::Raw (&fr)[R]
   using Dd = Dec<KIND>;
   const half8 ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
   Fx4 xs = {0.f, 0.f, 0.f, 0.f}, D[R];
+  typename Tr::Sc sc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) D[r] = Fx4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < R; ++r) {
+    D[r] = Fx4{0.f, 0.f, 0.f, 0.f};
+    sc[r] = Tr::prep(fr[r], G);
+  }
 #pragma unroll
   for (int st = 0; st < Dd::NSTEP; ++st) {
     const half8 a = __builtin_bit_cast(half8, abase[Tr::sel_of_step(st)][4 * st]);
     if constexpr (Tr::HAS_MIN) xs = gv::mfma16(a, ones, xs);
 #pragma unroll
-    for (int r = 0; r < R; ++r) D[r] = gv::mfma16(a, Tr::bop(fr[r], st), D[r]);
+    for (int r = 0; r < R; ++r) D[r] = gv::mfma16(a, Tr::bop(fr[r], sc[r], st), D[r]);
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] += weight * Tr::post(0.f, D[r], xs, Tr::prep(fr[r], G));
+  for (int r = 0; r < R; ++r) acc[r] += weight * Tr::post(0.f, D[r], xs, sc[r]);
 }
 
 // Launch 1.  Workgroup (t, p): pair p's gate tile t and up tile t + n_ff/16

@@ -72,7 +72,7 @@ def test_ffn_parity(oracle_mod, kind, N_ff, K):
         check(got, y, tol, f"{kind} M={M}")
 
 
-@pytest.mark.parametrize("kind", ["Q4_K", "Q6_K"])
+@pytest.mark.parametrize("kind", ["Q4_K", "Q6_K", "Q5_K", "Q2_K", "Q3_K"])
 @pytest.mark.parametrize("packed", [False, True])
 def test_ffn_two_launches(oracle_mod, kind, packed):
     """The two-launch FFN (fewer than four pairs per expert, whole

@@ -509,6 +509,9 @@ hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16,
   // step-scaled kinds keep this file's kernel for routed pairs).
   if (mt == 1 && rt.ids != nullptr && items <= 65535 && gemv_t1_supported(kind, false))
     return launch_moe_t1(kind, W, X, x_f16, Y, N, K, rt, items, s, packed);
+  // Grouped items over repacked experts: activations staged once for eight
+  // tiles.
+  if (packed && (mt == 8 || mt == 16) && items <= 65535) return launch_moe_xs(kind, W, X, x_f16, Y, mt, N, K, rt, items, s);
   if (packed) {
     switch (kind) {
       case Q4_K: return gv::run_routed<Q4_K, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);

@@ -24,6 +24,8 @@
 // no later than that round.  Every load is issued on every path (past the
 // last k-block the last one is read again), so no wait is ever widened by a
 // branch.
+#include <stdlib.h>
+
 #include <algorithm>
 #include <atomic>
 
@@ -38,10 +40,16 @@ namespace gv {
 // still be in flight).
 constexpr int kWaitLds = 0xC07F;
 
-template <int KIND, typename XT, int MT, int T, int S, int PD, int XD>
+// ROUTED: workgroup (b, item) serves work item `item` of a grouped expert
+// product (up to MT pairs of one expert, as the routing prologue of
+// qmm_moe.hip cut them): the expert's records, the pairs' activation rows
+// (gathered through the pair order) as the tokens, outputs scattered to the
+// pairs' rows.
+template <int KIND, typename XT, int MT, int T, int S, int PD, int XD, bool ROUTED = false>
 __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__restrict__ P,
                                                              const XT *__restrict__ X, float *__restrict__ Y,
-                                                             int M, int64_t N, int K, int per_wg, int extra) {
+                                                             int M, int64_t N, int K, int per_wg, int extra,
+                                                             MoeRoute rt) {
   using Dd = Dec<KIND>;
   using X4 = typename XVec<XT>::type;
   constexpr int kFrag = Dd::NSTEP * MT * 4;  // 16-byte fragments per k-block (layout of qmm_gemv_mfma.hip)
@@ -58,10 +66,22 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 15, G = lane >> 4;
   const int t = wave % T, kp = wave / T;
+  int c0 = 0;
+  const int32_t *order = nullptr;
+  if constexpr (ROUTED) {
+    const int item = blockIdx.y;
+    if (item >= rt.ws[rt.nwork_at]) return;  // the whole workgroup leaves before any barrier
+    const int e = rt.ws[rt.work_at + 2 * item];
+    c0 = rt.ws[rt.work_at + 2 * item + 1];
+    order = rt.ws + rt.order_at;
+    M = min(MT, rt.ws[rt.offsets_at + e + 1] - c0);
+    P += (int64_t)e * ((N + 15) / 16) * (K / Dd::KB) * kRec;  // expert e's records
+  }
   // Workgroup b owns tiles [t0, t1): per_wg each, one more for the first
-  // `extra` workgroups.
+  // `extra` workgroups (never past the last tile).
   const int b = blockIdx.x;
-  const int t0 = b * per_wg + min(b, extra), t1 = t0 + per_wg + (b < extra ? 1 : 0);
+  const int t0 = b * per_wg + min(b, extra);
+  const int t1 = (int)min<int64_t>(t0 + per_wg + (b < extra ? 1 : 0), (N + 15) / 16);
   // A wave without a tile (t >= t1 - t0) stages its share of the activations
   // and loads the workgroup's last tile again (cache hits), but decodes and
   // stores nothing.
@@ -85,7 +105,12 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
     const int h = t * kShare + in, f = h >> 1;
     const int g2 = f & 3, tok = (f >> 2) % MT, st = (f >> 2) / MT;
     xlive[i] = in < kShare && tok < M;
-    xoff[i] = xlive[i] ? tok * K + Dd::x_off(st, g2, h & 1) : 0;
+    int64_t xrow = (int64_t)tok * K;
+    if constexpr (ROUTED) {
+      const int pair = xlive[i] ? order[c0 + tok] : 0;
+      xrow = (int64_t)(rt.x_per_slot ? pair : pair / rt.topk) * K;
+    }
+    xoff[i] = xlive[i] ? (int)(xrow + Dd::x_off(st, g2, h & 1)) : 0;
     xdst[i] = in < kShare ? h : -1;
   }
   const uint8_t *wt = P + tile * nkb * kRec;
@@ -195,7 +220,7 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int tok = 4 * G + q;
-    if (tok < M) Y[(int64_t)tok * N + row] = acc[q];
+    if (tok < M) Y[(int64_t)(ROUTED ? order[c0 + tok] : tok) * N + row] = acc[q];
   }
 }
 
@@ -226,11 +251,53 @@ static hipError_t run_xs(const uint8_t *P, const void *x, int x_f16, float *y, i
   const dim3 grid((unsigned)wgs), block(64 * T * S);
   if (x_f16)
     hipLaunchKernelGGL((gemv_xs_kernel<KIND, _Float16, MT, T, S, PD, XD>), grid, block, lds, s, P,
-                       (const _Float16 *)x, y, M, N, (int)K, per_wg, extra);
+                       (const _Float16 *)x, y, M, N, (int)K, per_wg, extra, MoeRoute{});
   else
     hipLaunchKernelGGL((gemv_xs_kernel<KIND, float, MT, T, S, PD, XD>), grid, block, lds, s, P, (const float *)x, y, M,
-                       N, (int)K, per_wg, extra);
+                       N, (int)K, per_wg, extra, MoeRoute{});
   return hipGetLastError();
+}
+
+// Grouped expert products: grid (tile groups of T, work items); T tiles
+// share each staged activation k-block of the item's MT pairs.
+template <int KIND, int MT, int T, int S, int PD, int XD>
+static hipError_t run_xs_routed(const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K,
+                                hipStream_t s, const MoeRoute &rt, int items) {
+  constexpr int kFrag = Dec<KIND>::NSTEP * MT * 4;
+  const size_t lds = std::max<size_t>((size_t)S * 2 * kFrag * 16 + 16, (size_t)(S - 1) * T * 64 * 16);
+  const int64_t ntiles = (N + 15) / 16;
+  const dim3 grid((unsigned)((ntiles + T - 1) / T), (unsigned)items), block(64 * T * S);
+  if (x_f16)
+    hipLaunchKernelGGL((gemv_xs_kernel<KIND, _Float16, MT, T, S, PD, XD, true>), grid, block, lds, s, P,
+                       (const _Float16 *)x, y, MT, N, (int)K, T, 0, rt);
+  else
+    hipLaunchKernelGGL((gemv_xs_kernel<KIND, float, MT, T, S, PD, XD, true>), grid, block, lds, s, P,
+                       (const float *)x, y, MT, N, (int)K, T, 0, rt);
+  return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t run_xs_routed_m(const uint8_t *P, const void *x, int x_f16, float *y, int mt, int64_t N, int64_t K,
+                                  hipStream_t s, const MoeRoute &rt, int items) {
+#ifdef QMM_TUNING
+  static const int cfg = [] {
+    const char *e = getenv("QMM_MOE_XS_CFG");
+    return e ? atoi(e) : 0;
+  }();
+  if (mt == 16) {
+    switch (cfg) {
+      case 1: return run_xs_routed<KIND, 16, 4, 1, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
+      case 2: return run_xs_routed<KIND, 16, 8, 1, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
+      case 3: return run_xs_routed<KIND, 16, 16, 1, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
+      case 4: return run_xs_routed<KIND, 16, 4, 2, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
+      case 5: return run_xs_routed<KIND, 16, 8, 2, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
+      case 6: return run_xs_routed<KIND, 16, 8, 1, 2, 1>(P, x, x_f16, y, N, K, s, rt, items);
+      default: break;
+    }
+  }
+#endif
+  if (mt == 8) return run_xs_routed<KIND, 8, 8, 1, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
+  return run_xs_routed<KIND, 16, 8, 1, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
 }
 
 template <int KIND>
@@ -269,6 +336,19 @@ static hipError_t run_xs_m(const uint8_t *P, const void *x, int x_f16, float *y,
 }
 
 }  // namespace gv
+
+hipError_t launch_moe_xs(int kind, const uint8_t *P, const void *X, int x_f16, float *Y, int mt, int64_t N,
+                         int64_t K, const MoeRoute &rt, int items, hipStream_t s) {
+  switch (kind) {
+#define QMM_CASE(K_) \
+  case K_: return gv::run_xs_routed_m<K_>(P, X, x_f16, Y, mt, N, K, s, rt, items);
+    QMM_CASE(Q4_K) QMM_CASE(Q6_K) QMM_CASE(IQ4_XS) QMM_CASE(Q4_0) QMM_CASE(Q5_0) QMM_CASE(Q8_0) QMM_CASE(IQ4_NL)
+    QMM_CASE(MXFP4) QMM_CASE(Q2_K) QMM_CASE(Q3_K) QMM_CASE(Q5_K)
+#undef QMM_CASE
+    default: break;
+  }
+  return hipErrorNotSupported;
+}
 
 hipError_t launch_gemv_xs(int kind, const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N,
                           int64_t K, hipStream_t s, int cfg) {

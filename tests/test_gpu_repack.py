@@ -193,10 +193,11 @@ def test_moe_packed_parity(oracle_mod, kind):
             assert_within_bound(got, Yr, Br, f"{kind} M={M} per_slot={per_slot}")
 
 
-@pytest.mark.parametrize("e", [x for x in wl.C5 if x.M in (1, 16)], ids=lambda e: e.name)
+@pytest.mark.parametrize("e", [x for x in wl.C5 if x.M in (1, 16, 256)], ids=lambda e: e.name)
 def test_moe_packed_full_size_sampled(oracle_mod, e):
-    """The expert workload's gate/up matrices (128 experts of 1536 x 2048
-    Q4_K), repacked, at 1 and 16 tokens, on sampled rows."""
+    """The expert workload's gate/up matrices, repacked, at 1, 16 and 256
+    tokens (one pair per work item, and items of sixteen pairs), on sampled
+    rows."""
     ids = e.ids()
     W = e.w_gu()
     X = e.x()

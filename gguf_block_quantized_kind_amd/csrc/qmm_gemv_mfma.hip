@@ -509,9 +509,10 @@ hipError_t launch_moe_mfma(int kind, const uint8_t *W, const void *X, int x_f16,
   // step-scaled kinds keep this file's kernel for routed pairs).
   if (mt == 1 && rt.ids != nullptr && items <= 65535 && gemv_t1_supported(kind, false))
     return launch_moe_t1(kind, W, X, x_f16, Y, N, K, rt, items, s, packed);
-  // Grouped items over repacked experts: activations staged once for eight
-  // tiles.
-  if (packed && (mt == 8 || mt == 16) && items <= 65535) return launch_moe_xs(kind, W, X, x_f16, Y, mt, N, K, rt, items, s);
+  // Grouped items: activations staged once for eight tiles (repacked
+  // experts, or native rows of the super-block kinds).
+  if ((mt == 8 || mt == 16) && items <= 65535 && (packed || xs_native_supported(kind)))
+    return launch_moe_xs(kind, W, X, x_f16, Y, mt, N, K, rt, items, s, packed);
   if (packed) {
     switch (kind) {
       case Q4_K: return gv::run_routed<Q4_K, true>(W, X, x_f16, Y, mt, N, K, s, rt, items);
@@ -561,9 +562,12 @@ hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16
 #else
   constexpr int cfg = 0;
 #endif
-  // One token, a super-block kind: the single-token decoders.
+  // One token, a super-block kind: the single-token decoders; two to eight
+  // tokens: the staged-activation kernel.
   if (M == 1 && gemv_t1_supported(kind, false) && (cfg == 0 || cfg >= 200))
     return launch_gemv_t1(kind, W, x, x_f16, y, N, K, s, cfg, false);
+  if (M > 1 && xs_native_supported(kind) && (cfg == 0 || cfg >= 100))
+    return launch_gemv_xs_native(kind, W, x, x_f16, y, M, N, K, s);
   switch (kind) {
     case Q4_K: return gv::run_m<Q4_K>(W, x, x_f16, y, M, N, K, s, cfg);
     case Q6_K: return gv::run_m<Q6_K>(W, x, x_f16, y, M, N, K, s, cfg);

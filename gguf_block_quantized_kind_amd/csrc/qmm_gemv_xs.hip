@@ -28,6 +28,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "qmm_gemv_mfma.h"
 #include "qmm_internal.h"
@@ -45,11 +46,14 @@ constexpr int kWaitLds = 0xC07F;
 // qmm_moe.hip cut them): the expert's records, the pairs' activation rows
 // (gathered through the pair order) as the tokens, outputs scattered to the
 // pairs' rows.
-template <int KIND, typename XT, int MT, int T, int S, int PD, int XD, bool ROUTED = false>
+// PACKED false: P holds native GGUF rows of row_bytes bytes (decoders that
+// load their fields straight from global memory only, not the LDS-staged
+// ones).
+template <int KIND, typename XT, int MT, int T, int S, int PD, int XD, bool ROUTED = false, bool PACKED = true>
 __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__restrict__ P,
                                                              const XT *__restrict__ X, float *__restrict__ Y,
                                                              int M, int64_t N, int K, int per_wg, int extra,
-                                                             MoeRoute rt) {
+                                                             MoeRoute rt, int64_t row_bytes) {
   using Dd = Dec<KIND>;
   using X4 = typename XVec<XT>::type;
   constexpr int kFrag = Dd::NSTEP * MT * 4;  // 16-byte fragments per k-block (layout of qmm_gemv_mfma.hip)
@@ -61,6 +65,7 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
   static_assert(XD == 1 || XD == 2, "activation distance");
   constexpr int U = NS % 2 == 0 ? NS : 2 * NS;  // rounds per unrolled turn: every slot index static
   constexpr int64_t kRec = 16 * Dd::BYTES;   // one repacked record
+  static_assert(PACKED || !Dd::CHUNKED, "native rows: decoders with direct field loads only");
   extern __shared__ u32x4 lds[];  // S rings of 2 k-blocks of fragments, one zero fragment; later the reduction
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
     c0 = rt.ws[rt.work_at + 2 * item + 1];
     order = rt.ws + rt.order_at;
     M = min(MT, rt.ws[rt.offsets_at + e + 1] - c0);
-    P += (int64_t)e * ((N + 15) / 16) * (K / Dd::KB) * kRec;  // expert e's records
+    P += (int64_t)e * (PACKED ? ((N + 15) / 16) * (K / Dd::KB) * kRec : N * row_bytes);  // expert e's weights
   }
   // Workgroup b owns tiles [t0, t1): per_wg each, one more for the first
   // `extra` workgroups (never past the last tile).
@@ -113,10 +118,16 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
     xoff[i] = xlive[i] ? (int)(xrow + Dd::x_off(st, g2, h & 1)) : 0;
     xdst[i] = in < kShare ? h : -1;
   }
-  const uint8_t *wt = P + tile * nkb * kRec;
-  typename Rec<KIND>::Packed raw[NS];
+  // This tile's records, or row j of it (rows past N decode the last row;
+  // their outputs are not stored).
+  const uint8_t *wt = PACKED ? P + tile * nkb * kRec : P + min<int64_t>(tile * 16 + j, N - 1) * row_bytes;
+  typename std::conditional<PACKED, typename Rec<KIND>::Packed, typename Dd::Raw>::type raw[NS];
   X4 xv[XD][kPerLane];  // activation shares of the next XD k-blocks
-  auto issue_w = [&](int kb, int slot) { Rec<KIND>::load(wt + min(kb, kb_last) * kRec, lane, j, G, raw[slot]); };
+  auto issue_w = [&](int kb, int slot) {
+    kb = min(kb, kb_last);
+    if constexpr (PACKED) Rec<KIND>::load(wt + kb * kRec, lane, j, G, raw[slot]);
+    else Dd::load(wt + (int64_t)kb * Dd::BYTES, G, raw[slot]);
+  };
   auto issue_x = [&](int kb, int slot) {
     kb = min(kb, kb_last);
 #pragma unroll
@@ -147,7 +158,9 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (r >= cnt || !owner) return;  // this k-part has no k-block in this round, or the wave no tile
-    const typename Dd::Raw fr = Rec<KIND>::unpack(raw[d], G);
+    typename Dd::Raw fr;
+    if constexpr (PACKED) fr = Rec<KIND>::unpack(raw[d], G);
+    else fr = raw[d];
     const typename Dd::Sc sc = Dd::prep(fr, G);
     const u32x4 *xr = j < MT ? xk + j * 4 + G : zero;
     floatx4 xsum = {0.f, 0.f, 0.f, 0.f};
@@ -240,9 +253,10 @@ int device_cus() {
 
 namespace gv {
 
-template <int KIND, int MT, int T, int S, int PD, int XD = 2>
+template <int KIND, int MT, int T, int S, int PD, int XD = 2, bool PACKED = true>
 static hipError_t run_xs(const uint8_t *P, const void *x, int x_f16, float *y, int M, int64_t N, int64_t K,
                          hipStream_t s, bool spread = true) {
+  const int64_t row_bytes = (K / Geometry<KIND>::elems) * Geometry<KIND>::bytes;
   constexpr int kFrag = Dec<KIND>::NSTEP * MT * 4;
   const size_t lds = std::max<size_t>((size_t)S * 2 * kFrag * 16 + 16, (size_t)(S - 1) * T * 64 * 16);
   const int64_t ntiles = (N + 15) / 16;
@@ -250,33 +264,34 @@ static hipError_t run_xs(const uint8_t *P, const void *x, int x_f16, float *y, i
   const int per_wg = (int)(ntiles / wgs), extra = (int)(ntiles % wgs);
   const dim3 grid((unsigned)wgs), block(64 * T * S);
   if (x_f16)
-    hipLaunchKernelGGL((gemv_xs_kernel<KIND, _Float16, MT, T, S, PD, XD>), grid, block, lds, s, P,
-                       (const _Float16 *)x, y, M, N, (int)K, per_wg, extra, MoeRoute{});
+    hipLaunchKernelGGL((gemv_xs_kernel<KIND, _Float16, MT, T, S, PD, XD, false, PACKED>), grid, block, lds, s, P,
+                       (const _Float16 *)x, y, M, N, (int)K, per_wg, extra, MoeRoute{}, row_bytes);
   else
-    hipLaunchKernelGGL((gemv_xs_kernel<KIND, float, MT, T, S, PD, XD>), grid, block, lds, s, P, (const float *)x, y, M,
-                       N, (int)K, per_wg, extra, MoeRoute{});
+    hipLaunchKernelGGL((gemv_xs_kernel<KIND, float, MT, T, S, PD, XD, false, PACKED>), grid, block, lds, s, P,
+                       (const float *)x, y, M, N, (int)K, per_wg, extra, MoeRoute{}, row_bytes);
   return hipGetLastError();
 }
 
 // Grouped expert products: grid (tile groups of T, work items); T tiles
 // share each staged activation k-block of the item's MT pairs.
-template <int KIND, int MT, int T, int S, int PD, int XD>
+template <int KIND, int MT, int T, int S, int PD, int XD, bool PACKED = true>
 static hipError_t run_xs_routed(const uint8_t *P, const void *x, int x_f16, float *y, int64_t N, int64_t K,
                                 hipStream_t s, const MoeRoute &rt, int items) {
   constexpr int kFrag = Dec<KIND>::NSTEP * MT * 4;
+  const int64_t row_bytes = (K / Geometry<KIND>::elems) * Geometry<KIND>::bytes;
   const size_t lds = std::max<size_t>((size_t)S * 2 * kFrag * 16 + 16, (size_t)(S - 1) * T * 64 * 16);
   const int64_t ntiles = (N + 15) / 16;
   const dim3 grid((unsigned)((ntiles + T - 1) / T), (unsigned)items), block(64 * T * S);
   if (x_f16)
-    hipLaunchKernelGGL((gemv_xs_kernel<KIND, _Float16, MT, T, S, PD, XD, true>), grid, block, lds, s, P,
-                       (const _Float16 *)x, y, MT, N, (int)K, T, 0, rt);
+    hipLaunchKernelGGL((gemv_xs_kernel<KIND, _Float16, MT, T, S, PD, XD, true, PACKED>), grid, block, lds, s, P,
+                       (const _Float16 *)x, y, MT, N, (int)K, T, 0, rt, row_bytes);
   else
-    hipLaunchKernelGGL((gemv_xs_kernel<KIND, float, MT, T, S, PD, XD, true>), grid, block, lds, s, P,
-                       (const float *)x, y, MT, N, (int)K, T, 0, rt);
+    hipLaunchKernelGGL((gemv_xs_kernel<KIND, float, MT, T, S, PD, XD, true, PACKED>), grid, block, lds, s, P,
+                       (const float *)x, y, MT, N, (int)K, T, 0, rt, row_bytes);
   return hipGetLastError();
 }
 
-template <int KIND>
+template <int KIND, bool PACKED>
 static hipError_t run_xs_routed_m(const uint8_t *P, const void *x, int x_f16, float *y, int mt, int64_t N, int64_t K,
                                   hipStream_t s, const MoeRoute &rt, int items) {
 #ifdef QMM_TUNING
@@ -286,18 +301,18 @@ static hipError_t run_xs_routed_m(const uint8_t *P, const void *x, int x_f16, fl
   }();
   if (mt == 16) {
     switch (cfg) {
-      case 1: return run_xs_routed<KIND, 16, 4, 1, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
-      case 2: return run_xs_routed<KIND, 16, 8, 1, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
-      case 3: return run_xs_routed<KIND, 16, 16, 1, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
-      case 4: return run_xs_routed<KIND, 16, 4, 2, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
-      case 5: return run_xs_routed<KIND, 16, 8, 2, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
-      case 6: return run_xs_routed<KIND, 16, 8, 1, 2, 1>(P, x, x_f16, y, N, K, s, rt, items);
+      case 1: return run_xs_routed<KIND, 16, 4, 1, 1, 1, PACKED>(P, x, x_f16, y, N, K, s, rt, items);
+      case 3: return run_xs_routed<KIND, 16, 16, 1, 1, 1, PACKED>(P, x, x_f16, y, N, K, s, rt, items);
+      case 6: return run_xs_routed<KIND, 16, 8, 1, 2, 1, PACKED>(P, x, x_f16, y, N, K, s, rt, items);
       default: break;
     }
   }
 #endif
-  if (mt == 8) return run_xs_routed<KIND, 8, 8, 1, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
-  return run_xs_routed<KIND, 16, 8, 1, 1, 1>(P, x, x_f16, y, N, K, s, rt, items);
+  // Eight tiles per workgroup, one k-block of weights in flight (measured
+  // best among 4, 8 and 16 tiles, with K split in one or two parts, at the
+  // 128-expert top-8 workload with 256 tokens).
+  if (mt == 8) return run_xs_routed<KIND, 8, 8, 1, 1, 1, PACKED>(P, x, x_f16, y, N, K, s, rt, items);
+  return run_xs_routed<KIND, 16, 8, 1, 1, 1, PACKED>(P, x, x_f16, y, N, K, s, rt, items);
 }
 
 template <int KIND>
@@ -337,13 +352,42 @@ static hipError_t run_xs_m(const uint8_t *P, const void *x, int x_f16, float *y,
 
 }  // namespace gv
 
+bool xs_native_supported(int kind) {
+  return kind == Q4_K || kind == Q6_K || kind == Q5_K || kind == Q2_K || kind == Q3_K;
+}
+
 hipError_t launch_moe_xs(int kind, const uint8_t *P, const void *X, int x_f16, float *Y, int mt, int64_t N,
-                         int64_t K, const MoeRoute &rt, int items, hipStream_t s) {
+                         int64_t K, const MoeRoute &rt, int items, hipStream_t s, bool packed) {
+  if (!packed) {
+    switch (kind) {
+#define QMM_CASE(K_) \
+  case K_: return gv::run_xs_routed_m<K_, false>(P, X, x_f16, Y, mt, N, K, s, rt, items);
+      QMM_CASE(Q4_K) QMM_CASE(Q6_K) QMM_CASE(Q2_K) QMM_CASE(Q3_K) QMM_CASE(Q5_K)
+#undef QMM_CASE
+      default: return hipErrorNotSupported;
+    }
+  }
   switch (kind) {
 #define QMM_CASE(K_) \
-  case K_: return gv::run_xs_routed_m<K_>(P, X, x_f16, Y, mt, N, K, s, rt, items);
+  case K_: return gv::run_xs_routed_m<K_, true>(P, X, x_f16, Y, mt, N, K, s, rt, items);
     QMM_CASE(Q4_K) QMM_CASE(Q6_K) QMM_CASE(IQ4_XS) QMM_CASE(Q4_0) QMM_CASE(Q5_0) QMM_CASE(Q8_0) QMM_CASE(IQ4_NL)
     QMM_CASE(MXFP4) QMM_CASE(Q2_K) QMM_CASE(Q3_K) QMM_CASE(Q5_K)
+#undef QMM_CASE
+    default: break;
+  }
+  return hipErrorNotSupported;
+}
+
+// 2 to 8 tokens over native rows (the super-block kinds).
+hipError_t launch_gemv_xs_native(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int M, int64_t N,
+                                 int64_t K, hipStream_t s) {
+  switch (kind) {
+#define QMM_CASE(K_)                                                                         \
+  case K_:                                                                                   \
+    if (M <= 2) return gv::run_xs<K_, 2, 4, 2, 1, 1, false>(W, x, x_f16, y, M, N, K, s);     \
+    if (M <= 4) return gv::run_xs<K_, 4, 4, 2, 1, 1, false>(W, x, x_f16, y, M, N, K, s);     \
+    return gv::run_xs<K_, 8, 4, 2, 1, 1, false>(W, x, x_f16, y, M, N, K, s);
+    QMM_CASE(Q4_K) QMM_CASE(Q6_K) QMM_CASE(Q2_K) QMM_CASE(Q3_K) QMM_CASE(Q5_K)
 #undef QMM_CASE
     default: break;
   }

@@ -119,11 +119,18 @@ struct MoeRoute {
 // The matrix-core expert kernel: one workgroup per (work item, 16-row
 // tile); a work item is up to `mt` (1, 8 or 16) pairs of one expert.
 bool moe_mfma_supported(int kind, int64_t K);
-// Grouped expert products (work items of mt = 8 or 16 pairs of one expert)
-// over repacked experts, with each activation k-block staged once per
-// workgroup for several tiles (qmm_gemv_xs.hip).
+// Grouped expert products (work items of mt = 8 or 16 pairs of one expert),
+// with each activation k-block staged once per workgroup for several tiles
+// (qmm_gemv_xs.hip); repacked experts, or native rows of the kinds
+// xs_native_supported names.
 hipError_t launch_moe_xs(int kind, const uint8_t *P, const void *X, int x_f16, float *Y, int mt, int64_t N,
-                         int64_t K, const MoeRoute &rt, int items, hipStream_t s);
+                         int64_t K, const MoeRoute &rt, int items, hipStream_t s, bool packed);
+// Kinds whose staged-activation kernels also read native rows (decoders that
+// load their fields straight from global memory), and its 2-to-8-token GEMV
+// over native rows.
+bool xs_native_supported(int kind);
+hipError_t launch_gemv_xs_native(int kind, const uint8_t *W, const void *x, int x_f16, float *y, int M, int64_t N,
+                                 int64_t K, hipStream_t s);
 // The routed single-token form of launch_gemv_t1: one pair per workgroup,
 // the pair's expert read from rt.ids (MoeRoute below).
 hipError_t launch_moe_t1(int kind, const uint8_t *W, const void *X, int x_f16, float *Y, int64_t N, int64_t K,

@@ -589,7 +589,7 @@ hipError_t launch_moe_ffn(int kind, const uint8_t *W_gu, const uint8_t *W_d, int
   const int64_t P = M * topk;
   // Two launches: about one pair per expert (the routed products would not
   // group), a matrix-core decoder over this layout, whole k-blocks.
-  const bool fused_kind = packed ? packed_supported(kind) : (kind == Q4_K || kind == Q6_K);
+  const bool fused_kind = packed ? packed_supported(kind) : xs_native_supported(kind);
   if (fused_kind && P < 4 * E && N_ff % 256 == 0 && K % 256 == 0 && topk <= 64 && M * K < ((int64_t)1 << 31) &&
       P * N_ff < ((int64_t)1 << 31)) {
     switch (kind) {
@@ -599,6 +599,9 @@ hipError_t launch_moe_ffn(int kind, const uint8_t *W_gu, const uint8_t *W_d, int
                   : fz::run_fused<K_, false>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
       QMM_FUSED(Q4_K)
       QMM_FUSED(Q6_K)
+      QMM_FUSED(Q5_K)
+      QMM_FUSED(Q2_K)
+      QMM_FUSED(Q3_K)
 #undef QMM_FUSED
       case Q4_0: return fz::run_fused<Q4_0, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
       case Q5_0: return fz::run_fused<Q5_0, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
@@ -609,9 +612,6 @@ hipError_t launch_moe_ffn(int kind, const uint8_t *W_gu, const uint8_t *W_d, int
         return fz::run_fused<IQ4_XS, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
       case MXFP4:
         return fz::run_fused<MXFP4, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
-      case Q2_K: return fz::run_fused<Q2_K, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
-      case Q3_K: return fz::run_fused<Q3_K, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
-      case Q5_K: return fz::run_fused<Q5_K, true>(W_gu, W_d, E, ids, topk_w, topk, X, x_f16, Y, M, N_ff, K, H, G, s);
       default: break;
     }
   }

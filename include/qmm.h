@@ -143,8 +143,9 @@ int qmm_matmul(int kind, const void *W, const void *A, int a_dtype, float *C,
  * bits).  With fewer than four pairs per expert on average (M * topk < 4 E),
  * whole k-blocks (N_ff, K multiples of 256), topk <= 64 and a kind with a
  * matrix-core decoder over the layout given (repacked: as qmm_gemv_packed;
- * native: Q4_K, Q6_K), the FFN runs in two launches: gate/up with the
- * SiLU-product in its epilogue, then down with the combine in its epilogue.
+ * native: Q2_K, Q3_K, Q4_K, Q5_K, Q6_K), the FFN runs in two launches:
+ * gate/up with the SiLU-product in its epilogue, then down with the combine
+ * in its epilogue.
  * workspace: qmm_moe_ffn_workspace_bytes(E, M, topk, N_ff, K) bytes,
  * 256-byte aligned, overwritten; calls sharing it must not overlap.  Errors as qmm_moe, with both matrices' shapes checked (gate/up
  * first) and a NULL topk_w or misaligned Y as QMM_ERR_BAD_ARG. */

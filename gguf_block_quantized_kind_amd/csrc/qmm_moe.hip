@@ -53,25 +53,48 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
   }
   __syncthreads();
   // Exclusive scans of the pair counts and of the item counts: each thread
-  // sums its experts, a Hillis-Steele scan runs over the 1024 partial sums,
-  // then each thread writes its experts' offsets.
+  // sums its experts; an inclusive scan runs within each wave (lane
+  // shuffles), the 16 wave totals are scanned by one wave, and each thread
+  // then writes its experts' offsets.
   const int per = (E + 1023) / 1024, e0 = tid * per, e1 = min(E, e0 + per);
   int sp = 0, si = 0;
   for (int e = e0; e < e1; ++e) {
     sp += cnt[e];
     si += (cnt[e] + mt - 1) / mt;
   }
-  scan_p[tid] = sp;
-  scan_i[tid] = si;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int ap = tid >= off ? scan_p[tid - off] : 0, ai = tid >= off ? scan_i[tid - off] : 0;
-    __syncthreads();
-    scan_p[tid] += ap;
-    scan_i[tid] += ai;
-    __syncthreads();
+  const int lane = tid & 63, wv = tid >> 6;
+  int ip = sp, ii = si;  // inclusive within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ap = __shfl_up(ip, off, 64), ai = __shfl_up(ii, off, 64);
+    if (lane >= off) {
+      ip += ap;
+      ii += ai;
+    }
   }
-  int run = scan_p[tid] - sp, items = scan_i[tid] - si;  // exclusive prefix of this thread's experts
+  if (lane == 63) {
+    scan_p[wv] = ip;
+    scan_i[wv] = ii;
+  }
+  __syncthreads();
+  if (wv == 0) {  // inclusive scan of the 16 wave totals
+    int tp = lane < 16 ? scan_p[lane] : 0, ti = lane < 16 ? scan_i[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int ap = __shfl_up(tp, off, 64), ai = __shfl_up(ti, off, 64);
+      if (lane >= off) {
+        tp += ap;
+        ti += ai;
+      }
+    }
+    if (lane < 16) {
+      scan_p[64 + lane] = tp;
+      scan_i[64 + lane] = ti;
+    }
+  }
+  __syncthreads();
+  const int bp = wv > 0 ? scan_p[64 + wv - 1] : 0, bi = wv > 0 ? scan_i[64 + wv - 1] : 0;
+  int run = bp + ip - sp, items = bi + ii - si;  // exclusive prefix of this thread's experts
   for (int e = e0; e < e1; ++e) {
     offsets[e] = run;
     cur[e] = run;
@@ -81,8 +104,8 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t *__restri
     items += (cnt[e] + mt - 1) / mt;
   }
   if (tid == 1023) {
-    offsets[E] = scan_p[1023];
-    ws[L.nwork()] = scan_i[1023];
+    offsets[E] = bp + ip;
+    ws[L.nwork()] = bi + ii;
   }
   __syncthreads();
   for (int64_t p = tid; p < pairs; p += blockDim.x) {

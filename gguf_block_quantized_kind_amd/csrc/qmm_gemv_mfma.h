@@ -605,6 +605,44 @@ struct DecQ3K {
   __device__ static floatx4 post(floatx4 acc, const floatx4 *D, floatx4, const Sc &s) { return acc + s.d * D[0]; }
 };
 
+// A CHUNKED decoder's k-block of one row as 16-byte chunks: lane (j, G)
+// loads chunks G, G+4, ... of row j (past the last chunk it re-reads it),
+// then stores them into a wave-private LDS copy of the row, from which the
+// decoder's load() reads its fields at their natural alignment.
+template <typename Dd>
+struct Chunks {
+  static constexpr int C = (Dd::BYTES + 15) / 16;  // chunks per row (the last may overlap)
+  static constexpr int L = (C + 3) / 4;            // chunks per lane
+  static constexpr int RS = 16 * C;                // staging bytes per row
+  struct Held { u32x4 c[L]; };
+  __device__ static int offset(int c) { return c < C - 1 ? 16 * c : Dd::BYTES - 16; }
+  __device__ static void load(const uint8_t *blk, int G, Held &h) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) h.c[i] = ld16(blk + offset(min(4 * i + G, C - 1)));
+  }
+  __device__ static void stage(uint8_t *row, const Held &h, int G) {
+    constexpr int rem = Dd::BYTES - 16 * (C - 1);  // new bytes in the last chunk
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int c = 4 * i + G;
+      if (c >= C) continue;
+      const u32x4 v = h.c[i];
+      if constexpr (rem == 16) {
+        *reinterpret_cast<u32x4 *>(row + 16 * c) = v;
+      } else {
+        if (c < C - 1) {
+          *reinterpret_cast<u32x4 *>(row + 16 * c) = v;
+        } else if constexpr (rem == 8) {  // the last chunk overlaps: store its new bytes
+          *reinterpret_cast<u32x2 *>(row + 16 * c) = u32x2{v[2], v[3]};
+        } else {
+          static_assert(rem == 2, "last chunk layout");
+          *reinterpret_cast<uint16_t *>(row + 16 * c) = (uint16_t)(v[3] >> 16);
+        }
+      }
+    }
+  }
+};
+
 template <int KIND> struct Dec;
 template <> struct Dec<Q4_K> : DecQ4K {};
 template <> struct Dec<Q6_K> : DecQ6K {};

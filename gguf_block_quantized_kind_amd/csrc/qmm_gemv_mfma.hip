@@ -39,15 +39,7 @@ struct XSlice {
 
 // Weight bytes a lane holds for one tile and k-block between issue and
 // decode: the decoder's own fields, or (CHUNKED decoders) its share of the
-// k-block as 16-byte chunks -- lane (j, G) holds chunks G, G+4, ... of row j.
-template <typename Dd>
-struct Chunks {
-  static constexpr int C = (Dd::BYTES + 15) / 16;  // chunks per row (the last may overlap)
-  static constexpr int L = (C + 3) / 4;            // chunks per lane
-  static constexpr int RS = 16 * C;                // staging bytes per row
-  struct Held { u32x4 c[L]; };
-  __device__ static int offset(int c) { return c < C - 1 ? 16 * c : Dd::BYTES - 16; }
-};
+// k-block as 16-byte chunks (Chunks in qmm_gemv_mfma.h).
 template <int KIND, bool PACKED, typename Dd>
 struct HeldOf {  // native rows (kinds without repacked records stop here)
   using type = typename std::conditional<Dd::CHUNKED, typename Chunks<Dd>::Held, typename Dd::Raw>::type;
@@ -168,9 +160,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
       if constexpr (PACKED) {
         Rec<KIND>::load(wr[r] + kb * kRec, lane, j, G, raw[slot][r]);
       } else if constexpr (Dd::CHUNKED) {
-#pragma unroll
-        for (int i = 0; i < CK::L; ++i)  // past the last chunk: a harmless re-read of it
-          raw[slot][r].c[i] = ld16(wr[r] + (int64_t)kb * Dd::BYTES + CK::offset(min(4 * i + G, CK::C - 1)));
+        CK::load(wr[r] + (int64_t)kb * Dd::BYTES, G, raw[slot][r]);
       } else {
         Dd::load(wr[r] + (int64_t)kb * Dd::BYTES, G, raw[slot][r]);
       }
@@ -218,25 +208,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
       } else if constexpr (Dd::CHUNKED) {
         // Stage the tile's k-block in LDS, then read the decoder's fields.
         uint8_t *row = stage + j * CK::RS;
-        constexpr int rem = Dd::BYTES - 16 * (CK::C - 1);  // new bytes in the last chunk
-#pragma unroll
-        for (int i = 0; i < CK::L; ++i) {
-          const int c = 4 * i + G;
-          if (c >= CK::C) continue;
-          const u32x4 v = raw[d][r].c[i];
-          if constexpr (rem == 16) {
-            *reinterpret_cast<u32x4 *>(row + 16 * c) = v;
-          } else {
-            if (c < CK::C - 1) {
-              *reinterpret_cast<u32x4 *>(row + 16 * c) = v;
-            } else if constexpr (rem == 8) {  // the last chunk overlaps: store its new bytes
-              *reinterpret_cast<u32x2 *>(row + 16 * c) = u32x2{v[2], v[3]};
-            } else {
-              static_assert(rem == 2, "last chunk layout");
-              *reinterpret_cast<uint16_t *>(row + 16 * c) = (uint16_t)(v[3] >> 16);
-            }
-          }
-        }
+        CK::stage(row, raw[d][r], G);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -562,9 +534,9 @@ hipError_t launch_gemv_mfma(int kind, const uint8_t *W, const void *x, int x_f16
 #else
   constexpr int cfg = 0;
 #endif
-  // One token, a super-block kind: the single-token decoders; two to eight
-  // tokens: the staged-activation kernel.
-  if (M == 1 && gemv_t1_supported(kind, false) && (cfg == 0 || cfg >= 200))
+  // One token: the single-token decoders; two to eight tokens of a
+  // super-block kind: the staged-activation kernel.
+  if (M == 1 && K % 256 == 0 && gemv_t1_supported(kind, false) && (cfg == 0 || cfg >= 200))
     return launch_gemv_t1(kind, W, x, x_f16, y, N, K, s, cfg, false);
   if (M > 1 && xs_native_supported(kind) && (cfg == 0 || cfg >= 100))
     return launch_gemv_xs_native(kind, W, x, x_f16, y, M, N, K, s);

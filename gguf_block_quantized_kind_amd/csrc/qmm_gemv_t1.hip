@@ -58,6 +58,7 @@ __global__ __launch_bounds__(64 * S) __attribute__((amdgpu_waves_per_eu(OCC, 8))
   using Dd = typename Tr::Dd;
   using Raw = typename Tr::Raw;
   using X4 = typename XVec<XT>::type;
+  static_assert(PACKED || !Dd::CHUNKED, "native rows: decoders with direct field loads only");
   using Held = typename std::conditional<PACKED, typename Rec<KIND>::Packed, Raw>::type;
   constexpr int kFrag = Dd::NSTEP * 4;  // 16-byte fragments of one k-block (step s, group G at 4s + G)
   constexpr int NS = PD + 1;
@@ -232,8 +233,10 @@ static hipError_t run_t1_routed(const uint8_t *W, const void *x, int x_f16, floa
 
 }  // namespace gv
 
-// Over native rows only the folded kinds: the step-scaled kinds read native
-// rows through the LDS staging of qmm_gemv_mfma.hip.
+// Over native rows only the super-block kinds: the step-scaled kinds read
+// native rows through an LDS staging (the matrix-core GEMV's), with which
+// this kernel measured no faster (Q4_0, IQ4_NL, IQ4_XS) or slower (MXFP4
+// 15.4 -> 17.3 us at 11008 x 4096).
 bool gemv_t1_supported(int kind, bool packed) {
   switch (kind) {
     case Q4_K: case Q6_K: case Q5_K: case Q2_K: case Q3_K: return true;

@@ -292,11 +292,13 @@ def test_matmul_dispatch_and_determinism(oracle_mod):
 # ---------------------------------------------------------------------------
 # Routed experts
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("kind", ["Q4_K", "Q8_0", "MXFP4", "Q6_K", "IQ4_XS", "Q5_0", "Q5_K"])
+@pytest.mark.parametrize("kind", ["Q4_K", "Q8_0", "MXFP4", "Q6_K", "IQ4_XS", "Q5_0", "Q5_K", "Q2_K", "Q3_K"])
 def test_moe_parity(oracle_mod, kind):
-    """Both expert kernels: K=1280 reaches the matrix-core one for every kind
-    that has a decoder (M=40: items of 16 pairs; M=9: 8 pairs; M=2, 5: one
-    pair), K=1312 and Q5_K the f32 one."""
+    """The expert kernels on native rows: with whole 256-element k-blocks
+    (K=1280) every kind takes a matrix-core form (M=40: items of 16 pairs;
+    M=9: items of up to 8; M=2, 5: one pair per item -- the single-token and
+    staged-activation kernels for the super-block kinds), and K=1312 (the
+    32-element kinds only) the f32 one."""
     E, N, topk = 6, 130, 3
     for K in gemv_Ks(kind):
         for M in (5, 2, 9, 40):

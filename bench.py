@@ -288,9 +288,8 @@ def secondary_cases(torch, qmm, wl, layout: str = "packed"):
 
                 cases.append(Case(w.name + ("_packed" if layout == "packed" else ""), w.kind, launch, copies,
                                   w.weight_bytes, w.flops))
-    # The codebook prefill workloads over repacked records (the 32-element
-    # kinds the packed GEMM takes).
-    for w in [w for w in wl.C4 if w.M > 8 and w.kind in ("IQ4_NL", "MXFP4")]:
+    # The codebook prefill workloads over repacked records.
+    for w in [w for w in wl.C4 if w.M > 8 and w.kind in ("IQ4_NL", "IQ4_XS", "MXFP4")]:
         copies = packed_copies(torch, qmm, w)
         x = torch.from_numpy(w.x()).cuda()
         y = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")

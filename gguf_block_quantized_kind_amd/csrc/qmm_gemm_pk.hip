@@ -70,6 +70,7 @@ __device__ __forceinline__ u32x2 ld_b64(__amdgpu_buffer_rsrc_t r, int voff, int 
 // lane group G's elements 8G .. 8G+7 of it.
 template <int TN> struct Rows<Q8_0, TN> {
   static constexpr int kRec = 16 * 272;
+  static constexpr bool kPostScale = false;
   static constexpr int kParts = 1, kPartElems = 8;
   static __device__ __forceinline__ int a_part(int u, int h, int G, int) { return 64 * u + 32 * h + 8 * G; }
   static constexpr int loads(int u) { return u == 0 ? 2 : 1; }
@@ -106,6 +107,7 @@ template <int TN> struct Rows<Q8_0, TN> {
 // two runs of four at 4G and 16 + 4G of that block.
 template <int KIND, int TN> struct NibRows {
   static constexpr int kParts = 2, kPartElems = 4;
+  static constexpr bool kPostScale = false;  // B carries the block scale
   static __device__ __forceinline__ int a_part(int u, int h, int G, int e) { return 64 * u + 32 * h + 16 * e + 4 * G; }
   u32x4 w[2][2][TN];
   __device__ __forceinline__ void load_sections(__amdgpu_buffer_rsrc_t r, int lane, const int (&rec)[TN], int wk, int u,
@@ -211,6 +213,37 @@ template <int TN> struct Rows<MXFP4, TN> : NibRows<MXFP4, TN> {
     const uint32_t p3 = gm::bits(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc, 3));
     return u32x4{perm(p1, p0, 0x05040100u), perm(p3, p2, 0x05040100u), perm(p1, p0, 0x07060302u),
                  perm(p3, p2, 0x07060302u)};
+  }
+};
+
+// IQ4_XS: row section at 2048 + 8 j, the super-block header (f16 d,
+// scales_h, scales_l).  Group s's scale d * (ls_s - 32) is exact in f32 but
+// not in f16, so B is the exact table value and the scale multiplies each
+// step's product in f32 (kPostScale).
+template <int TN> struct Rows<IQ4_XS, TN> : NibRows<IQ4_XS, TN> {
+  using B = NibRows<IQ4_XS, TN>;
+  static constexpr int kRec = 16 * 136;
+  static constexpr bool kPostScale = true;
+  static constexpr int loads(int u) { return u == 0 ? 2 : u == 2 ? 1 : 0; }
+  u32x2 s[2][TN];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int lane, int j, const int (&rec)[TN], int wk, int u,
+                                       int p) {
+    B::load_sections(r, lane, rec, wk, u, p);
+    if (u == 0) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) s[p][tn] = ld_b64(r, 2048 + 8 * j, rec[tn] + wk);
+    }
+  }
+  __device__ __forceinline__ u32x4 b(int u, int p, int tn, int h, int) const {
+    const uint32_t q = B::codes(u, p, tn, h);
+    const half2v one = {(_Float16)1.0f, (_Float16)1.0f}, off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    return B::affine8(iq4_lookup(q & 0x0F0F0F0Fu), iq4_lookup((q >> 4) & 0x0F0F0F0Fu), off, one);
+  }
+  __device__ __forceinline__ float scale(int u, int p, int tn, int h) const {
+    const int g = 2 * u + h;
+    const uint32_t x = s[p][tn][0], y = s[p][tn][1];
+    const uint32_t ls = ((y >> (4 * g)) & 15u) | (((x >> (16 + 2 * g)) & 3u) << 4);
+    return f16_bits_to_f32(x & 0xFFFFu) * (float)((int)ls - 32);
   }
 };
 
@@ -379,10 +412,22 @@ __global__ __launch_bounds__(64 * KQ * NH, 1) void gemm_pk_kernel(const uint8_t 
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       const half8 bf = as_h8(rows.b(u, p, tn, h, G));
+      if constexpr (R::kPostScale) {
+        // The step is one group: its product, then its f32 scale.
+        const float sc = rows.scale(u, p, tn, h);
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[tm], bf, acc[tm][tn], 0, 0, 0);
-        if constexpr (kF32) acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[tm], bf, acc[tm][tn], 0, 0, 0);
+        for (int tm = 0; tm < TM; ++tm) {
+          floatx4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[tm], bf, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          if constexpr (kF32) D = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[tm], bf, D, 0, 0, 0);
+          acc[tm][tn] += sc * D;
+        }
+      } else {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[tm], bf, acc[tm][tn], 0, 0, 0);
+          if constexpr (kF32)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[tm], bf, acc[tm][tn], 0, 0, 0);
+        }
       }
     }
   };
@@ -533,7 +578,7 @@ static hipError_t run_kind(const uint8_t *P, const void *A, int a_f16, float *C,
 }  // namespace pk
 
 bool gemm_packed_supported(int kind) {
-  return kind == Q8_0 || kind == Q4_0 || kind == Q5_0 || kind == IQ4_NL || kind == MXFP4;
+  return kind == Q8_0 || kind == Q4_0 || kind == Q5_0 || kind == IQ4_NL || kind == MXFP4 || kind == IQ4_XS;
 }
 
 hipError_t launch_gemm_packed(int kind, const uint8_t *P, const void *A, int a_f16, float *C, int64_t M, int64_t N,
@@ -544,6 +589,7 @@ hipError_t launch_gemm_packed(int kind, const uint8_t *P, const void *A, int a_f
     case Q5_0: return pk::run_kind<Q5_0>(P, A, a_f16, C, M, N, K, s);
     case IQ4_NL: return pk::run_kind<IQ4_NL>(P, A, a_f16, C, M, N, K, s);
     case MXFP4: return pk::run_kind<MXFP4>(P, A, a_f16, C, M, N, K, s);
+    case IQ4_XS: return pk::run_kind<IQ4_XS>(P, A, a_f16, C, M, N, K, s);
     default: break;
   }
   return hipErrorNotSupported;

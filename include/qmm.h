@@ -268,10 +268,13 @@ int qmm_gemv_packed(int kind, const void *P, const void *x, int x_dtype, float *
  * batch of M tokens against one weight matrix, f32 output, beta = 0) over
  * the repacked fast path of Vulkore quant_test.cpp, section 4.  M <=
  * QMM_GEMV_MAX_M runs qmm_gemv_packed; larger M runs the prefill GEMM over
- * the records, which takes Q8_0, Q4_0, Q5_0, IQ4_NL and MXFP4 (other kinds
- * give QMM_ERR_UNSUPPORTED_KIND there).  A is [M][K] f32 or f16, C [M][N] f32, overwritten.  Numerics of
- * the GEMM: each weight rounded once to f16 (the f16 product of the code and
- * the block scale), f16 activations exact, f32 activations split into two
+ * the records, which takes Q8_0, Q4_0, Q5_0, IQ4_NL, MXFP4 and IQ4_XS (other
+ * kinds give QMM_ERR_UNSUPPORTED_KIND there).  A is [M][K] f32 or f16, C
+ * [M][N] f32, overwritten.  Numerics of the GEMM: each weight rounded once
+ * to f16 (the f16 product of the code and the block scale; IQ4_XS instead
+ * multiplies each 32-element group's product by its exact f32 scale
+ * d * (ls - 32), so its weights are not rounded), f16 activations exact, f32
+ * activations split into two
  * f16 halves (hi = RN_f16(a), lo = RN_f16(a - hi)) that are both multiplied,
  * f32 accumulation in a fixed order (deterministic):
  * |C - exact| <= 1e-3 . sum|w||a| + 1e-6; as in qmm_gemm_ex, a weight beyond

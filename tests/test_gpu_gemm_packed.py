@@ -7,7 +7,8 @@ prefill GEMM for M > 8, the packed GEMV below.
   ragged tail, row counts that leave a partial 16-row tile and a partial
   128-row tile, and k-block counts that split unevenly over the four waves
   (5 k-blocks) or leave waves without work (1 k-block);
-* one-hot rows: each output is the weight rounded once to f16, exactly;
+* one-hot rows: each output is the weight rounded once to f16, exactly (the
+  f32 weight itself for IQ4_XS, whose group scales apply after the product);
 * the same call twice gives the same bits (fixed summation order);
 * the 512 x 4096 x 4096 prefill workload on sampled rows;
 * grids whose 64 x 128 tiles would take more than one round of the compute
@@ -27,7 +28,10 @@ import gguf_block_quantized_kind_amd as qmm  # noqa: E402
 
 from test_gpu_parity import SENTINEL, assert_within_bound, dev, filled, host, _sample_rows  # noqa: E402
 
-KINDS = ["Q8_0", "Q4_0", "Q5_0", "IQ4_NL", "MXFP4"]
+KINDS = ["Q8_0", "Q4_0", "Q5_0", "IQ4_NL", "MXFP4", "IQ4_XS"]
+# Kinds whose group scale multiplies each step's product in f32 (no weight
+# rounding): a unit vector returns the f32 weight itself.
+POST_SCALED = {"IQ4_XS"}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -73,7 +77,9 @@ def test_matmul_packed_unit_vectors_return_f16_weights(oracle_mod, kind):
     g = wl.rng("gpu_gemm_packed_unit", kind)
     W = (wl.random_weights(kind, N, K, g, e8m0_range=(100, 140)) if kind == "MXFP4"
          else wl.random_weights(kind, N, K, g, scales="stress"))
-    want = oracle_mod.dequant(kind, W).reshape(N, K).astype(np.float16).astype(np.float32)
+    want = oracle_mod.dequant(kind, W).reshape(N, K).astype(np.float32)
+    if kind not in POST_SCALED:
+        want = want.astype(np.float16).astype(np.float32)
     ks = [0, 1, 7, 8, 31, 32, 255, 256, 511, 600, K - 1] + list(range(100, 121))
     X = np.zeros((len(ks), K), dtype=np.float16)
     for i, k in enumerate(ks):

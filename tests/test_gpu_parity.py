@@ -156,6 +156,24 @@ def test_gemv_parity(oracle_mod, kind, xdt):
             assert_within_bound(host(y), Y, B, f"{kind} K={K} M={M} {xdt}")
 
 
+@pytest.mark.parametrize("kind", ["Q2_K", "Q3_K", "Q4_K", "Q5_K", "Q6_K"])
+def test_gemv_native_rows_half_tiles(oracle_mod, kind):
+    """2 to 8 tokens over native rows at 4500 rows (282 tiles, the last one
+    ragged): on 256 compute units that is more than one tile per unit and
+    under 3.5, so workgroups own ranges of 8-row half tiles (a wave's tile
+    may be its lower or upper half only)."""
+    N, K = 4500, 768
+    g = wl.rng("gpu_gemv_half_tiles", kind)
+    W = wl.random_weights(kind, N, K, g)
+    Wd = dev(W)
+    for M, dt in ((2, np.float32), (5, np.float16), (8, np.float32)):
+        X = wl.activations((M, K), dt, g)
+        y = filled((M, N))
+        qmm.qmm_gemv_ex(kind, Wd, dev(X), y, M, N, K)
+        Y, B = oracle_mod.matmul(kind, W, K, X)
+        assert_within_bound(host(y), Y, B, f"{kind} M={M} N={N} K={K}")
+
+
 @pytest.mark.parametrize("kind,K", [(k, K) for k in ALL_KINDS for K in gemv_Ks(k)])
 def test_gemv_unit_vectors_return_the_weights(oracle_mod, kind, K):
     N = 70

@@ -53,7 +53,7 @@ template <int KIND, typename XT, int MT, int T, int S, int PD, int XD, bool ROUT
 __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__restrict__ P,
                                                              const XT *__restrict__ X, float *__restrict__ Y,
                                                              int M, int64_t N, int K, int per_wg, int extra,
-                                                             int unit, MoeRoute rt, int64_t row_bytes) {
+                                                             MoeRoute rt, int64_t row_bytes) {
   using Dd = Dec<KIND>;
   using X4 = typename XVec<XT>::type;
   constexpr int kFrag = Dd::NSTEP * MT * 4;  // 16-byte fragments per k-block (layout of qmm_gemv_mfma.hip)
@@ -82,24 +82,16 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
     M = min(MT, rt.ws[rt.offsets_at + e + 1] - c0);
     P += (int64_t)e * (PACKED ? ((N + 15) / 16) * (K / Dd::KB) * kRec : N * row_bytes);  // expert e's weights
   }
-  // Workgroup b owns the 8-row half tiles [h0, h1): `unit` (2: whole tiles,
-  // 1: halves) times per_wg each, one unit more for the first `extra`
-  // workgroups, never past the last tile.  Wave t takes the t-th tile the
-  // range touches and, within it, the rows [jlo, jhi) the range holds.
+  // Workgroup b owns tiles [t0, t1): per_wg each, one more for the first
+  // `extra` workgroups (never past the last tile).
   const int b = blockIdx.x;
-  const int nh = 2 * (int)((N + 15) / 16);
-  const int h0 = unit * (b * per_wg + min(b, extra));
-  const int h1 = min(h0 + unit * (per_wg + (b < extra ? 1 : 0)), nh);
-  const int tt = h0 / 2 + t, hl = max(h0, 2 * tt), hh = min(h1, 2 * tt + 2);
-  // A wave without a tile stages its share of the activations and loads the
-  // workgroup's last tile again (cache hits), but decodes and stores nothing.
-  const bool owner = hl < hh;
-  const int64_t tile = owner ? tt : (h1 - 1) / 2;
-  const int jlo = owner ? 8 * (hl - 2 * tt) : 0, jhi = owner ? 8 * (hh - 2 * tt) : 16;
-  // A lane whose row lies outside [jlo, jhi) loads row j ^ 8 (the other half
-  // of the same 128-byte lines), so a half tile reads half the lines; its
-  // column of the product is not stored.
-  const int jl = (j >= jlo && j < jhi) ? j : (j ^ 8);
+  const int t0 = b * per_wg + min(b, extra);
+  const int t1 = (int)min<int64_t>(t0 + per_wg + (b < extra ? 1 : 0), (N + 15) / 16);
+  // A wave without a tile (t >= t1 - t0) stages its share of the activations
+  // and loads the workgroup's last tile again (cache hits), but decodes and
+  // stores nothing.
+  const bool owner = t0 + t < t1;
+  const int64_t tile = owner ? t0 + t : t1 - 1;
   const int nkb = K / Dd::KB;
   const int kb0 = (int)((int64_t)kp * nkb / S), kb1 = (int)((int64_t)(kp + 1) * nkb / S);
   const int cnt = kb1 - kb0;
@@ -128,12 +120,12 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
   }
   // This tile's records, or row j of it (rows past N decode the last row;
   // their outputs are not stored).
-  const uint8_t *wt = PACKED ? P + tile * nkb * kRec : P + min<int64_t>(tile * 16 + jl, N - 1) * row_bytes;
+  const uint8_t *wt = PACKED ? P + tile * nkb * kRec : P + min<int64_t>(tile * 16 + j, N - 1) * row_bytes;
   typename std::conditional<PACKED, typename Rec<KIND>::Packed, typename Dd::Raw>::type raw[NS];
   X4 xv[XD][kPerLane];  // activation shares of the next XD k-blocks
   auto issue_w = [&](int kb, int slot) {
     kb = min(kb, kb_last);
-    if constexpr (PACKED) Rec<KIND>::load(wt + kb * kRec, (lane & 48) | jl, jl, G, raw[slot]);
+    if constexpr (PACKED) Rec<KIND>::load(wt + kb * kRec, lane, j, G, raw[slot]);
     else Dd::load(wt + (int64_t)kb * Dd::BYTES, G, raw[slot]);
   };
   auto issue_x = [&](int kb, int slot) {
@@ -234,7 +226,7 @@ __global__ __launch_bounds__(64 * T * S) void gemv_xs_kernel(const uint8_t *__re
 #pragma unroll
     for (int q = 1; q < S; ++q) acc += red[((q - 1) * T + t) * 64 + lane];
   }
-  if (!owner || j < jlo || j >= jhi) return;
+  if (!owner) return;
   // Lane (j, G) holds D[token 4G + q][row j].
   const int64_t row = tile * 16 + j;
   if (row >= N) return;
@@ -267,27 +259,16 @@ static hipError_t run_xs(const uint8_t *P, const void *x, int x_f16, float *y, i
   const int64_t row_bytes = (K / Geometry<KIND>::elems) * Geometry<KIND>::bytes;
   constexpr int kFrag = Dec<KIND>::NSTEP * MT * 4;
   const size_t lds = std::max<size_t>((size_t)S * 2 * kFrag * 16 + 16, (size_t)(S - 1) * T * 64 * 16);
-  const int64_t ntiles = (N + 15) / 16, cus = device_cus();
-  int64_t wgs = std::max<int64_t>((ntiles + T - 1) / T, spread ? std::min<int64_t>(ntiles, cus) : 1);
-  int64_t units = ntiles;
-  int unit = 2;
-  // One workgroup per compute unit with more than one tile each: split the
-  // rows in 8-row halves when that lowers the most any workgroup reads (896
-  // tiles over 256 units: 3.5 tiles each instead of 4 for half of them); a
-  // range of at most 2T - 1 halves touches at most T tiles.
-  if (spread && wgs == cus && ntiles > cus && (2 * ntiles + cus - 1) / cus <= 2 * T - 1 &&
-      (2 * ntiles + cus - 1) / cus < 2 * ((ntiles + cus - 1) / cus)) {
-    units = 2 * ntiles;
-    unit = 1;
-  }
-  const int per_wg = (int)(units / wgs), extra = (int)(units % wgs);
+  const int64_t ntiles = (N + 15) / 16;
+  const int64_t wgs = std::max<int64_t>((ntiles + T - 1) / T, spread ? std::min<int64_t>(ntiles, device_cus()) : 1);
+  const int per_wg = (int)(ntiles / wgs), extra = (int)(ntiles % wgs);
   const dim3 grid((unsigned)wgs), block(64 * T * S);
   if (x_f16)
     hipLaunchKernelGGL((gemv_xs_kernel<KIND, _Float16, MT, T, S, PD, XD, false, PACKED>), grid, block, lds, s, P,
-                       (const _Float16 *)x, y, M, N, (int)K, per_wg, extra, unit, MoeRoute{}, row_bytes);
+                       (const _Float16 *)x, y, M, N, (int)K, per_wg, extra, MoeRoute{}, row_bytes);
   else
     hipLaunchKernelGGL((gemv_xs_kernel<KIND, float, MT, T, S, PD, XD, false, PACKED>), grid, block, lds, s, P,
-                       (const float *)x, y, M, N, (int)K, per_wg, extra, unit, MoeRoute{}, row_bytes);
+                       (const float *)x, y, M, N, (int)K, per_wg, extra, MoeRoute{}, row_bytes);
   return hipGetLastError();
 }
 
@@ -303,10 +284,10 @@ static hipError_t run_xs_routed(const uint8_t *P, const void *x, int x_f16, floa
   const dim3 grid((unsigned)((ntiles + T - 1) / T), (unsigned)items), block(64 * T * S);
   if (x_f16)
     hipLaunchKernelGGL((gemv_xs_kernel<KIND, _Float16, MT, T, S, PD, XD, true, PACKED>), grid, block, lds, s, P,
-                       (const _Float16 *)x, y, MT, N, (int)K, T, 0, 2, rt, row_bytes);
+                       (const _Float16 *)x, y, MT, N, (int)K, T, 0, rt, row_bytes);
   else
     hipLaunchKernelGGL((gemv_xs_kernel<KIND, float, MT, T, S, PD, XD, true, PACKED>), grid, block, lds, s, P,
-                       (const float *)x, y, MT, N, (int)K, T, 0, 2, rt, row_bytes);
+                       (const float *)x, y, MT, N, (int)K, T, 0, rt, row_bytes);
   return hipGetLastError();
 }
 

@@ -157,11 +157,10 @@ def test_gemv_parity(oracle_mod, kind, xdt):
 
 
 @pytest.mark.parametrize("kind", ["Q2_K", "Q3_K", "Q4_K", "Q5_K", "Q6_K"])
-def test_gemv_native_rows_half_tiles(oracle_mod, kind):
+def test_gemv_native_rows_more_tiles_than_units(oracle_mod, kind):
     """2 to 8 tokens over native rows at 4500 rows (282 tiles, the last one
-    ragged): on 256 compute units that is more than one tile per unit and
-    under 3.5, so workgroups own ranges of 8-row half tiles (a wave's tile
-    may be its lower or upper half only)."""
+    ragged): more tiles than compute units, so workgroups of one and two
+    tiles and waves without a tile."""
     N, K = 4500, 768
     g = wl.rng("gpu_gemv_half_tiles", kind)
     W = wl.random_weights(kind, N, K, g)

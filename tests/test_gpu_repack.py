@@ -80,9 +80,8 @@ def test_gemv_packed_two_to_eight_tokens(oracle_mod, kind, N, K):
     """The 2-to-8-token kernel: K split over k-parts unevenly (11
     k-blocks: a k-part idles a round; 2 k-blocks), whole and remainder
     rounds of the weight pipeline, ragged tiles (N = 17, 300), and
-    more tiles than compute units (N = 4500: on 256 compute units,
-    workgroups of two or three 8-row half tiles, so that a wave may own
-    the lower or upper half of a tile only, and waves without a tile)."""
+    more tiles than compute units (N = 4500: workgroups of one and two
+    tiles, waves without a tile)."""
     g = wl.rng("gpu_gemv_packed_xs", f"{kind}_{N}_{K}")
     W = wl.random_weights(kind, N, K, g)
     P = packed(kind, dev(W), N, K)

@@ -8,7 +8,10 @@ independent of the oracle's own code.
 * Q4_0's -8 bias and Q5_0's fifth-bit splice;
 * bit ownership: which elements each bit of a block moves;
 * cross-format identities (Q5_K with no high bits is Q4_K, IQ4_XS with every
-  group scale 33 is IQ4_NL, Q3_K with a full high mask is Q2_K without mins);
+  group scale 33 is IQ4_NL, Q3_K with a full high mask is Q2_K without mins,
+  Q2_K with pairwise-equal sub-block scales is Q4_K with two-bit codes, and
+  Q3_K is Q6_K with codes 28..35 and scales -32..31: the two kinds the pages
+  do not lay out are tied to two they do);
 * the matmul against exact rational arithmetic, numpy's matmul, unit
   vectors, row selection and permutation;
 * the routed-expert products against per-expert matmuls.
@@ -212,6 +215,83 @@ def test_q3_k_full_mask_is_q2_k_without_mins(oracle_mod):
         q3[:, 104 + m] = hi.astype(np.uint8)
     q3[:, 108:110] = q2[:, 80:82]
     assert _same_bits(oracle_mod.dequant("Q3_K", q3), oracle_mod.dequant("Q2_K", q2))
+
+def _f16_words(g, shape):
+    """Finite, nonzero binary16 values (as uint16) of either sign."""
+    v = (g.standard_normal(shape) * 0.5).astype(np.float16)
+    v[v == 0] = np.float16(0.25)
+    return v.view(np.uint16)
+
+
+def test_q2_k_is_q4_k_with_two_bit_codes(oracle_mod):
+    """Q2_K whose sub-blocks 2j and 2j+1 share scale a_j and min b_j (4 bits
+    each) decodes to the same bits as Q4_K with sub-block j's scale a_j, min
+    b_j, the same d and dmin, and codes 0..3 as its nibbles: d*a*q and dmin*b
+    are exact in binary32 for both, so any placement slip in either layout
+    shows.  Q4_K's layout is the one the pages print."""
+    g = wl.rng("pins", "q2k_q4k")
+    R = 24
+    q = g.integers(0, 4, size=(R, 256))
+    a = g.integers(0, 16, size=(R, 8))
+    b = g.integers(0, 16, size=(R, 8))
+    d, dmin = _f16_words(g, R), _f16_words(g, R)
+    r = np.arange(256)
+    q2 = np.zeros((R, 84), dtype=np.uint8)
+    q2[:, 0:16] = (a | (b << 4))[:, np.arange(16) // 2]        # sc[i] = a | b << 4 of pair i / 2
+    n, jj, l = r // 128, (r % 128) // 32, r % 32
+    for row in range(R):
+        np.bitwise_or.at(q2[row], 16 + 32 * n + l, (q[row] << (2 * jj)).astype(np.uint8))
+    q2[:, 80:82] = d.view(np.uint8).reshape(R, 2)
+    q2[:, 82:84] = dmin.view(np.uint8).reshape(R, 2)
+    q4 = np.zeros((R, 144), dtype=np.uint8)
+    q4[:, 0:2] = d.view(np.uint8).reshape(R, 2)
+    q4[:, 2:4] = dmin.view(np.uint8).reshape(R, 2)
+    q4[:, 4:8] = a[:, 0:4]                                     # 6-bit fields, high bits 0
+    q4[:, 8:12] = b[:, 0:4]
+    q4[:, 12:16] = a[:, 4:8] | (b[:, 4:8] << 4)
+    pos = 16 + (r // 64) * 32 + r % 32
+    hi = (r % 64) >= 32
+    for row in range(R):
+        np.bitwise_or.at(q4[row], pos, (q[row] << (4 * hi)).astype(np.uint8))
+    assert _same_bits(oracle_mod.dequant("Q2_K", q2), oracle_mod.dequant("Q4_K", q4))
+
+
+def test_q3_k_is_q6_k_with_three_bit_codes(oracle_mod):
+    """Q3_K with two-bit codes q2, high-mask bits h and 6-bit scales s equals
+    Q6_K with codes 32 + q2 - 4(1 - h) (28..35), int8 scales s - 32 and the
+    same d: both are d * scale * code with exact binary32 products.  Q6_K's
+    layout is the one the pages print."""
+    g = wl.rng("pins", "q3k_q6k")
+    R = 24
+    q = g.integers(0, 4, size=(R, 256))
+    h = g.integers(0, 2, size=(R, 256))
+    sc = g.integers(0, 64, size=(R, 16))
+    d = _f16_words(g, R)
+    r = np.arange(256)
+    n, jj, l = r // 128, (r % 128) // 32, r % 32
+    q3 = np.zeros((R, 110), dtype=np.uint8)
+    for row in range(R):
+        np.bitwise_or.at(q3[row], l, (h[row] << (4 * n + jj)).astype(np.uint8))
+        np.bitwise_or.at(q3[row], 32 + 32 * n + l, (q[row] << (2 * jj)).astype(np.uint8))
+    low, high = sc & 15, sc >> 4
+    q3[:, 96:104] = low[:, 0:8] | (low[:, 8:16] << 4)
+    for m in range(4):
+        q3[:, 104 + m] = sum(high[:, i] << (2 * (i // 4)) for i in (m, m + 4, m + 8, m + 12))
+    q3[:, 108:110] = d.view(np.uint8).reshape(R, 2)
+    code = 32 + q - 4 * (1 - h)
+    hh, u = r // 128, r % 128
+    l6, gq = u % 32, u // 32
+    q6 = np.zeros((R, 210), dtype=np.uint8)
+    for row in range(R):
+        lo = (code[row] & 15) << (4 * (gq >= 2))
+        np.bitwise_or.at(q6[row], 64 * hh + l6 + 32 * (gq & 1), lo.astype(np.uint8))
+        np.bitwise_or.at(q6[row], 128 + 32 * hh + l6, ((code[row] >> 4) << (2 * gq)).astype(np.uint8))
+    sub = 8 * hh + l6 // 16 + 2 * gq                           # the sub-block of element r
+    assert np.array_equal(sub, r // 16)
+    q6[:, 192:208] = (sc - 32).astype(np.int8).view(np.uint8)
+    q6[:, 208:210] = d.view(np.uint8).reshape(R, 2)
+    assert _same_bits(oracle_mod.dequant("Q3_K", q3), oracle_mod.dequant("Q6_K", q6))
+
 
 
 @pytest.mark.parametrize("kind", ALL_KINDS)

@@ -33,6 +33,11 @@ MUTATIONS = {
     "matmul_reversed_x": ("acc += w[k] * x[k];\n                    mag += fabs(w[k]) * fabs(x[k]);\n                }\n                Y[m * n_sel + i]",
                           "acc += w[k] * x[K - 1 - k];\n                    mag += fabs(w[k]) * fabs(x[k]);\n                }\n                Y[m * n_sel + i]"),
     "moe_wrong_expert": ("const int64_t e = ids[p];", "const int64_t e = ids[p] ^ 1;"),
+    # The same slip in both off-page kinds (their shared code placement), so
+    # that tying them to each other cannot see it; only the pins against the
+    # on-page Q4_K and Q6_K can.
+    "k2_k3_plane_order": ("j = (r % 128) / 32, l = r % 32;", "j = 3 - (r % 128) / 32, l = r % 32;", 2),
+    "k2_k3_half_order": ("const int n = r / 128, j", "const int n = 1 - r / 128, j", 2),
 }
 
 
@@ -43,7 +48,8 @@ def _all_pin_cases():
     for fn in (pins.test_binary16_exhaustive, pins.test_e8m0_every_byte, pins.test_q4_0_bias,
                pins.test_q5_0_fifth_bit_splice, pins.test_q5_k_without_high_bits_is_q4_k,
                pins.test_iq4_xs_with_unit_scales_is_iq4_nl,
-               pins.test_q3_k_full_mask_is_q2_k_without_mins, pins.test_moe_matches_per_expert_matmul):
+               pins.test_q3_k_full_mask_is_q2_k_without_mins, pins.test_q2_k_is_q4_k_with_two_bit_codes,
+               pins.test_q3_k_is_q6_k_with_three_bit_codes, pins.test_moe_matches_per_expert_matmul):
         cases.append((fn, {}))
     for kind in pins.ALL_KINDS:
         for fn in (pins.test_bit_ownership, pins.test_matmul_exact_brute_force,
@@ -54,10 +60,10 @@ def _all_pin_cases():
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_reject_planted_mistake(name, tmp_path):
-    old, new = MUTATIONS[name]
+    old, new, *count = MUTATIONS[name]
     with open(oracle.SOURCE) as f:
         src = f.read()
-    assert src.count(old) == 1, f"mutation {name} no longer matches the oracle source"
+    assert src.count(old) == (count[0] if count else 1), f"mutation {name} no longer matches the oracle source"
     path = os.path.join(tmp_path, "mutant.c")
     with open(path, "w") as f:
         f.write(src.replace(old, new))

@@ -319,7 +319,11 @@ QMM_EXPORT int qmm_matmul_packed(int kind, const void *P, const void *A, int a_d
   if (!qmm::gemm_packed_supported(kind))
     return fail(QMM_ERR_UNSUPPORTED_KIND, "the prefill GEMM over repacked weights does not take kind %d (M > %d)",
                 kind, QMM_GEMV_MAX_M);
-  if (qmm::packed_bytes_of(kind, N, K) >= ((int64_t)1 << 32) || M >= ((int64_t)1 << 24))
+  // The GEMM addresses P and A through buffer descriptors with signed 32-bit
+  // byte offsets.
+  const int64_t a_bytes = M * K * (a_dtype == QMM_F16 ? 2 : 4);
+  if (qmm::packed_bytes_of(kind, N, K) >= ((int64_t)1 << 31) || a_bytes >= ((int64_t)1 << 31) ||
+      M >= ((int64_t)1 << 24))
     return fail(QMM_ERR_BAD_ARG, "N=%lld, K=%lld, M=%lld exceed the GEMM's 32-bit offsets", (long long)N,
                 (long long)K, (long long)M);
   return hip_status(qmm::launch_gemm_packed(kind, (const uint8_t *)P, A, a_dtype == QMM_F16, C, M, N, K,

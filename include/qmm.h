@@ -279,8 +279,9 @@ int qmm_gemv_packed(int kind, const void *P, const void *x, int x_dtype, float *
  * f32 accumulation in a fixed order (deterministic):
  * |C - exact| <= 1e-3 . sum|w||a| + 1e-6; as in qmm_gemm_ex, a weight beyond
  * the f16 range (|w| > 65504) becomes an infinity.  Errors: as qmm_gemv_packed for
- * kind, K, dtype and pointers (without its M limit), M * K >= 2^31 or
- * packed bytes >= 2^32 QMM_ERR_BAD_ARG. */
+ * kind, K, dtype and pointers (without its M limit), M * K >= 2^31
+ * QMM_ERR_BAD_ARG; above QMM_GEMV_MAX_M tokens also packed bytes >= 2^31 or
+ * A bytes (M * K * 2 for f16, * 4 for f32) >= 2^31 QMM_ERR_BAD_ARG. */
 int qmm_matmul_packed(int kind, const void *P, const void *A, int a_dtype, float *C,
                       int64_t M, int64_t N, int64_t K, void *stream);
 

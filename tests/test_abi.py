@@ -98,6 +98,20 @@ def test_gemv_refusals_in_order(lib):
     assert g(2, FAKE, FAKE, 0, FAKE, 1, 10, (1 << 30) + 32, None) == ARG  # K > 2^30
 
 
+def test_matmul_packed_refusals(lib):
+    m = lib.qmm_matmul_packed
+    # above eight tokens, a kind the prefill GEMM over records does not take
+    assert m(12, FAKE, FAKE, 1, FAKE, 9, 16, 256, None) == KIND
+    # M * K at 2^31, for any token count
+    assert m(8, FAKE, FAKE, 1, FAKE, 1 << 21, 16, 1024, None) == ARG
+    # activation bytes at 2^31 (the GEMM's signed 32-bit offsets): 2^29
+    # f32 values, 2^30 f16 values
+    assert m(8, FAKE, FAKE, 0, FAKE, 1 << 18, 16, 2048, None) == ARG
+    assert m(8, FAKE, FAKE, 1, FAKE, 1 << 19, 16, 2048, None) == ARG
+    # repacked weights of 2 GiB or more (Q8_0: 272 bytes per row of 256)
+    assert m(8, FAKE, FAKE, 1, FAKE, 16, (1 << 31) // 272 + 16, 256, None) == ARG
+
+
 def test_gemm_refusals_in_order(lib):
     g = lib.qmm_gemm_ex
     assert g(2, FAKE, FAKE, 1, FAKE, 0, 10, 64, None) == EMPTY

@@ -6,7 +6,8 @@ FFN):
 * qmm_matmul over native rows and qmm_matmul_packed over repacked records:
   every kind, K in whole 256-element k-blocks up to 3072, 1 to 2499 rows,
   token counts from 1 to 200 (the decode GEMVs at 8 or fewer, the prefill
-  GEMMs above), f16 and f32 activations;
+  GEMMs above), f16 and f32 activations; and 20 larger cases (up to 23999
+  rows, K up to 8192, up to 600 tokens: grids of several rounds);
 * qmm_moe / qmm_moe_packed: 1 to 39 experts, top-1 to top-8, 1 to 256
   tokens, shared or per-slot activations, sometimes a skipped slot;
 * qmm_moe_ffn / qmm_moe_ffn_packed on the same routing (a token whose only
@@ -50,6 +51,31 @@ def _matmul_cases(n):
 def test_sweep_matmul_native_and_packed(oracle_mod, chunk):
     for i, kind, M, N, K, f16 in list(_matmul_cases(240))[chunk::4]:
         r = wl.rng("gpu_sweep_matmul", str(i))
+        W = wl.random_weights(kind, N, K, r)
+        X = wl.activations((M, K), np.float16 if f16 else np.float32, r)
+        Y, B = oracle_mod.matmul(kind, W, K, X)
+        what = f"{kind} M={M} N={N} K={K} {'f16' if f16 else 'f32'}"
+        Wd, Xd = dev(W), dev(X)
+        C = filled((M, N))
+        qmm.qmm_matmul(kind, Wd, Xd, C, M, N, K)
+        assert_within_bound(host(C), Y, B, "native " + what)
+        if kind in PACKED and (M <= 8 or kind in PACKED_GEMM):
+            P = torch.full((qmm.qmm_packed_bytes(kind, N, K),), 0xA5, dtype=torch.uint8, device="cuda")
+            qmm.qmm_repack(kind, Wd, P, N, K)
+            C = filled((M, N))
+            qmm.qmm_matmul_packed(kind, P, Xd, C, M, N, K)
+            assert_within_bound(host(C), Y, B, "packed " + what)
+
+
+def test_sweep_matmul_large_grids(oracle_mod):
+    """Larger shapes, so that grids take several rounds of the compute
+    units: up to 23999 rows, K up to 8192, up to 600 tokens."""
+    g = np.random.default_rng(20261205)
+    for i in range(20):
+        kind = KINDS[g.integers(len(KINDS))]
+        K, N = 256 * int(g.integers(1, 33)), int(g.integers(1, 24000))
+        M, f16 = int(g.choice([1, 3, 8, 9, 100, 257, 600])), bool(g.integers(2))
+        r = wl.rng("gpu_sweep_large", str(i))
         W = wl.random_weights(kind, N, K, r)
         X = wl.activations((M, K), np.float16 if f16 else np.float32, r)
         Y, B = oracle_mod.matmul(kind, W, K, X)
